@@ -1,0 +1,28 @@
+"""Plain float64 CPU oracle for the Matryoshka-nested integer matmul.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the product path.  It shares no
+code with the HIP library (nested_int_matmul_amd) and imports nothing from it.
+Every function cites the passage of the pages it restates.
+"""
+from .matquant import (  # noqa: F401
+    C_BITS,
+    LAYER_LINEARS,
+    bf16_bits_from_float,
+    bf16_round,
+    dequant,
+    dequant_rows,
+    effective_bits,
+    float_from_bf16_bits,
+    linear,
+    mixnmatch_forward,
+    mixnmatch_layer,
+    pack_codes,
+    pack_indices,
+    quantize_minmax,
+    rms_normalize,
+    slice_index,
+    slice_value,
+    slice_value_noclamp,
+    unpack_indices,
+)

@@ -1,0 +1,304 @@
+"""Float64 CPU oracle for the Matryoshka-nested integer matmul.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module; only the tests, the smoke check and the CPU-baseline leg
+of the benchmark do.  It shares no code with the HIP library and imports
+nothing from it.
+
+Sources (the pages this restates, by title and section):
+  [MQX]  "Matryoshka Quantization" explainer (paper-graph-ui, training-methods),
+         §3.4 Detailed Breakdown: "Quantization Primitives" (Eq. 1),
+         "The Bit-Slicing Operator" (Eq. 6, worked examples, errata Eq. 8),
+         "Mix'n'Match and Interpolative Slicing".
+  [MQR]  "Pith review of Matryoshka Quantization", "What carries the argument".
+  [ROSAQ] "Pith review of ROSAQ", method summary (per-group granularity of 128).
+
+Everything is computed in float64 (plain Python integers for the integer
+steps), step by step in the order the pages state, with no blocking, fusion or
+reordering.  Readings taken where the pages are silent or ambiguous are marked
+READING and listed in the design notes of the repository.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+C_BITS = 8  # the stored code width c (int8 codes, [MQX] "The Bit-Slicing Operator")
+
+
+# --------------------------------------------------------------------------
+# bf16 (used for the activations, which the pages keep in bfloat16)
+# --------------------------------------------------------------------------
+
+def bf16_bits_from_float(v) -> np.ndarray:
+    """Round float values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns as uint16.
+
+    Written from the IEEE definition: a bf16 is the upper half of an fp32;
+    the value is first rounded to fp32, then the low 16 bits are rounded away
+    to nearest, ties to even.  NaN is not expected in any input.
+    """
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    high = u >> 16
+    round_up = (low > 0x8000) | ((low == 0x8000) & ((high & 1) == 1))
+    high = high + round_up.astype(np.uint64)
+    return high.astype(np.uint16)
+
+
+def float_from_bf16_bits(b) -> np.ndarray:
+    """The float64 value of bf16 bit patterns (exact)."""
+    b = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Eq. 1: min-max asymmetric quantizer Q_MM(w, c)
+# --------------------------------------------------------------------------
+
+def quantize_minmax(w, group: int):
+    """Min-max quantization of weights to c = 8-bit unsigned codes ([MQX] Eq. 1).
+
+    w: float32 [N, K] (a real weight matrix stored out-channel major, K = input
+    dimension contiguous).  Each "real-valued weight vector" of Eq. 1 is one
+    group of `group` consecutive entries of a row (group == K: per output
+    channel; group == 128: per group along K, the granularity of [ROSAQ]).
+
+    Per vector:  alpha = (max - min) / (2^c - 1),  z = -min / alpha,
+                 q = clamp(round(w / alpha + z), 0, 2^c - 1).
+    READINGS: alpha and z are stored as fp32 (z is real, not rounded); alpha is
+    the float64 quotient rounded to fp32, z the float64 quotient -min/alpha32
+    rounded to fp32; the codes use those stored fp32 values, evaluated in
+    float64; round() is floor(v + 1/2); a constant vector (max == min) takes
+    alpha = 1, z = -min, so every code is 0 and dequantizes to min exactly.
+
+    Returns (q uint8 [N, K], alpha float32 [N, G], zero float32 [N, G]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    if group <= 0 or k % group:
+        raise ValueError("group must divide K")
+    g = k // group
+    levels = 2 ** C_BITS - 1
+    wv = w.reshape(n, g, group).astype(np.float64)
+    mn = wv.min(axis=2)
+    mx = wv.max(axis=2)
+    alpha64 = (mx - mn) / float(levels)
+    alpha32 = alpha64.astype(np.float32)
+    constant = (mx == mn)
+    alpha32 = np.where(constant, np.float32(1.0), alpha32)
+    zero32 = (-mn / alpha32.astype(np.float64)).astype(np.float32)
+    a = alpha32.astype(np.float64)[:, :, None]
+    z = zero32.astype(np.float64)[:, :, None]
+    v = wv / a + z
+    q = np.floor(v + 0.5)
+    q = np.clip(q, 0, levels)
+    return q.astype(np.uint8).reshape(n, k), alpha32, zero32
+
+
+# --------------------------------------------------------------------------
+# Eq. 6 (and the erratum Eq. 8): the bit-slicing operator S(q_c, r)
+# --------------------------------------------------------------------------
+
+def _round_half_up(v: np.ndarray) -> np.ndarray:
+    # The first discarded bit decides: 1 rounds up, 0 rounds down.  For a
+    # quotient by a power of two this is "round half up" ([MQX] "The
+    # Bit-Slicing Operator", the tie-breaking rule stated after Eq. 6).
+    return np.floor(v + 0.5)
+
+
+def slice_value(q, r: int) -> np.ndarray:
+    """S(q, r) = clamp(round(q / 2^(c-r)), 0, 2^r - 1) * 2^(c-r)  ([MQX] Eq. 6).
+
+    q: integer codes in [0, 2^c - 1].  Returns int64 values on the int8 scale
+    (multiples of 2^(c-r) with c - r trailing zero bits).  q / 2^(c-r) is exact
+    in float64, so the rounding is exact.
+    """
+    if not 1 <= r <= C_BITS:
+        raise ValueError("r must be in 1..8")
+    step = float(2 ** (C_BITS - r))
+    t = _round_half_up(np.asarray(q, dtype=np.float64) / step)
+    t = np.clip(t, 0, 2 ** r - 1)
+    return (t * step).astype(np.int64)
+
+
+def slice_index(q, r: int) -> np.ndarray:
+    """The r-bit index t with S(q, r) = t * 2^(c-r); t in [0, 2^r - 1]."""
+    return slice_value(q, r) // (2 ** (C_BITS - r))
+
+
+def slice_value_noclamp(q, r: int) -> np.ndarray:
+    """The erratum operator without the clamp ([MQX] "The errata correction",
+    Eq. 8): round(q / 2^(c-r)) * 2^(c-r).  Takes 2^r + 1 levels; the top one is
+    2^c = 256, which needs an extra bit ("Extra-Precision MatQuant")."""
+    if not 1 <= r <= C_BITS:
+        raise ValueError("r must be in 1..8")
+    step = float(2 ** (C_BITS - r))
+    t = _round_half_up(np.asarray(q, dtype=np.float64) / step)
+    return (t * step).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Storage of a sliced plane (the pages fix values only; this is the layout)
+# --------------------------------------------------------------------------
+
+def pack_indices(t, r: int) -> np.ndarray:
+    """Pack r-bit indices t [N, K] into bytes [N, K*r/8].
+
+    LAYOUT (a reading; the pages define values, not storage): rows stay rows;
+    within a row, byte j holds the 8/r consecutive elements j*8/r + i,
+    i = 0 .. 8/r - 1, element i in bits [i*r, i*r + r) (little-endian fields).
+    r must divide 8 and K must be a multiple of 8/r.
+    """
+    if r not in (1, 2, 4, 8):
+        raise ValueError("byte-aligned packing needs r in {1,2,4,8}")
+    t = np.asarray(t, dtype=np.int64)
+    n, k = t.shape
+    per = 8 // r
+    if k % per:
+        raise ValueError("K must be a multiple of 8/r")
+    if t.min(initial=0) < 0 or t.max(initial=0) >= 2 ** r:
+        raise ValueError("index out of range for r bits")
+    fields = t.reshape(n, k // per, per)
+    out = np.zeros((n, k // per), dtype=np.int64)
+    for i in range(per):
+        out |= fields[:, :, i] << (i * r)
+    return out.astype(np.uint8)
+
+
+def unpack_indices(packed, r: int, k: int) -> np.ndarray:
+    """Inverse of pack_indices: bytes [N, K*r/8] -> indices int64 [N, K]."""
+    if r not in (1, 2, 4, 8):
+        raise ValueError("byte-aligned packing needs r in {1,2,4,8}")
+    p = np.asarray(packed, dtype=np.int64)
+    per = 8 // r
+    n = p.shape[0]
+    if p.shape[1] * per != k:
+        raise ValueError("packed width does not match K")
+    mask = (1 << r) - 1
+    fields = [(p >> (i * r)) & mask for i in range(per)]
+    return np.stack(fields, axis=2).reshape(n, k)
+
+
+def pack_codes(q, r: int) -> np.ndarray:
+    """Slice stored codes to r bits and pack them: the plane a server at
+    precision r reads ([MQX] §2: lower precisions are obtained from the one
+    stored int8 model by slicing)."""
+    return pack_indices(slice_index(q, r), r)
+
+
+# --------------------------------------------------------------------------
+# Dequantization and the matrix product
+# --------------------------------------------------------------------------
+
+def dequant(q, alpha, zero, group: int, r: int) -> np.ndarray:
+    """w_hat = (S(q, r) - z) * alpha, float64 [N, K]  ([MQX] Eq. 1's
+    dequantization alpha*(q - z), applied to the sliced value, which is used
+    "as if it were an int8 value", "The Bit-Slicing Operator").
+    READING: the sliced model keeps the int8 alpha and z."""
+    q = np.asarray(q)
+    n, k = q.shape
+    g = k // group
+    s = slice_value(q, r).astype(np.float64).reshape(n, g, group)
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(n, g, 1)
+    z = np.asarray(zero, dtype=np.float32).astype(np.float64).reshape(n, g, 1)
+    return ((s - z) * a).reshape(n, k)
+
+
+def dequant_rows(q_rows, alpha_rows, zero_rows, group: int, r: int) -> np.ndarray:
+    """dequant() of a subset of rows (for sampled checks of large matrices)."""
+    return dequant(q_rows, alpha_rows, zero_rows, group, r)
+
+
+def linear(x_bf16_bits, q, alpha, zero, group: int, r: int) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * w_hat[n, k]  in float64.
+
+    x: bf16 bit patterns uint16 [M, K]; the weight matrix is stored [N, K]
+    (the transpose of the pages' W in XW), so y = x @ w_hat^T.
+    """
+    x = float_from_bf16_bits(x_bf16_bits)
+    if x.ndim == 1:
+        x = x[None, :]
+    return x @ dequant(q, alpha, zero, group, r).T
+
+
+# --------------------------------------------------------------------------
+# Mix'n'Match: a stack of linears, each layer at its own precision r
+# --------------------------------------------------------------------------
+
+LAYER_LINEARS = ("q", "k", "v", "o", "up", "gate", "down")
+
+
+def rms_normalize(h) -> np.ndarray:
+    """h / sqrt(mean(h^2)) per row (no gain, no epsilon).  READING: the pages
+    give no layer dataflow for a Mix'n'Match stack; a gain-free RMS
+    normalization keeps the activations bounded through the stack."""
+    h = np.asarray(h, dtype=np.float64)
+    rms = np.sqrt(np.mean(h * h, axis=-1, keepdims=True))
+    return h / rms
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round float values to the nearest bf16 value (ties to even), float64."""
+    return float_from_bf16_bits(bf16_bits_from_float(v))
+
+
+def mixnmatch_layer(h, layer, trace=None):
+    """One layer of the Mix'n'Match stack ([MQX] "Mix'n'Match": one stored
+    int8 model, a different slice precision r per layer).
+
+    READING of the layer dataflow (the pages give none):
+      a = bf16(rms_normalize(h));
+      q, k, v, u, g = W_q a, W_k a, W_v a, W_up a, W_gate a;
+      o = W_o bf16(q);  d = W_down bf16(u * g);
+      h <- h + o + d.
+    k and v are computed and not consumed (attention is out of scope).
+    layer: dict with key "r" and, per linear name, a dict with q, alpha, zero,
+    group (stored codes; the layer's r is applied by slicing).
+    trace: optional dict that receives the intermediate values.
+    """
+    r = layer["r"]
+    a_bits = bf16_bits_from_float(rms_normalize(h))
+
+    def lin(name, xb):
+        p = layer[name]
+        return linear(xb, p["q"], p["alpha"], p["zero"], p["group"], r)
+
+    outs = {name: lin(name, a_bits) for name in ("q", "k", "v", "up", "gate")}
+    q_bits = bf16_bits_from_float(outs["q"])
+    ug_bits = bf16_bits_from_float(outs["up"] * outs["gate"])
+    o = lin("o", q_bits)
+    d = lin("down", ug_bits)
+    h_new = np.asarray(h, dtype=np.float64) + o + d
+    if trace is not None:
+        trace.update(a_bits=a_bits, q_bits=q_bits, ug_bits=ug_bits, o=o, d=d, **outs)
+    return h_new
+
+
+def mixnmatch_forward(layers, x_bf16_bits, traces=None) -> np.ndarray:
+    """Run the stack: h0 = x (bf16 values), then every layer in order.
+    Returns float64 h [M, H].  traces: optional list that receives one dict of
+    intermediates per layer."""
+    h = float_from_bf16_bits(x_bf16_bits)
+    if h.ndim == 1:
+        h = h[None, :]
+    for layer in layers:
+        tr = {} if traces is not None else None
+        h = mixnmatch_layer(h, layer, tr)
+        if traces is not None:
+            traces.append(tr)
+    return h
+
+
+def effective_bits(layers) -> float:
+    """Average stored bits per weight of a Mix'n'Match assignment (the
+    "effective bits per parameter" measure of [MQX] "Mix'n'Match")."""
+    total = 0
+    bits = 0
+    for layer in layers:
+        for name in LAYER_LINEARS:
+            n = int(np.asarray(layer[name]["q"]).size)
+            total += n
+            bits += n * layer["r"]
+    return bits / total

@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print, the rounding rule as the pages state it in words (a bit-level
+formulation, independent of the oracle's division-based one), closed forms,
+brute force over every code, exact rational arithmetic, and torch's own bf16
+conversion.
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ALL_CODES = np.arange(256)
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+# ---------------------------------------------------------------- slicing
+
+def test_worked_examples():
+    for q, r, s in _rows("slice_worked_examples.txt"):
+        assert oracle.slice_value(int(q), int(r)) == int(s)
+
+
+def test_ties_follow_the_rule_in_words():
+    for q, r, s in _rows("slice_ties.txt"):
+        assert oracle.slice_value(int(q), int(r)) == int(s)
+
+
+def _slice_by_bits(q: int, r: int) -> int:
+    """The operator as the pages describe it in words: keep the r most
+    significant bits, round up when the first discarded bit is 1, clamp to
+    the r-bit range, shift back."""
+    if r == 8:
+        return q
+    kept = q >> (8 - r)
+    first_discarded = (q >> (7 - r)) & 1
+    t = min(kept + first_discarded, 2 ** r - 1)
+    return t << (8 - r)
+
+
+@pytest.mark.parametrize("r", range(1, 9))
+def test_bruteforce_against_bit_rule(r):
+    got = oracle.slice_value(ALL_CODES, r)
+    want = [_slice_by_bits(int(q), r) for q in ALL_CODES]
+    assert got.tolist() == want
+
+
+@pytest.mark.parametrize("r", range(1, 9))
+def test_nearest_level_with_ties_up(r):
+    # S(q, r) is the nearest level t * 2^(8-r), t in [0, 2^r - 1], with ties
+    # going to the larger level (the rounding rule), by exhaustive search.
+    levels = np.arange(2 ** r) * 2 ** (8 - r)
+    for q in range(256):
+        d = np.abs(levels - q)
+        best = levels[d == d.min()].max()
+        assert oracle.slice_value(q, r) == best
+
+
+def test_r8_is_identity():
+    assert oracle.slice_value(ALL_CODES, 8).tolist() == ALL_CODES.tolist()
+    assert oracle.slice_index(ALL_CODES, 8).tolist() == ALL_CODES.tolist()
+
+
+@pytest.mark.parametrize("r", range(1, 9))
+def test_multiples_and_range(r):
+    s = oracle.slice_value(ALL_CODES, r)
+    step = 2 ** (8 - r)
+    assert np.all(s % step == 0)
+    assert s.min() >= 0 and s.max() <= (2 ** r - 1) * step <= 255
+    t = oracle.slice_index(ALL_CODES, r)
+    assert np.array_equal(t * step, s)
+
+
+def test_level_sets():
+    for row in _rows("slice_levels.txt"):
+        variant, r, levels = row[0], int(row[1]), [int(v) for v in row[2:]]
+        fn = oracle.slice_value if variant == "clamp" else oracle.slice_value_noclamp
+        assert sorted(set(fn(ALL_CODES, r).tolist())) == levels
+
+
+def test_r2_buckets():
+    # Consequence of Eq. 6 over all codes: [0,31]->0, [32,95]->64,
+    # [96,159]->128, [160,255]->192.
+    s = oracle.slice_value(ALL_CODES, 2)
+    want = np.select([ALL_CODES < 32, ALL_CODES < 96, ALL_CODES < 160], [0, 64, 128], 192)
+    assert np.array_equal(s, want)
+
+
+@pytest.mark.parametrize("r", range(1, 9))
+def test_nesting_and_idempotence(r):
+    s = oracle.slice_value(ALL_CODES, r)
+    assert np.array_equal(oracle.slice_value(s, r), s)
+    for r2 in range(r, 9):
+        # the value set of a coarser slice lies inside every finer one
+        assert np.array_equal(oracle.slice_value(s, r2), s)
+
+
+def test_slicing_does_not_compose_downwards():
+    # Slicing the int4 slice to int2 is not the int2 slice: double rounding
+    # changes exactly the 24 codes 24-31, 88-95, 152-159.
+    via4 = oracle.slice_value(oracle.slice_value(ALL_CODES, 4), 2)
+    direct = oracle.slice_value(ALL_CODES, 2)
+    diff = np.nonzero(via4 != direct)[0].tolist()
+    assert diff == list(range(24, 32)) + list(range(88, 96)) + list(range(152, 160))
+
+
+@pytest.mark.parametrize("r", range(1, 9))
+def test_noclamp_overflow_count(r):
+    # Without the clamp, round(q / 2^(8-r)) = 2^r exactly when
+    # q >= 256 - 2^(7-r): 2^(7-r) codes for r <= 7, none for r = 8.
+    s = oracle.slice_value_noclamp(ALL_CODES, r)
+    n256 = int(np.sum(s == 256))
+    assert n256 == (2 ** (7 - r) if r < 8 else 0)
+    clamped = oracle.slice_value(ALL_CODES, r)
+    assert np.array_equal(np.minimum(s, (2 ** r - 1) * 2 ** (8 - r)), clamped)
+
+
+# ---------------------------------------------------------------- quantizer
+
+def _hand():
+    d = {}
+    for row in _rows("hand_linear.txt"):
+        d.setdefault(row[0], []).append(row[1:])
+    return d
+
+
+def test_hand_quantize():
+    h = _hand()
+    w = np.array([[float(v) for v in h["w"][0]]], dtype=np.float32)
+    q, a, z = oracle.quantize_minmax(w, 4)
+    assert q[0].tolist() == [int(v) for v in h["q"][0]]
+    assert a[0, 0] == np.float32(2.0 / 255.0)
+    assert z[0, 0] == np.float32(127.49999237060547)
+
+
+@pytest.mark.parametrize("group", [128, 512])
+def test_quantizer_invariants(group):
+    rg = np.random.default_rng(7)
+    w = (rg.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    q, a, z = oracle.quantize_minmax(w, group)
+    g = 512 // group
+    qv = q.reshape(16, g, group).astype(np.int64)
+    wv = w.reshape(16, g, group)
+    # the minimum of every vector maps to 0 and the maximum to 255
+    assert np.all(qv[np.arange(16)[:, None], np.arange(g)[None, :], wv.argmin(2)] == 0)
+    assert np.all(qv[np.arange(16)[:, None], np.arange(g)[None, :], wv.argmax(2)] == 255)
+    # monotone within a vector
+    order = np.argsort(wv, axis=2, kind="stable")
+    qs = np.take_along_axis(qv, order, axis=2)
+    assert np.all(np.diff(qs, axis=2) >= 0)
+    # reconstruction error of the int8 model is at most half a step
+    what = oracle.dequant(q, a, z, group, 8)
+    step = np.repeat(a.astype(np.float64), group, axis=1)
+    assert np.all(np.abs(what - w) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+
+
+def test_quantizer_exact_rationals():
+    # q = floor(w/alpha + z + 1/2) with the stored fp32 alpha, z, in exact
+    # rational arithmetic, agrees with the float64 evaluation.
+    rg = np.random.default_rng(11)
+    w = (rg.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    q, a, z = oracle.quantize_minmax(w, 128)
+    for n in range(8):
+        for k in range(256):
+            g = k // 128
+            v = Fraction(float(w[n, k])) / Fraction(float(a[n, g])) + Fraction(float(z[n, g]))
+            want = min(max(int(np.floor(v + Fraction(1, 2))), 0), 255)
+            assert q[n, k] == want
+
+
+def test_constant_vector():
+    w = np.full((2, 128), -0.25, dtype=np.float32)
+    w[1] = 0.0
+    q, a, z = oracle.quantize_minmax(w, 128)
+    assert np.all(q == 0) and np.all(a == 1.0)
+    for r in (8, 4, 2):
+        assert np.array_equal(oracle.dequant(q, a, z, 128, r), w.astype(np.float64))
+
+
+# ---------------------------------------------------------------- packing
+
+def test_hand_packing():
+    h = _hand()
+    q = np.array([[int(v) for v in h["q"][0]]])
+    for row in h["t"]:
+        r = int(row[0])
+        assert oracle.slice_index(q, r)[0].tolist() == [int(v) for v in row[1:]]
+    for row in h["packed"]:
+        r = int(row[0])
+        assert oracle.pack_codes(q, r)[0].tolist() == [int(v, 16) for v in row[1:]]
+
+
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_pack_bit_layout_and_roundtrip(r):
+    rg = np.random.default_rng(r)
+    t = rg.integers(0, 2 ** r, size=(3, 64))
+    p = oracle.pack_indices(t, r)
+    per = 8 // r
+    for n in range(3):
+        for j in range(64 // per):
+            byte = 0
+            for i in range(per):
+                byte += int(t[n, j * per + i]) * 2 ** (i * r)
+            assert p[n, j] == byte
+    assert np.array_equal(oracle.unpack_indices(p, r, 64), t)
+
+
+# ---------------------------------------------------------------- bf16
+
+def test_bf16_rounding_matches_torch():
+    rg = np.random.default_rng(3)
+    v = np.concatenate([
+        rg.standard_normal(20000).astype(np.float32) * 10.0 ** rg.integers(-30, 30, 20000),
+        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 1.0 + 2 ** -8 + 2 ** -20,
+                  3.0e38, 1e-40, -1e-39, 65504.0], dtype=np.float32),
+    ]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_bits_from_float(v), want)
+    back = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().double().numpy()
+    assert np.array_equal(oracle.float_from_bf16_bits(want), back)
+
+
+# ---------------------------------------------------------------- the product
+
+def test_hand_linear():
+    h = _hand()
+    w = np.array([[float(v) for v in h["w"][0]]], dtype=np.float32)
+    q, a, z = oracle.quantize_minmax(w, 4)
+    x = oracle.bf16_bits_from_float(np.ones((1, 4)))
+    for r, num, den in h["y"]:
+        y = oracle.linear(x, q, a, z, 4, int(r))
+        # closed form with alpha = 2/255, z = 127.5; the fp32 storage of alpha
+        # and z moves it by less than 3e-7
+        assert abs(y[0, 0] - int(num) / int(den)) < 3e-7
+
+
+def _exact_linear(x_bits, q, a, z, group, r):
+    m, k = x_bits.shape
+    n = q.shape[0]
+    xs = [[Fraction(float(v)) for v in row] for row in oracle.float_from_bf16_bits(x_bits)]
+    out = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                g = kk // group
+                s = _slice_by_bits(int(q[j, kk]), r)
+                acc += xs[i][kk] * (s - Fraction(float(z[j, g]))) * Fraction(float(a[j, g]))
+            out[i, j] = float(acc)
+    return out
+
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("group", [4, 8])
+def test_linear_exact_rationals(r, group):
+    rg = np.random.default_rng(100 + r + group)
+    w = (rg.standard_normal((5, 8)) * 0.02).astype(np.float32)
+    q, a, z = oracle.quantize_minmax(w, group)
+    x = oracle.bf16_bits_from_float(rg.standard_normal((3, 8)))
+    got = oracle.linear(x, q, a, z, group, r)
+    want = _exact_linear(x, q, a, z, group, r)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- Mix'n'Match
+
+def _const_layer(h_dim, f_dim, consts, r):
+    layer = {"r": r}
+    shapes = {"q": (h_dim, h_dim), "k": (4, h_dim), "v": (4, h_dim), "o": (h_dim, h_dim),
+              "up": (f_dim, h_dim), "gate": (f_dim, h_dim), "down": (h_dim, f_dim)}
+    for name, (n, k) in shapes.items():
+        w = np.full((n, k), consts[name], dtype=np.float32)
+        q, a, z = oracle.quantize_minmax(w, k)
+        layer[name] = {"q": q, "alpha": a, "zero": z, "group": k}
+    return layer
+
+
+def _bf16(v):
+    return torch.tensor(np.asarray(v, dtype=np.float64)).float().to(torch.bfloat16).double().numpy()
+
+
+def test_mixnmatch_constant_weights_closed_form():
+    # Constant weight matrices quantize to code 0 with alpha = 1, z = -c, so
+    # every slice dequantizes to c exactly and each linear returns
+    # c * sum(input) in every output.  One layer, worked out directly.
+    h_dim, f_dim = 8, 16
+    consts = {"q": 0.125, "k": -0.5, "v": 0.25, "o": -0.0625, "up": 0.03125,
+              "gate": 0.5, "down": 0.25}
+    rg = np.random.default_rng(5)
+    x = oracle.bf16_bits_from_float(rg.standard_normal((2, h_dim)))
+    for r in (8, 4, 2):
+        got = oracle.mixnmatch_forward([_const_layer(h_dim, f_dim, consts, r)], x)
+        h0 = oracle.float_from_bf16_bits(x)
+        a = _bf16(h0 / np.sqrt(np.mean(h0 ** 2, axis=1, keepdims=True)))
+        sa = a.sum(axis=1, keepdims=True)
+        qv, uv, gv = consts["q"] * sa, consts["up"] * sa, consts["gate"] * sa
+        o = consts["o"] * h_dim * _bf16(qv)
+        d = consts["down"] * f_dim * _bf16(uv * gv)
+        assert np.allclose(got, h0 + o + d, rtol=1e-14, atol=1e-14)
+
+
+def test_mixnmatch_zero_weights_is_identity():
+    consts = {k: 0.0 for k in oracle.LAYER_LINEARS}
+    rg = np.random.default_rng(6)
+    x = oracle.bf16_bits_from_float(rg.standard_normal((1, 8)))
+    layers = [_const_layer(8, 16, consts, r) for r in (8, 2, 4)]
+    assert np.array_equal(oracle.mixnmatch_forward(layers, x), oracle.float_from_bf16_bits(x))
+
+
+def test_mixnmatch_input_scale_property():
+    # The normalization makes a layer's update o + d invariant to scaling its
+    # input by a power of two, exactly.
+    rg = np.random.default_rng(8)
+    layer = {"r": 4}
+    for name, (n, k) in {"q": (16, 16), "k": (4, 16), "v": (4, 16), "o": (16, 16),
+                         "up": (32, 16), "gate": (32, 16), "down": (16, 32)}.items():
+        q, a, z = oracle.quantize_minmax((rg.standard_normal((n, k)) * 0.02).astype(np.float32), k)
+        layer[name] = {"q": q, "alpha": a, "zero": z, "group": k}
+    x = oracle.bf16_bits_from_float(rg.standard_normal((1, 16)))
+    x2 = oracle.bf16_bits_from_float(2.0 * oracle.float_from_bf16_bits(x))
+    t1, t2 = [], []
+    oracle.mixnmatch_forward([layer], x, t1)
+    oracle.mixnmatch_forward([layer], x2, t2)
+    assert np.array_equal(t1[0]["a_bits"], t2[0]["a_bits"])
+    assert np.array_equal(t1[0]["o"], t2[0]["o"]) and np.array_equal(t1[0]["d"], t2[0]["d"])
+    assert np.any(t1[0]["o"] != 0)
+
+
+def test_effective_bits_of_the_stack_pattern():
+    from nested_int_matmul_amd import inputs
+
+    rs = inputs.mixnmatch_pattern(32)
+    assert rs.count(8) == 16 and rs.count(4) == 11 and rs.count(2) == 5
+    assert [i for i, r in enumerate(rs) if r == 2] == [10, 13, 16, 19, 22]
+    layers = [{"r": r, **{nm: {"q": np.zeros((1, 1))} for nm in oracle.LAYER_LINEARS}} for r in rs]
+    assert oracle.effective_bits(layers) == 5.6875
+
+
+def test_oracle_and_library_share_no_code():
+    root = os.path.dirname(GOLDEN)
+    root = os.path.dirname(root)
+    for dirpath, _, files in os.walk(os.path.join(root, "oracle")):
+        for f in files:
+            if f.endswith(".py"):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "nested_int_matmul_amd" not in src.replace("(nested_int_matmul_amd)", "")
+    for dirpath, _, files in os.walk(os.path.join(root, "nested_int_matmul_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src
