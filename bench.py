@@ -1,0 +1,404 @@
+"""Benchmark of the sliced-integer (Matryoshka-nested) matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+
+One step is one decode pass (batch 1) through the Gemma-2-9B MLP matrices
+(up/gate 3584 -> 14336, down 14336 -> 3584, per-channel scales, 0.1% x10
+outlier weights) at each slice precision r = 8, 4, 2: three grouped GEMV
+launches (one per r, the three matrices in each).  Weights rotate over
+>= 1 GiB of distinct copies per r so that the 256 MB last-level cache cannot
+serve them.  `value` is the effective HBM bandwidth over the step:
+algorithmic bytes (packed plane + fp32 alpha/zero + bf16 x + fp32 y) per
+second.
+
+The same JSON line also carries:
+  roofline      the dominant kernel (by time) against 8 TB/s, its duration
+                measured live with HIP events on the launch stream;
+  rows          the other steps of the path measured in the same run: pack,
+                small-batch GEMM (Mistral shapes, g128), prefill GEMM
+                (M = 2048) and the 32-layer Mix'n'Match stack;
+  cpu_baseline  the float64 CPU oracle on the same workload (host cores).
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s (GEMV) & TFLOP/s (GEMM) of sliced-int matmul at r=8/4/2"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30
+RS = (8, 4, 2)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_gemma9b_mlp.md")
+GEMV_SOURCE = os.path.join(ROOT, "nested_int_matmul_amd", "csrc", "gemv.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def linear_bytes(n, k, r, group, m):
+    """Algorithmic bytes of one product: packed plane, fp32 alpha and zero,
+    bf16 activations, fp32 outputs."""
+    g = k // group
+    return n * k * r // 8 + 8 * n * g + 2 * m * k + 4 * m * n
+
+
+class Timer:
+    """HIP events on the given stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+# --------------------------------------------------------------------------- main step
+
+def setup_gemma(torch, mq, inputs, dev):
+    mats = []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=i, outlier_frac=1e-3)
+        codes, alpha, zero = mq.quantize(w, k)
+        del w
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        x = torch.from_numpy(xb.view("int16")).to(dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        mats.append(dict(name=name, N=n, K=k, codes=codes, alpha=alpha, zero=zero, x=x, y=y))
+    planes = {}
+    for r in RS:
+        base = [mq.pack(m["codes"], r) for m in mats]
+        mlp_bytes = sum(linear_bytes(m["N"], m["K"], r, m["K"], 1) for m in mats)
+        ncopy = max(2, -(-ROTATE_BYTES // mlp_bytes))
+        planes[r] = [base] + [[p.clone() for p in base] for _ in range(ncopy - 1)]
+    for m in mats:
+        del m["codes"]
+    torch.cuda.synchronize()
+    return mats, planes
+
+
+def gemma_problems(mq, mats, plane_set):
+    return [dict(packed=p, alpha=m["alpha"], zero=m["zero"], x=m["x"], y=m["y"], N=m["N"],
+                 K=m["K"], group=m["K"]) for m, p in zip(mats, plane_set)]
+
+
+def run_main(torch, mq, inputs, dev, steps, warmup):
+    mats, planes = setup_gemma(torch, mq, inputs, dev)
+    stream = torch.cuda.current_stream()
+    T = Timer(torch, stream)
+    # prebuilt problem lists (argument marshalling is outside the GPU work)
+    probs = {r: [gemma_problems(mq, mats, ps) for ps in planes[r]] for r in RS}
+    step_bytes = sum(linear_bytes(m["N"], m["K"], r, m["K"], 1) for m in mats for r in RS)
+
+    def step(i, evs=None):
+        for r in RS:
+            pl = probs[r][i % len(probs[r])]
+            if evs is not None:
+                evs[r].append(T.event())
+            mq.gemv_grouped(pl, r, 1)
+            if evs is not None:
+                evs[r].append(T.event())
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = {r: [] for r in RS}
+    t0 = T.event()
+    for i in range(steps):
+        step(warmup + i, evs)
+    t1 = T.event()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per_r_us = {}
+    for r in RS:
+        e = evs[r]
+        durs = [e[2 * j].elapsed_time(e[2 * j + 1]) * 1e3 for j in range(steps)]
+        per_r_us[r] = sum(durs) / len(durs)
+    return dict(total_ms=total_ms, step_bytes=step_bytes, per_r_us=per_r_us, mats=mats)
+
+
+# --------------------------------------------------------------------------- roofline
+
+def traffic_for(source_sha, kernel):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy of known size), if recorded for the
+    current kernel source; None otherwise."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip().strip("-* ")] = v.strip().strip("`")
+    if rec.get("gemv.hip sha256") != source_sha:
+        return None
+    v = rec.get(f"traffic bytes per launch {kernel}")
+    return float(v) if v else None
+
+
+def sha256(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+# --------------------------------------------------------------------------- extra rows
+
+def time_loop(torch, fn, iters, warmup=3):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / iters  # us
+
+
+def run_rows(torch, mq, inputs, dev):
+    rows = {}
+    # a1: slice-and-pack of the Gemma down matrix (reads N*K, writes N*K*r/8)
+    n, k = inputs.GEMMA9B_MLP["down"]
+    w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=2, outlier_frac=1e-3)
+    codes, _, _ = mq.quantize(w, k)
+    del w
+    copies = [codes] + [codes.clone() for _ in range(6)]
+    pack = {}
+    for r in RS:
+        outs = [torch.empty((n, k * r // 8), dtype=torch.uint8, device=dev) for _ in copies]
+        us = time_loop(torch, lambda i: mq.pack(copies[i % 7], r, out=outs[i % 7]), 21)
+        b = n * k * (1 + r / 8)
+        pack[f"r{r}"] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1)}
+    rows["pack_gemma_down"] = pack
+    del copies, codes
+    # a3: small-batch GEMM, Mistral shapes, group 128
+    small = {}
+    for (N2, K2) in inputs.MISTRAL_SMALL_SHAPES:
+        w = inputs.device_gaussian_weights("mistral_small", N2, K2, dev, matrix=N2 // 4096)
+        c2, a2, z2 = mq.quantize(w, 128)
+        del w
+        for r in (4, 2):
+            pl = mq.pack(c2, r)
+            b1 = linear_bytes(N2, K2, r, 128, 0)
+            nc = max(2, -(-ROTATE_BYTES // b1))
+            pls = [pl] + [pl.clone() for _ in range(nc - 1)]
+            for M2 in (16, 64):
+                xb = inputs.activations_bf16("mistral_small", M2, K2, heavy_channels=8)
+                x2 = torch.from_numpy(xb.view("int16")).to(dev)
+                y2 = torch.empty((M2, N2), dtype=torch.float32, device=dev)
+                us = time_loop(torch, lambda i: mq.gemm(pls[i % nc], r, a2, z2, 128, N2, K2, x2,
+                                                        out=y2), 40)
+                b = linear_bytes(N2, K2, r, 128, M2)
+                small[f"M{M2}_N{N2}_K{K2}_r{r}"] = {
+                    "us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                    "TFLOP/s": round(2 * M2 * N2 * K2 / us / 1e6, 2)}
+            del pls, pl
+        del c2, a2, z2
+    rows["gemm_mistral_small"] = small
+    # a4: prefill GEMM
+    M, K, N = inputs.PREFILL_SHAPE
+    w = inputs.device_gaussian_weights("prefill", N, K, dev)
+    c5, a5, z5 = mq.quantize(w, 128)
+    del w
+    xb = inputs.activations_bf16("prefill", M, K)
+    x5 = torch.from_numpy(xb.view("int16")).to(dev)
+    y5 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    pre = {}
+    for r in (4, 2, 8):
+        pl = mq.pack(c5, r)
+        us = time_loop(torch, lambda i: mq.gemm(pl, r, a5, z5, 128, N, K, x5, out=y5), 10)
+        tf = 2 * M * N * K / us / 1e6
+        pre[f"r{r}"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+                        "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    rows["gemm_prefill_M2048"] = pre
+    del c5, a5, z5, x5, y5
+    # a5: Mix'n'Match stack, 32 Mistral-7B layers, batch 1
+    rows["mixnmatch_mistral7b_32l"] = run_stack(torch, mq, inputs, dev)
+    return rows
+
+
+def run_stack(torch, mq, inputs, dev, n_layers=32):
+    rs = inputs.mixnmatch_pattern(n_layers)
+    layers = []
+    codes_bytes = 0
+    meta_bytes = 0
+    for li, r in enumerate(rs):
+        L = {"r": r}
+        for mi, name in enumerate(mq.LAYER_LINEARS):
+            n, k = inputs.MISTRAL_LAYER[name]
+            w = inputs.device_gaussian_weights("mistral_stack", n, k, dev, layer=li, matrix=mi)
+            codes, a, z = mq.quantize(w, k)
+            del w
+            L[name] = {"packed": mq.pack(codes, r), "alpha": a, "zero": z, "N": n, "K": k,
+                       "group": k}
+            del codes
+            codes_bytes += n * k * r // 8
+            meta_bytes += 8 * n
+        layers.append(L)
+    arr = mq.make_layers(layers)
+    H = inputs.MISTRAL_LAYER["q"][0]
+    ws = torch.empty(mq.mixnmatch_workspace_bytes(arr, 1), dtype=torch.uint8, device=dev)
+    xb = inputs.activations_bf16("mistral_stack", 1, H)
+    x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16).float()
+    h = x.clone()
+
+    def fwd(i):
+        h.copy_(x)
+        mq.mixnmatch_forward(arr, h, ws)
+
+    us = time_loop(torch, fwd, 10, warmup=2)
+    b = codes_bytes + meta_bytes
+    out = {"us_per_token": round(us, 1), "GB/s": round(b / us / 1e3, 1),
+           "codes_GB": round(codes_bytes / 1e9, 3), "layers": n_layers,
+           "r_pattern": "".join(str(r) for r in rs), "avg_bits": sum(rs) / len(rs)}
+    del layers, arr, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(inputs):
+    """The float64 oracle on the host: slice -> dequantize -> product for the
+    three Gemma MLP matrices at r = 8, 4, 2 (the same work as one GPU step)
+    on seeded numpy inputs of the same law."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    data = []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        w = inputs.gaussian_weights("gemma9b_mlp", n, k, matrix=i, outlier_frac=1e-3)
+        q, a, z = oracle.quantize_minmax(w, k)
+        del w
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        data.append((q, a, z, k, xb, n))
+    t0 = time.perf_counter()
+    nbytes = 0
+    for r in RS:
+        for q, a, z, k, xb, n in data:
+            y = oracle.linear(xb, q, a, z, k, r)
+            assert np.all(np.isfinite(y))
+            nbytes += linear_bytes(n, k, r, k, 1)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": ("one full step: the 3 Gemma-2-9B MLP matrices at r=8,4,2, batch 1, "
+                       f"float64 numpy oracle, {dt:.1f} s")}
+
+
+# --------------------------------------------------------------------------- entry
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-rows", action="store_true", help="skip the extra per-row timings")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
+              "the multi-GPU sharding is a design note, not a measured path.", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import nested_int_matmul_amd as mq
+    from nested_int_matmul_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", flush=True)
+        sys.exit(2)
+    mq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log("main step: Gemma-2-9B MLP decode, r = 8/4/2")
+    res = run_main(torch, mq, inputs, dev, args.steps, args.warmup)
+    ms_per_step = res["total_ms"] / args.steps
+    value = res["step_bytes"] * args.steps / (res["total_ms"] * 1e-3) / 1e9
+
+    # dominant kernel: the grouped GEMV launch with the largest time per step
+    per_r = res["per_r_us"]
+    r_dom = max(per_r, key=lambda r: per_r[r])
+    bytes_dom = sum(linear_bytes(m["N"], m["K"], r_dom, m["K"], 1) for m in res["mats"])
+    achieved = bytes_dom / (per_r[r_dom] * 1e-6) / 1e9
+    kernel_name = f"skinny_kernel<{r_dom}, per-channel>"
+    traffic = traffic_for(sha256(GEMV_SOURCE), f"r{r_dom}")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": kernel_name, "launch_us": round(per_r[r_dom], 3),
+                "bytes_per_launch": bytes_dom,
+                "per_r_launch_us": {f"r{r}": round(v, 3) for r, v in per_r.items()}}
+    del res
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    rows = None
+    if not args.no_rows:
+        log("extra rows: pack, small GEMM, prefill GEMM, Mix'n'Match stack")
+        rows = run_rows(torch, mq, inputs, dev)
+    cpu = None
+    if not args.no_cpu:
+        log("CPU baseline: float64 oracle")
+        cpu = cpu_baseline(inputs)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gemma2_9b_mlp_decode", "M": 1,
+                   "matrices": "up/gate 3584->14336, down 14336->3584",
+                   "r": list(RS), "scales": "per-channel fp32 alpha,z",
+                   "weights": "N(0,0.02), 0.1% x10 outliers", "rotation_bytes": ROTATE_BYTES},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * mq.h: C ABI of the Matryoshka-nested integer matmul library (libmq.so),
+ * gfx950 (MI355X) only.
+ *
+ * The method ("Matryoshka Quantization" explainer, §3.4): a model is stored
+ * once as unsigned 8-bit codes q with an fp32 scale alpha and zero point z per
+ * weight vector (min-max quantizer, Eq. 1).  At serve time the codes are
+ * sliced to their r most significant bits with rounding and clamping,
+ *   S(q, r) = clamp(round(q / 2^(8-r)), 0, 2^r - 1) * 2^(8-r)       (Eq. 6),
+ * dequantized as (S(q, r) - z) * alpha (the sliced value is used as if it
+ * were an int8 value, "The Bit-Slicing Operator"), and multiplied by bf16
+ * activations with fp32 accumulation.  Different layers may use different r
+ * over the one stored model ("Mix'n'Match").
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc or torch CUDA
+ *    tensors), owned by the caller, which keeps them alive until the work
+ *    enqueued on `stream` has finished.  Inputs and outputs must not overlap.
+ *  - A weight matrix has logical shape [N, K] (N outputs, K inputs), stored
+ *    row-major with K contiguous: the transpose of the pages' W in X W.
+ *  - `group` is the length of the weight vector that owns one (alpha, z):
+ *    group == K (per output channel) or group == 128 (128 consecutive inputs
+ *    of a row).  alpha and zero are fp32 [N, K / group] row-major.
+ *  - Activations are bf16 bit patterns (uint16_t) [M, K] row-major; outputs
+ *    are fp32 [M, N] row-major.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    and the call returns without synchronizing.
+ *  - Every argument is validated before anything is enqueued: on an error
+ *    nothing is enqueued and no output is touched.  A failed launch returns
+ *    MQ_ERR_HIP and records the hipError_t (see mq_last_hip_error).  Faults
+ *    during execution surface at the caller's next synchronization.
+ *  - Entry points other than the explicitly allocating ones allocate no
+ *    device memory; the library keeps no state except cached device
+ *    properties.  Calls are thread-safe.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mq_status {
+  MQ_OK = 0,
+  MQ_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  MQ_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)       */
+  MQ_ERR_PRECISION = 3, /* r is not 2, 4 or 8                                  */
+  MQ_ERR_GROUP = 4,     /* group is neither K nor 128                          */
+  MQ_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                    */
+  MQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than required          */
+  MQ_ERR_DEVICE = 7,    /* the current device is not a gfx950                  */
+  MQ_ERR_HIP = 8        /* a HIP runtime call failed                            */
+} mq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mq_status_string(int status);
+
+/* hipError_t value recorded by the last MQ_ERR_HIP returned on this thread
+ * (0 if none). */
+int mq_last_hip_error(void);
+
+/* Library version string, e.g. "mq 0.1 gfx950". */
+const char* mq_version(void);
+
+/* Bytes of one packed r-bit plane of an [N, K] matrix: N * K * r / 8.
+ * Returns 0 for r not in {2, 4, 8} or negative sizes. */
+size_t mq_packed_bytes(int64_t N, int64_t K, int r);
+
+/*
+ * mq_quantize: min-max quantization of fp32 weights to 8-bit codes
+ * ("Matryoshka Quantization" explainer, §3.4 "Quantization Primitives", Eq. 1,
+ * with c = 8).  For every weight vector v (group consecutive entries of a row):
+ *   alpha = fp32((max v - min v) / 255),  z = fp32(-min v / alpha),
+ *   q = clamp(floor(v / alpha + z + 1/2), 0, 255),
+ * evaluated in IEEE float64 from the stored fp32 alpha and z.  A constant
+ * vector gets alpha = 1, z = -min (all codes 0).
+ *   w      fp32 [N, K], finite values
+ *   codes  uint8 [N, K] (output)
+ *   alpha  fp32 [N, K/group] (output), zero fp32 [N, K/group] (output)
+ * Sizes: N >= 1, K >= 1, group divides K and group == K or group == 128.
+ */
+mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group,
+                      uint8_t* codes, float* alpha, float* zero, void* stream);
+
+/*
+ * mq_pack: slice stored codes to r bits and pack them (Eq. 6; the explainer's
+ * §2 and "The Bit-Slicing Operator": a lower-precision model is extracted from
+ * the one stored int8 model by slicing).  Writes, for every code,
+ *   t = min((q + 2^(7-r)) >> (8-r), 2^r - 1)   (r < 8),   t = q   (r = 8),
+ * the index with S(q, r) = t * 2^(8-r), packed 8/r per byte: byte j of a row
+ * holds elements j*8/r + i in bits [i*r, i*r + r) (little-endian fields).
+ *   codes   uint8 [N, K]
+ *   packed  uint8 [N, K*r/8] (output), 16-byte aligned
+ * Sizes: N >= 1, K >= 64, K % 64 == 0; r in {2, 4, 8}.
+ */
+mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
+                  void* stream);
+
+/*
+ * mq_gemv: decode-shaped product against an r-bit plane, M <= 8 rows of
+ * activations:
+ *   y[m, n] = sum_k x[m, k] * (S(q[n, k], r) - z[n, g]) * alpha[n, g],
+ *   g = k / group,
+ * with the slice read from `packed` (the output of mq_pack for the same r),
+ * bf16 x, fp32 accumulation and an fp32 result.
+ *   packed  uint8 [N, K*r/8], 16-byte aligned
+ *   alpha, zero  fp32 [N, K/group]
+ *   x       bf16 bits [M, K], 16-byte aligned
+ *   y       fp32 [M, N] (output), 16-byte aligned
+ * Sizes: 1 <= M <= 8, N >= 1, K >= 64, K % 64 == 0, K <= 65536.
+ */
+mq_status mq_gemv(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                  int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                  float* y, void* stream);
+
+/* One product of a grouped GEMV launch (see mq_gemv_grouped). */
+typedef struct mq_gemv_problem {
+  const uint8_t* packed; /* uint8 [N, K*r/8]                 */
+  const float* alpha;    /* fp32 [N, K/group]                */
+  const float* zero;     /* fp32 [N, K/group]                */
+  const uint16_t* x;     /* bf16 bits [M, K]                 */
+  float* y;              /* fp32 [M, N] (output)             */
+  int64_t N, K, group;
+} mq_gemv_problem;
+
+/*
+ * mq_gemv_grouped: several independent mq_gemv products at the same r and M
+ * in one launch (for example the three matrices of a feed-forward block, or
+ * the projections that share one input).  Same definitions, constraints and
+ * result as calling mq_gemv on each problem; outputs must not overlap.
+ * 1 <= count <= 8.
+ */
+mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int64_t M,
+                          void* stream);
+
+/*
+ * mq_gemm: the same product for any number of activation rows M >= 1 (small
+ * batches and prefill), on bf16 matrix cores with fp32 accumulation.  Same
+ * definitions and layouts as mq_gemv; M <= 8 takes the mq_gemv kernel.
+ *   workspace  device scratch of at least mq_gemm_workspace_bytes(M, N, K, group)
+ *              bytes (may be NULL when that is 0), 256-byte aligned
+ * Sizes: M >= 1, N >= 1, K >= 64, K % 64 == 0, K <= 65536.
+ */
+size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                  int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mix'n'Match stack ("Matryoshka Quantization" explainer, §3.4 "Mix'n'Match
+ * and Interpolative Slicing"): a stack of layers over one stored int8 model,
+ * each layer sliced to its own r.
+ *
+ * Layer dataflow (the pages give none; this is the library's definition):
+ *   a = bf16(h / sqrt(mean(h^2)))            (per row, fp32 arithmetic)
+ *   q = W_q a, k = W_k a, v = W_v a, u = W_up a, g = W_gate a
+ *   o = W_o bf16(q),  d = W_down bf16(u * g)  (u * g in fp32)
+ *   h = h + o + d                             (fp32 residual stream)
+ * k and v are computed and written to the workspace but not consumed.
+ * Shapes: q, o: [H, H]; k, v: [Hkv, H]; up, gate: [F, H]; down: [H, F];
+ * the same H, Hkv, F in every layer.  Each mq_linear holds the plane packed
+ * at its layer's r.
+ */
+typedef struct mq_linear {
+  const uint8_t* packed; /* uint8 [N, K*r/8] at the layer's r */
+  const float* alpha;    /* fp32 [N, K/group]                 */
+  const float* zero;     /* fp32 [N, K/group]                 */
+  int64_t N, K, group;
+} mq_linear;
+
+typedef struct mq_layer {
+  int r; /* 2, 4 or 8 */
+  mq_linear q, k, v, o, up, gate, down;
+} mq_layer;
+
+/* Workspace bytes for mq_mixnmatch_forward (0 on invalid shapes). */
+size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_t M);
+
+/*
+ * Byte offsets inside the workspace of the intermediates of the LAST layer
+ * run, valid after the call's work completes: a (bf16 [M, H]), q, k, v
+ * (fp32 [M, H] / [M, Hkv]), u, g (fp32 [M, F]), o, d (fp32 [M, H]).
+ * offsets must have room for 8 entries, in that order.
+ */
+mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, int64_t M,
+                                         size_t* offsets);
+
+/*
+ * mq_mixnmatch_forward: run n_layers layers in place on the fp32 residual
+ * stream h [M, H] (16-byte aligned).  1 <= M <= 8, 1 <= n_layers.
+ * `layers` is a HOST array read during the call only.
+ */
+mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, int64_t M,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MQ_H */

@@ -1,0 +1,243 @@
+"""Matryoshka-nested integer matmul on MI355X (gfx950).
+
+A thin Python binding over the C ABI of libmq.so (include/mq.h): argument
+marshalling only; every step of the computation runs in the library's HIP
+kernels.  torch is used for device memory and streams.
+
+    import nested_int_matmul_amd as mq
+    codes, alpha, zero = mq.quantize(w_fp32_cuda, group=128)
+    plane = mq.pack(codes, r=4)
+    y = mq.gemm(plane, 4, alpha, zero, 128, x_bf16_cuda)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmq.so")
+
+MQ_OK = 0
+STATUS_NAMES = {
+    0: "MQ_OK", 1: "MQ_ERR_NULL", 2: "MQ_ERR_SHAPE", 3: "MQ_ERR_PRECISION",
+    4: "MQ_ERR_GROUP", 5: "MQ_ERR_ALIGN", 6: "MQ_ERR_WORKSPACE", 7: "MQ_ERR_DEVICE",
+    8: "MQ_ERR_HIP",
+}
+
+# Every exported symbol of include/mq.h.
+EXPORTS = (
+    "mq_status_string", "mq_last_hip_error", "mq_version", "mq_packed_bytes",
+    "mq_quantize", "mq_pack", "mq_gemv", "mq_gemv_grouped", "mq_gemm_workspace_bytes",
+    "mq_gemm", "mq_mixnmatch_workspace_bytes", "mq_mixnmatch_workspace_offsets",
+    "mq_mixnmatch_forward",
+)
+
+
+class MQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mq_status_string(status).decode()
+        if status == 8:
+            msg += f" (hipError {lib().mq_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+class GemvProblem(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
+                ("zero", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("group", ctypes.c_int64)]
+
+
+class Linear(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
+                ("zero", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("group", ctypes.c_int64)]
+
+
+LAYER_LINEARS = ("q", "k", "v", "o", "up", "gate", "down")
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_int)] + [(n, Linear) for n in LAYER_LINEARS]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmq.so (built in-tree by nested_int_matmul_amd/build.py).  Raises
+    if it is missing: there is no fallback implementation."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m nested_int_matmul_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.mq_status_string.restype = ctypes.c_char_p
+    L.mq_status_string.argtypes = [i32]
+    L.mq_last_hip_error.restype = i32
+    L.mq_version.restype = ctypes.c_char_p
+    L.mq_packed_bytes.restype = sz
+    L.mq_packed_bytes.argtypes = [i64, i64, i32]
+    L.mq_quantize.restype = i32
+    L.mq_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    L.mq_pack.restype = i32
+    L.mq_pack.argtypes = [vp, i64, i64, i32, vp, vp]
+    L.mq_gemv.restype = i32
+    L.mq_gemv.argtypes = [vp, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp]
+    L.mq_gemv_grouped.restype = i32
+    L.mq_gemv_grouped.argtypes = [ctypes.POINTER(GemvProblem), i32, i32, i64, vp]
+    L.mq_gemm_workspace_bytes.restype = sz
+    L.mq_gemm_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.mq_gemm.restype = i32
+    L.mq_gemm.argtypes = [vp, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]
+    L.mq_mixnmatch_workspace_bytes.restype = sz
+    L.mq_mixnmatch_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i32, i64]
+    L.mq_mixnmatch_workspace_offsets.restype = i32
+    L.mq_mixnmatch_workspace_offsets.argtypes = [ctypes.POINTER(Layer), i32, i64,
+                                                 ctypes.POINTER(sz)]
+    L.mq_mixnmatch_forward.restype = i32
+    L.mq_mixnmatch_forward.argtypes = [ctypes.POINTER(Layer), i32, vp, i64, vp, sz, vp]
+    _LIB = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != MQ_OK:
+        raise MQError(status, where)
+
+
+def _stream(stream=None):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _bits16(x):
+    """bf16 activations as a 16-bit view (bf16 or int16/uint16 tensors)."""
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        return x
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError("activations must be bf16 (or their 16-bit patterns)")
+
+
+# ----------------------------------------------------------------- entry points
+
+def packed_bytes(N: int, K: int, r: int) -> int:
+    return int(lib().mq_packed_bytes(N, K, r))
+
+
+def quantize(w, group: int, stream=None):
+    """Eq. 1 min-max quantization on the GPU: fp32 [N, K] -> (codes uint8
+    [N, K], alpha fp32 [N, K/group], zero fp32 [N, K/group])."""
+    import torch
+
+    n, k = w.shape
+    g = k // group if group else 0
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    alpha = torch.empty((n, max(g, 1)), dtype=torch.float32, device=w.device)
+    zero = torch.empty_like(alpha)
+    _check(lib().mq_quantize(_ptr(w), n, k, group, _ptr(codes), _ptr(alpha), _ptr(zero),
+                             _stream(stream)), "mq_quantize")
+    return codes, alpha, zero
+
+
+def pack(codes, r: int, out=None, stream=None):
+    """Slice uint8 codes [N, K] to r bits and pack: uint8 [N, K*r/8]."""
+    import torch
+
+    n, k = codes.shape
+    if out is None:
+        out = torch.empty((n, k * r // 8), dtype=torch.uint8, device=codes.device)
+    _check(lib().mq_pack(_ptr(codes), n, k, r, _ptr(out), _stream(stream)), "mq_pack")
+    return out
+
+
+def gemv(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, stream=None):
+    """y = x @ dequant(S(q, r))^T for M <= 8 rows of bf16 x: fp32 [M, N]."""
+    import torch
+
+    x = _bits16(x)
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _check(lib().mq_gemv(_ptr(packed), r, _ptr(alpha), _ptr(zero), group, N, K, _ptr(x), m,
+                         _ptr(out), _stream(stream)), "mq_gemv")
+    return out
+
+
+def gemv_grouped(problems, r: int, M: int, stream=None):
+    """problems: list of dicts with packed, alpha, zero, x, y (tensors), N, K, group."""
+    arr = (GemvProblem * len(problems))()
+    for i, p in enumerate(problems):
+        arr[i] = GemvProblem(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
+                             _bits16(p["x"]).data_ptr(), p["y"].data_ptr(), p["N"], p["K"],
+                             p["group"])
+    _check(lib().mq_gemv_grouped(arr, len(problems), r, M, _stream(stream)), "mq_gemv_grouped")
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:
+    return int(lib().mq_gemm_workspace_bytes(M, N, K, group))
+
+
+def gemm(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, workspace=None,
+         stream=None):
+    """y = x @ dequant(S(q, r))^T for any M: fp32 [M, N]."""
+    import torch
+
+    x = _bits16(x)
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    need = gemm_workspace_bytes(m, N, K, group)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mq_gemm(_ptr(packed), r, _ptr(alpha), _ptr(zero), group, N, K, _ptr(x), m,
+                         _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)), "mq_gemm")
+    return out
+
+
+def make_layers(layers):
+    """layers: list of dicts {"r": r, name: {"packed", "alpha", "zero", "N", "K", "group"}}
+    -> ctypes array of Layer (keeps no references: the caller keeps the tensors)."""
+    arr = (Layer * len(layers))()
+    for i, L in enumerate(layers):
+        kw = {"r": L["r"]}
+        for n in LAYER_LINEARS:
+            p = L[n]
+            kw[n] = Linear(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
+                           p["N"], p["K"], p["group"])
+        arr[i] = Layer(**kw)
+    return arr
+
+
+def mixnmatch_workspace_bytes(layer_arr, M: int) -> int:
+    return int(lib().mq_mixnmatch_workspace_bytes(layer_arr, len(layer_arr), M))
+
+
+def mixnmatch_workspace_offsets(layer_arr, M: int):
+    off = (ctypes.c_size_t * 8)()
+    _check(lib().mq_mixnmatch_workspace_offsets(layer_arr, len(layer_arr), M, off),
+           "mq_mixnmatch_workspace_offsets")
+    return list(off)
+
+
+def mixnmatch_forward(layer_arr, h, workspace, stream=None):
+    """Run the stack in place on the fp32 residual stream h [M, H]."""
+    m = h.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().mq_mixnmatch_forward(layer_arr, len(layer_arr), _ptr(h), m, _ptr(workspace),
+                                      ws_bytes, _stream(stream)), "mq_mixnmatch_forward")
+    return h

@@ -1,0 +1,333 @@
+// C ABI of libmq: argument validation, status codes, dispatch to the gfx950
+// kernels.  Nothing is enqueued unless every argument is valid.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/mq.h"
+#include "mq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+mq_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MQ_ERR_HIP;
+}
+
+// Per-device cache of "is gfx950" (0 unknown, 1 yes, 2 no).
+std::atomic<int> g_dev_ok[64];
+
+mq_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return MQ_ERR_DEVICE;
+  int s = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(s, std::memory_order_relaxed);
+  }
+  return s == 1 ? MQ_OK : MQ_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_r(int r) { return r == 2 || r == 4 || r == 8; }
+
+constexpr int64_t kMaxK = 65536;
+constexpr int64_t kMaxPlaneBytes = (int64_t)1 << 31;
+
+// Shape checks shared by the products.
+mq_status check_matrix(int64_t N, int64_t K, int64_t group, int r) {
+  if (!valid_r(r)) return MQ_ERR_PRECISION;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK) return MQ_ERR_SHAPE;
+  if (N * K > kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (!(group == K || (group == 128 && K % 128 == 0))) return MQ_ERR_GROUP;
+  return MQ_OK;
+}
+
+mq_status check_product(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                        int64_t group, int64_t N, int64_t K, const void* x, const float* y) {
+  if (!packed || !alpha || !zero || !x || !y) return MQ_ERR_NULL;
+  mq_status s = check_matrix(N, K, group, r);
+  if (s != MQ_OK) return s;
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(y)) return MQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(zero) & 3u))
+    return MQ_ERR_ALIGN;
+  return MQ_OK;
+}
+
+mq_status skinny_run(mq::SkinnyArgs& a, int r, bool grouped, hipStream_t stream) {
+  hipError_t e = mq::launch_skinny(a, r, grouped, stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mq_status_string(int status) {
+  switch (status) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_ERR_NULL: return "MQ_ERR_NULL: a required pointer is NULL";
+    case MQ_ERR_SHAPE: return "MQ_ERR_SHAPE: a size is out of range";
+    case MQ_ERR_PRECISION: return "MQ_ERR_PRECISION: r must be 2, 4 or 8";
+    case MQ_ERR_GROUP: return "MQ_ERR_GROUP: group must be K or 128 (with K % 128 == 0)";
+    case MQ_ERR_ALIGN: return "MQ_ERR_ALIGN: a pointer is not suitably aligned";
+    case MQ_ERR_WORKSPACE: return "MQ_ERR_WORKSPACE: workspace missing or too small";
+    case MQ_ERR_DEVICE: return "MQ_ERR_DEVICE: the current device is not a gfx950";
+    case MQ_ERR_HIP: return "MQ_ERR_HIP: a HIP runtime call failed";
+    default: return "unknown mq_status";
+  }
+}
+
+int mq_last_hip_error(void) { return g_last_hip_error; }
+
+const char* mq_version(void) { return "mq 0.1 gfx950"; }
+
+size_t mq_packed_bytes(int64_t N, int64_t K, int r) {
+  if (!valid_r(r) || N < 0 || K < 0) return 0;
+  return (size_t)(N * K * r / 8);
+}
+
+mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* codes,
+                      float* alpha, float* zero, void* stream) {
+  if (!w || !codes || !alpha || !zero) return MQ_ERR_NULL;
+  if (N < 1 || K < 1 || N * K > kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (!(group == K || (group == 128 && K % 128 == 0))) return MQ_ERR_GROUP;
+  if ((reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
+      (reinterpret_cast<uintptr_t>(zero) & 3u))
+    return MQ_ERR_ALIGN;
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_quantize(w, N, K, group, codes, alpha, zero, (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
+                  void* stream) {
+  if (!codes || !packed) return MQ_ERR_NULL;
+  if (!valid_r(r)) return MQ_ERR_PRECISION;
+  if (N < 1 || K < 64 || K % 64 != 0 || N * K > kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(packed)) return MQ_ERR_ALIGN;
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_pack(codes, N, K, r, packed, (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+mq_status mq_gemv(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                  int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                  void* stream) {
+  mq_status s = check_product(packed, r, alpha, zero, group, N, K, x, y);
+  if (s != MQ_OK) return s;
+  if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
+  s = check_device();
+  if (s != MQ_OK) return s;
+  mq::SkinnyArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.count = 1;
+  a.M = (int)M;
+  a.p[0] = mq::SkinnyProblem{packed, alpha, zero, x, nullptr, y, (int)N, (int)K, (int)group,
+                             mq::kXBf16, 0, 0, 0, 0};
+  return skinny_run(a, r, group != K, (hipStream_t)stream);
+}
+
+mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int64_t M,
+                          void* stream) {
+  if (!problems) return MQ_ERR_NULL;
+  if (count < 1 || count > mq::kMaxProblems) return MQ_ERR_SHAPE;
+  if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
+  int n_grouped = 0;
+  for (int i = 0; i < count; ++i) {
+    const mq_gemv_problem& p = problems[i];
+    mq_status s = check_product(p.packed, r, p.alpha, p.zero, p.group, p.N, p.K, p.x, p.y);
+    if (s != MQ_OK) return s;
+    n_grouped += (p.group != p.K) ? 1 : 0;
+  }
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  // One launch per scale granularity present.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool grouped = pass == 1;
+    if (grouped ? n_grouped == 0 : n_grouped == count) continue;
+    mq::SkinnyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.M = (int)M;
+    for (int i = 0; i < count; ++i) {
+      const mq_gemv_problem& p = problems[i];
+      if ((p.group != p.K) != grouped) continue;
+      a.p[a.count++] = mq::SkinnyProblem{p.packed, p.alpha, p.zero, p.x, nullptr, p.y, (int)p.N,
+                                         (int)p.K, (int)p.group, mq::kXBf16, 0, 0, 0, 0};
+    }
+    s = skinny_run(a, r, grouped, (hipStream_t)stream);
+    if (s != MQ_OK) return s;
+  }
+  return MQ_OK;
+}
+
+size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+  return mq::gemm_workspace_bytes(M, N, K, group);
+}
+
+mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                  int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  mq_status s = check_product(packed, r, alpha, zero, group, N, K, x, y);
+  if (s != MQ_OK) return s;
+  if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+  const size_t need = mq::gemm_workspace_bytes(M, N, K, group);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MQ_ERR_WORKSPACE;
+  s = check_device();
+  if (s != MQ_OK) return s;
+  if (M <= mq::kSkinnyMaxM) return mq_gemv(packed, r, alpha, zero, group, N, K, x, M, y, stream);
+  hipError_t e = mq::launch_gemm(packed, r, alpha, zero, group, N, K, x, M, y, workspace,
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- Mix'n'Match
+
+namespace {
+
+struct StackDims {
+  int64_t H, Hkv, F;
+};
+
+bool linear_ok(const mq_linear& l, int64_t n, int64_t k, int r) {
+  if (!l.packed || !l.alpha || !l.zero) return false;
+  if (l.N != n || l.K != k) return false;
+  if (check_matrix(l.N, l.K, l.group, r) != MQ_OK) return false;
+  if (!aligned16(l.packed)) return false;
+  return true;
+}
+
+mq_status check_stack(const mq_layer* layers, int n_layers, int64_t M, StackDims* d) {
+  if (!layers) return MQ_ERR_NULL;
+  if (n_layers < 1 || M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
+  const int64_t H = layers[0].q.N, Hkv = layers[0].k.N, F = layers[0].up.N;
+  for (int i = 0; i < n_layers; ++i) {
+    const mq_layer& L = layers[i];
+    const mq_linear* all[7] = {&L.q, &L.k, &L.v, &L.o, &L.up, &L.gate, &L.down};
+    for (const mq_linear* l : all)
+      if (!l->packed || !l->alpha || !l->zero) return MQ_ERR_NULL;
+    if (!valid_r(L.r)) return MQ_ERR_PRECISION;
+    if (!linear_ok(L.q, H, H, L.r) || !linear_ok(L.k, Hkv, H, L.r) ||
+        !linear_ok(L.v, Hkv, H, L.r) || !linear_ok(L.o, H, H, L.r) ||
+        !linear_ok(L.up, F, H, L.r) || !linear_ok(L.gate, F, H, L.r) ||
+        !linear_ok(L.down, H, F, L.r))
+      return MQ_ERR_SHAPE;
+  }
+  d->H = H;
+  d->Hkv = Hkv;
+  d->F = F;
+  return MQ_OK;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+void stack_offsets(const StackDims& d, int64_t M, size_t* off, size_t* total) {
+  size_t o = 0;
+  const size_t sizes[8] = {(size_t)(M * d.H * 2), (size_t)(M * d.H * 4), (size_t)(M * d.Hkv * 4),
+                           (size_t)(M * d.Hkv * 4), (size_t)(M * d.F * 4), (size_t)(M * d.F * 4),
+                           (size_t)(M * d.H * 4), (size_t)(M * d.H * 4)};
+  for (int i = 0; i < 8; ++i) {
+    off[i] = o;
+    o += up256(sizes[i]);
+  }
+  *total = o;
+}
+
+// Run the problems of one launch, split by scale granularity.
+mq_status run_mixed(mq::SkinnyProblem* probs, int count, int r, int64_t M, hipStream_t s) {
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool grouped = pass == 1;
+    mq::SkinnyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.M = (int)M;
+    for (int i = 0; i < count; ++i)
+      if ((probs[i].group != probs[i].K) == grouped) a.p[a.count++] = probs[i];
+    if (a.count == 0) continue;
+    mq_status st = skinny_run(a, r, grouped, s);
+    if (st != MQ_OK) return st;
+  }
+  return MQ_OK;
+}
+
+mq::SkinnyProblem prob(const mq_linear& l, const void* x0, const void* x1, int xmode, float* y) {
+  return mq::SkinnyProblem{l.packed, l.alpha, l.zero, x0, x1, y, (int)l.N, (int)l.K,
+                           (int)l.group, xmode, 0, 0, 0, 0};
+}
+
+}  // namespace
+
+size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_t M) {
+  StackDims d;
+  if (check_stack(layers, n_layers, M, &d) != MQ_OK) return 0;
+  size_t off[8], total;
+  stack_offsets(d, M, off, &total);
+  return total;
+}
+
+mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, int64_t M,
+                                         size_t* offsets) {
+  if (!offsets) return MQ_ERR_NULL;
+  StackDims d;
+  mq_status s = check_stack(layers, n_layers, M, &d);
+  if (s != MQ_OK) return s;
+  size_t total;
+  stack_offsets(d, M, offsets, &total);
+  return MQ_OK;
+}
+
+mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, int64_t M,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  StackDims d;
+  mq_status s = check_stack(layers, n_layers, M, &d);
+  if (s != MQ_OK) return s;
+  if (!h) return MQ_ERR_NULL;
+  if (!aligned16(h)) return MQ_ERR_ALIGN;
+  size_t off[8], total;
+  stack_offsets(d, M, off, &total);
+  if (!workspace || workspace_bytes < total) return MQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MQ_ERR_ALIGN;
+  s = check_device();
+  if (s != MQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* a = reinterpret_cast<uint16_t*>(ws + off[0]);
+  float* q = reinterpret_cast<float*>(ws + off[1]);
+  float* k = reinterpret_cast<float*>(ws + off[2]);
+  float* v = reinterpret_cast<float*>(ws + off[3]);
+  float* u = reinterpret_cast<float*>(ws + off[4]);
+  float* g = reinterpret_cast<float*>(ws + off[5]);
+  float* o = reinterpret_cast<float*>(ws + off[6]);
+  float* dd = reinterpret_cast<float*>(ws + off[7]);
+
+  hipError_t e = mq::launch_rmsnorm_bf16(h, a, M, d.H, st);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int i = 0; i < n_layers; ++i) {
+    const mq_layer& L = layers[i];
+    mq::SkinnyProblem p1[5] = {prob(L.q, a, nullptr, mq::kXBf16, q),
+                               prob(L.k, a, nullptr, mq::kXBf16, k),
+                               prob(L.v, a, nullptr, mq::kXBf16, v),
+                               prob(L.up, a, nullptr, mq::kXBf16, u),
+                               prob(L.gate, a, nullptr, mq::kXBf16, g)};
+    s = run_mixed(p1, 5, L.r, M, st);
+    if (s != MQ_OK) return s;
+    mq::SkinnyProblem p2[2] = {prob(L.o, q, nullptr, mq::kXF32, o),
+                               prob(L.down, u, g, mq::kXF32Prod, dd)};
+    s = run_mixed(p2, 2, L.r, M, st);
+    if (s != MQ_OK) return s;
+    // the last layer leaves its own input a in the workspace
+    e = mq::launch_residual_rmsnorm(h, o, dd, i + 1 < n_layers ? a : nullptr, M, d.H, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,291 @@
+// Batched product (M > 8 activation rows: small batches and prefill) against
+// r-bit planes, on bf16 matrix cores.
+//
+//   y[m, n] = sum_g alpha[n, g] * (2^(8-r) * sum_{k in g} x[m, k] t[n, k]
+//                                   - z[n, g] * sum_{k in g} x[m, k])
+// which is sum_k x[m, k] (S(q[n, k], r) - z[n, g]) alpha[n, g] with
+// S = t * 2^(8-r) ("Matryoshka Quantization" explainer, §3.4, Eq. 6 and the
+// dequantization of Eq. 1).  The integer index (plus the encoding offset of
+// mq_device.h) is contracted exactly in bf16 x bf16 -> fp32; alpha, 2^(8-r)
+// and z are applied in fp32 once per group of 128 (or once at the end for
+// per-channel scales).
+//
+// Tiling (gfx950, v_mfma_f32_32x32x16_bf16): A = activations (32 rows of m x
+// 16 k), B = unpacked weights (16 k x 32 rows of n), D = y tile [m][n].  A
+// workgroup of 4 waves computes a BM x BN tile; each K iteration covers 128
+// codes (one scale group): the activation tile (bf16, permuted to the
+// unpacked operand order) and the packed weight tile are staged in LDS, the
+// next tile's global loads are issued before the current tile's MFMAs.
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+constexpr int kBK = 128;     // codes per K iteration (one group of 128)
+constexpr int kXsPad = 8;    // bf16 padding per staged activation row
+
+template <int R, int MB, int NB, int WM, int WN>
+struct Gm {
+  static constexpr int BM = 32 * MB * WM;
+  static constexpr int BN = 32 * NB * WN;
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int XS = kBK + kXsPad;         // staged x row stride (elements)
+  static constexpr int WROW = kBK * R / 8;        // packed bytes per row per iteration
+  static constexpr int WS = WROW + 16;            // staged weight row stride (bytes)
+  static constexpr int PB = XPerm<R>::PB;
+  // x tile loads: BM rows x 128 codes = BM * 16 vectors of 8 bf16
+  static constexpr int XV = BM * 16 / THREADS;    // 16-byte vectors per thread
+  static constexpr int WV = BN * WROW / 16 / THREADS;  // 16-byte packed vectors per thread
+  static_assert(XV >= 1 && (BM * 16) % THREADS == 0, "x tile split");
+  static_assert((BN * WROW / 16) % THREADS == 0 && WV >= 1, "w tile split");
+};
+
+// Position in the staged (permuted) activation tile of the 8 values that lane
+// slot s feeds at k-step kk (16 codes per k-step), and the packed byte offset
+// of the matching weight word(s).
+template <int R>
+__device__ __forceinline__ int xpos(int kk, int s) {
+  return R == 2 ? 32 * (kk >> 1) + 16 * s + 8 * (kk & 1) : 16 * kk + 8 * s;
+}
+template <int R>
+__device__ __forceinline__ int wbyte(int kk, int s) {
+  return R == 2 ? 8 * (kk >> 1) + 4 * s : (R == 4 ? 8 * kk + 4 * s : 16 * kk + 8 * s);
+}
+
+template <int R, int MB, int NB, int WM, int WN, bool GROUPED>
+__global__ void __launch_bounds__(64 * WM * WN)
+    gemm_kernel(const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
+                const float* __restrict__ zero, const uint16_t* __restrict__ x,
+                float* __restrict__ y, int M, int N, int K, int group) {
+  using C = Gm<R, MB, NB, WM, WN>;
+  __shared__ __align__(16) uint16_t xs[C::BM * C::XS];
+  __shared__ __align__(16) uint8_t ws[C::BN * C::WS];
+  __shared__ float sxg[C::BM];   // per-group sums of x (this iteration)
+  __shared__ float sxh[C::BM * 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const int G = K / group;
+  const int rowbytes = K * R / 8;
+  const uint32_t plane = (uint32_t)((int64_t)N * rowbytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, plane);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  const int iters = (K + kBK - 1) / kBK;
+
+  // ---- per-thread staging assignment
+  // x: thread covers XV consecutive 16-byte vectors of one row (PB | 8*XV)
+  const int xvec0 = tid * C::XV;             // first vector index in [0, BM*16)
+  const int xrow = xvec0 / 16, xcol = (xvec0 % 16) * 8;
+  const bool xrow_ok = (m0 + xrow) < M;
+  const uint32_t xoff_row = xrow_ok ? (uint32_t)((m0 + xrow) * K) * 2u : 0xffffffffu;
+  // w: thread covers WV vectors of 16 packed bytes
+  auto wvec_off = [&](int v, int it) -> uint32_t {
+    const int vid = tid * C::WV + v;
+    const int row = vid / (C::WROW / 16), cb = (vid % (C::WROW / 16)) * 16;
+    const int n = n0 + row;
+    if (n >= N) return 0xffffffffu;
+    return (uint32_t)n * (uint32_t)rowbytes + (uint32_t)(it * C::WROW + cb);
+  };
+
+  u32x4 xreg[C::XV], wreg[C::WV];
+  auto gload = [&](int it) {
+#pragma unroll
+    for (int v = 0; v < C::XV; ++v) {
+      const int k = it * kBK + xcol + 8 * v;
+      const uint32_t off = (xrow_ok && k < K) ? xoff_row + (uint32_t)k * 2u : 0xffffffffu;
+      xreg[v] = buf_load16(xr, off);
+    }
+#pragma unroll
+    for (int v = 0; v < C::WV; ++v) wreg[v] = buf_load16(wr, wvec_off(v, it));
+  };
+  float xsum_run = 0.f;  // per-channel: running sum of this thread's x values
+  auto lstore = [&]() {
+    // activations: permute inside PB blocks, sum
+    uint32_t v16[C::XV * 8];
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < C::XV; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v16[8 * v + 2 * e] = xreg[v][e] & 0xffffu;
+        v16[8 * v + 2 * e + 1] = xreg[v][e] >> 16;
+      }
+#pragma unroll
+    for (int e = 0; e < C::XV * 8; ++e) s += bf16_to_f32(v16[e]);
+    uint32_t o[C::XV * 4];
+#pragma unroll
+    for (int b = 0; b < C::XV * 8 / C::PB; ++b)
+#pragma unroll
+      for (int q = 0; q < C::PB / 2; ++q)
+        o[b * C::PB / 2 + q] = v16[b * C::PB + XPerm<R>::src(2 * q)] |
+                               (v16[b * C::PB + XPerm<R>::src(2 * q + 1)] << 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(xs + xrow * C::XS + xcol);
+#pragma unroll
+    for (int v = 0; v < C::XV; ++v) {
+      u32x4 w4 = {o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]};
+      dst[v] = w4;
+    }
+    // threads of one row: 16 / XV of them; reduce their sums
+    constexpr int TPR = 16 / C::XV;
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) s += __shfl_xor(s, off);
+    if ((tid % TPR) == 0) sxg[xrow] = s;
+    xsum_run += s;
+#pragma unroll
+    for (int v = 0; v < C::WV; ++v) {
+      const int vid = tid * C::WV + v;
+      const int row = vid / (C::WROW / 16), cb = (vid % (C::WROW / 16)) * 16;
+      *reinterpret_cast<u32x4*>(ws + row * C::WS + cb) = wreg[v];
+    }
+  };
+
+  f32x16 part[MB][NB], tot[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        part[i][j][e] = 0.f;
+        tot[i][j][e] = 0.f;
+      }
+
+  const int l32 = lane & 31, s = lane >> 5;
+  const int am0 = wm * MB * 32, bn0 = wn * NB * 32;
+
+  gload(0);
+#pragma unroll 1
+  for (int it = 0; it < iters; ++it) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (it + 1 < iters) gload(it + 1);
+
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 a[MB], b[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xs + (am0 + 32 * i + l32) * C::XS +
+                                                        xpos<R>(kk, s));
+        a[i] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint8_t* wp = ws + (bn0 + 32 * j + l32) * C::WS + wbyte<R>(kk, s);
+        if (R == 4) {
+          b[j] = unpack_r4(*reinterpret_cast<const uint32_t*>(wp));
+        } else if (R == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(wp);
+          b[j] = (kk & 1) ? unpack_r2<1>(w) : unpack_r2<0>(w);
+        } else {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(wp);
+          b[j] = unpack_r8(w[0], w[1]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], part[i][j], 0, 0, 0);
+    }
+
+    if (GROUPED) {
+      const int g = it;  // group == 128 == kBK
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + bn0 + 32 * j + l32;
+        float av = 0.f, bv = 0.f;
+        if (n < N) {
+          const float al = alpha[(int64_t)n * G + g];
+          const float ze = zero[(int64_t)n * G + g];
+          av = al * Enc<R>::kStep;
+          bv = al * (ze + Enc<R>::kOffsetShift);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int mrow = am0 + 32 * i + 8 * (e >> 2) + 4 * s + (e & 3);
+            tot[i][j][e] = tot[i][j][e] + av * part[i][j][e] - bv * sxg[mrow];
+            part[i][j][e] = 0.f;
+          }
+      }
+    }
+  }
+
+  // ---- epilogue
+  if (!GROUPED) {
+    constexpr int TPR = 16 / C::XV;
+    __syncthreads();
+    if ((tid % TPR) == 0) sxh[xrow] = 0.f;
+    __syncthreads();
+    // xsum_run of the TPR threads of a row were already reduced per iteration
+    if ((tid % TPR) == 0) sxh[xrow] = xsum_run;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int n = n0 + bn0 + 32 * j + l32;
+    if (n >= N) continue;
+    float av = 0.f, bv = 0.f;
+    if (!GROUPED) {
+      av = alpha[n] * Enc<R>::kStep;
+      bv = alpha[n] * (zero[n] + Enc<R>::kOffsetShift);
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int mrow = am0 + 32 * i + 8 * (e >> 2) + 4 * s + (e & 3);
+        const int m = m0 + mrow;
+        if (m >= M) continue;
+        float v;
+        if (GROUPED) {
+          v = tot[i][j][e];
+        } else {
+          v = av * part[i][j][e] - bv * sxh[mrow];
+        }
+        y[(int64_t)m * N + n] = v;
+      }
+  }
+}
+
+size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+template <int R, int MB, int NB, int WM, int WN>
+static hipError_t launch_cfg(const uint8_t* packed, const float* alpha, const float* zero,
+                             int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                             float* y, hipStream_t s) {
+  using C = Gm<R, MB, NB, WM, WN>;
+  dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
+  if (group == K)
+    hipLaunchKernelGGL((gemm_kernel<R, MB, NB, WM, WN, false>), grid, dim3(C::THREADS), 0, s,
+                       packed, alpha, zero, x, y, (int)M, (int)N, (int)K, (int)group);
+  else
+    hipLaunchKernelGGL((gemm_kernel<R, MB, NB, WM, WN, true>), grid, dim3(C::THREADS), 0, s,
+                       packed, alpha, zero, x, y, (int)M, (int)N, (int)K, (int)group);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_r(const uint8_t* packed, const float* alpha, const float* zero,
+                           int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                           float* y, hipStream_t s) {
+  if (M <= 32) return launch_cfg<R, 1, 1, 1, 4>(packed, alpha, zero, group, N, K, x, M, y, s);
+  if (M <= 64) return launch_cfg<R, 1, 2, 2, 2>(packed, alpha, zero, group, N, K, x, M, y, s);
+  return launch_cfg<R, 2, 2, 2, 2>(packed, alpha, zero, group, N, K, x, M, y, s);
+}
+
+hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                       int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                       void*, hipStream_t s) {
+  switch (r) {
+    case 2: return launch_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
+    case 4: return launch_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);
+    default: return launch_r<8>(packed, alpha, zero, group, N, K, x, M, y, s);
+  }
+}
+
+}  // namespace mq

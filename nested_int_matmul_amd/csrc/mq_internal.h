@@ -1,0 +1,60 @@
+// Internal launcher interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+// How a skinny-kernel problem reads its activations.
+enum XMode : int {
+  kXBf16 = 0,     // x: bf16 bits [M, K]
+  kXF32 = 1,      // x0: fp32 [M, K], rounded to bf16 (nearest even) on load
+  kXF32Prod = 2,  // x0 * x1 (fp32 product), rounded to bf16 on load
+};
+
+constexpr int kMaxProblems = 8;
+constexpr int kSkinnyMaxM = 8;
+
+struct SkinnyProblem {
+  const uint8_t* packed;
+  const float* alpha;
+  const float* zero;
+  const void* x0;
+  const void* x1;
+  float* y;
+  int N, K, group, xmode;
+  int ks;        // waves sharing one 16-row block (split of K)
+  int rbpw;      // 16-row blocks per workgroup (rbpw * ks == waves per workgroup)
+  int tiles;     // workgroups of this problem
+  int tile0;     // first workgroup index of this problem
+};
+
+struct SkinnyArgs {
+  SkinnyProblem p[kMaxProblems];
+  int count;
+  int M;
+  int kc;        // activation codes staged per chunk (multiple of every step size)
+};
+
+// Host-side planning + launch of the skinny (M <= 8) kernel.  `probs` hold the
+// pointers and shapes; tiling fields are filled in here.
+hipError_t launch_skinny(SkinnyArgs& args, int r, bool grouped, hipStream_t stream);
+
+hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* codes,
+                           float* alpha, float* zero, hipStream_t stream);
+hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
+                       hipStream_t stream);
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                       int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                       void* workspace, hipStream_t stream);
+
+// Mix'n'Match helpers.
+hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H,
+                               hipStream_t stream);
+hipError_t launch_residual_rmsnorm(float* h, const float* o, const float* d, uint16_t* a,
+                                   int64_t M, int64_t H, hipStream_t stream);
+
+}  // namespace mq

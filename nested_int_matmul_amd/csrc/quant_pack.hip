@@ -1,0 +1,140 @@
+// Quantizer (Eq. 1) and slice-and-pack (Eq. 6) kernels.
+//
+// "Matryoshka Quantization" explainer, §3.4 "Quantization Primitives" (Eq. 1,
+// min-max quantization with c = 8) and "The Bit-Slicing Operator" (Eq. 6).
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+// ---------------------------------------------------------------------------
+// mq_quantize: one wavefront per weight vector (group consecutive entries of a
+// row).  Min and max are exact; alpha, z and the codes are evaluated in IEEE
+// float64 from the stored fp32 alpha and z, in this order:
+//   alpha = fp32((max - min) / 255), z = fp32(-min / alpha),
+//   q = clamp(floor((w / alpha + z) + 0.5), 0, 255).
+// A constant vector takes alpha = 1, z = -min.
+// ---------------------------------------------------------------------------
+#pragma clang fp contract(off)
+__global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ w, int64_t n_vec,
+                                                       int group, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ alpha,
+                                                       float* __restrict__ zero) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (v >= n_vec) return;
+  const float* src = w + v * group;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = lane; i < group; i += 64) {
+    float f = src[i];
+    mn = fminf(mn, f);
+    mx = fmaxf(mx, f);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off));
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  }
+  float a32;
+  float z32;
+  if (mx == mn) {
+    a32 = 1.0f;
+    z32 = -mn;
+  } else {
+    double a64 = ((double)mx - (double)mn) / 255.0;
+    a32 = (float)a64;
+    z32 = (float)(-(double)mn / (double)a32);
+  }
+  if (lane == 0) {
+    alpha[v] = a32;
+    zero[v] = z32;
+  }
+  const double ad = (double)a32, zd = (double)z32;
+  uint8_t* dst = codes + v * group;
+  for (int i = lane; i < group; i += 64) {
+    double t = (double)src[i] / ad;
+    t = t + zd;
+    t = t + 0.5;
+    double f = floor(t);
+    f = f < 0.0 ? 0.0 : (f > 255.0 ? 255.0 : f);
+    dst[i] = (uint8_t)(int)f;
+  }
+}
+#pragma clang fp contract(on)
+
+hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* codes,
+                           float* alpha, float* zero, hipStream_t stream) {
+  int64_t n_vec = N * (K / group);
+  int64_t blocks = (n_vec + 3) / 4;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, n_vec,
+                     (int)group, codes, alpha, zero);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// mq_pack: t = min((q + 2^(7-r)) >> (8-r), 2^r - 1) (t = q for r = 8), i.e.
+// round half up of q / 2^(8-r) followed by the clamp of Eq. 6; 8/r indices
+// per byte, index i of a byte in bits [i*r, i*r + r).  Rows need no special
+// handling: K is a multiple of 64, so the flat packing of the [N, K] array is
+// the row-by-row packing.  Each thread writes 16 output bytes (one
+// 128-bit store) from 128/r input bytes; the loop is grid-strided.
+// ---------------------------------------------------------------------------
+template <int R>
+__device__ __forceinline__ uint32_t slice_byte(uint32_t q) {
+  if (R == 8) return q;
+  uint32_t t = (q + (1u << (7 - R))) >> (8 - R);
+  uint32_t hi = (1u << R) - 1u;
+  return t > hi ? hi : t;
+}
+
+template <int R>
+__global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ codes, u32x4* __restrict__ out,
+                                                   int64_t n_out16) {
+  constexpr int IN16 = 8 / R;  // 16-byte input vectors per 16-byte output vector
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_out16;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    u32x4 in[IN16];
+#pragma unroll
+    for (int j = 0; j < IN16; ++j) in[j] = __builtin_nontemporal_load(codes + i * IN16 + j);
+    uint32_t o[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t acc = 0;
+      constexpr int PER_WORD = 32 / R;  // indices per output word
+#pragma unroll
+      for (int e = 0; e < PER_WORD; ++e) {
+        const int flat = w * PER_WORD + e;  // input byte index within this thread's span
+        const uint32_t word = in[flat / 16][(flat / 4) & 3];
+        const uint32_t q = (word >> (8 * (flat & 3))) & 0xffu;
+        acc |= slice_byte<R>(q) << (e * R);
+      }
+      o[w] = acc;
+    }
+    u32x4 ov = {o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(ov, out + i);
+  }
+}
+
+hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
+                       hipStream_t stream) {
+  const int64_t out_bytes = N * K * r / 8;
+  const int64_t n16 = out_bytes / 16;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks < 1) blocks = 1;
+  const u32x4* in = reinterpret_cast<const u32x4*>(codes);
+  u32x4* out = reinterpret_cast<u32x4*>(packed);
+  switch (r) {
+    case 2:
+      hipLaunchKernelGGL(pack_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
+      break;
+    case 4:
+      hipLaunchKernelGGL(pack_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
+      break;
+    default:
+      hipLaunchKernelGGL(pack_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mq

@@ -1,0 +1,99 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and validates arguments before touching the GPU (these calls
+return before any HIP runtime call, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import nested_int_matmul_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mq.LIB_PATH):
+        pytest.skip("libmq.so not built")
+    return mq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(mq.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_sizes(L):
+    for code, name in mq.STATUS_NAMES.items():
+        assert L.mq_status_string(code).decode().startswith(name)
+    assert L.mq_status_string(99).decode() == "unknown mq_status"
+    assert L.mq_version().decode().startswith("mq ")
+    assert L.mq_packed_bytes(14336, 3584, 2) == 14336 * 3584 // 4
+    assert L.mq_packed_bytes(10, 64, 3) == 0
+    assert L.mq_gemm_workspace_bytes(2048, 14336, 4096, 128) >= 0
+
+
+NULL = None
+P16 = ctypes.c_void_p(0x10000)  # a 16-byte-aligned dummy address: never dereferenced
+P1 = ctypes.c_void_p(0x10001)
+
+
+def test_pack_validation(L):
+    assert L.mq_pack(NULL, 4, 64, 4, P16, NULL) == 1
+    assert L.mq_pack(P16, 4, 64, 3, P16, NULL) == 3
+    assert L.mq_pack(P16, 4, 65, 4, P16, NULL) == 2
+    assert L.mq_pack(P16, 0, 64, 4, P16, NULL) == 2
+    assert L.mq_pack(P1, 4, 64, 4, P16, NULL) == 5
+
+
+def test_gemv_validation(L):
+    args = lambda **kw: dict(dict(p=P16, r=4, a=P16, z=P16, g=64, N=4, K=64, x=P16, M=1, y=P16), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.mq_gemv(a["p"], a["r"], a["a"], a["z"], a["g"], a["N"], a["K"], a["x"], a["M"],
+                         a["y"], NULL)
+
+    assert call(p=NULL) == 1
+    assert call(y=NULL) == 1
+    assert call(r=3) == 3
+    assert call(K=96, g=96) == 2
+    assert call(g=32) == 4
+    assert call(K=192, g=128) == 4
+    assert call(M=0) == 2
+    assert call(M=9) == 2
+    assert call(x=P1) == 5
+
+
+def test_gemm_and_grouped_validation(L):
+    assert L.mq_gemm(P16, 5, P16, P16, 64, 4, 64, P16, 16, P16, NULL, 0, NULL) == 3
+    assert L.mq_gemm(P16, 4, P16, P16, 64, 4, 64, P16, 0, P16, NULL, 0, NULL) == 2
+    probs = (mq.GemvProblem * 2)()
+    assert L.mq_gemv_grouped(probs, 2, 4, 1, NULL) == 1
+    assert L.mq_gemv_grouped(probs, 0, 4, 1, NULL) == 2
+    assert L.mq_gemv_grouped(probs, 9, 4, 1, NULL) == 2
+
+
+def test_mixnmatch_validation(L):
+    layers = (mq.Layer * 1)()
+    assert L.mq_mixnmatch_forward(layers, 1, P16, 1, P16, 1 << 20, NULL) == 1
+    assert L.mq_mixnmatch_workspace_bytes(layers, 1, 1) == 0
+    assert L.mq_mixnmatch_forward(layers, 0, P16, 1, P16, 1 << 20, NULL) == 2
+
+
+def test_quantize_validation(L):
+    assert L.mq_quantize(NULL, 4, 64, 64, P16, P16, P16, NULL) == 1
+    assert L.mq_quantize(P16, 4, 64, 32, P16, P16, P16, NULL) == 4
+    assert L.mq_quantize(P16, 0, 64, 64, P16, P16, P16, NULL) == 2

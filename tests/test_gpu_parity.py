@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Integer work (codes, slices, packed planes) must match bit for bit; products
+must be within rel-L2 1e-3 and max-abs 2e-2 of the oracle.  Full-size
+workloads are checked on sampled output rows the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import nested_int_matmul_amd as mq
+import oracle
+from nested_int_matmul_amd import inputs
+
+from gpu_helpers import compare, dev, note, quantized, x_device
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- quantize / pack
+
+@pytest.mark.parametrize("shape,group,outliers", [
+    ((256, 512), 512, 0.0),         # tiny linear, per-channel
+    ((300, 3584), 3584, 1e-3),      # Gemma up-proj rows with outliers, ragged N
+    ((64, 4096), 128, 0.0),         # group 128
+])
+def test_quantize_bit_exact(shape, group, outliers):
+    n, k = shape
+    note(f"quantize {shape} group {group}")
+    w = inputs.gaussian_weights("tiny_linear", n, k, outlier_frac=outliers)
+    w[3, :] = 0.125                     # a constant vector (alpha = 1 case)
+    q, a, z = oracle.quantize_minmax(w, group)
+    codes, alpha, zero = mq.quantize(torch.from_numpy(w).to(dev()), group)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), q)
+    assert np.array_equal(alpha.cpu().numpy().view(np.uint32), a.view(np.uint32))
+    assert np.array_equal(zero.cpu().numpy().view(np.uint32), z.view(np.uint32))
+
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+def test_pack_all_codes_bit_exact(r):
+    note(f"pack all codes r={r}")
+    q = np.tile(np.arange(256, dtype=np.uint8), (7, 4))          # [7, 1024], every code
+    q[3] = np.random.default_rng(r).integers(0, 256, 1024, dtype=np.uint8)
+    got = mq.pack(torch.from_numpy(q).to(dev()), r)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.pack_codes(q, r))
+    # unpacking the GPU plane on the host gives back the oracle's indices
+    t = oracle.unpack_indices(got.cpu().numpy(), r, 1024)
+    assert np.array_equal(t, oracle.slice_index(q, r))
+
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+def test_pack_gemma_down_full_size(r):
+    note(f"pack gemma down full r={r}")
+    m = quantized("gemma9b_mlp", 3584, 14336, 14336, matrix=2, outlier_frac=1e-3)
+    got = mq.pack(m["q_d"], r)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.pack_codes(m["q"], r))
+
+
+# ---------------------------------------------------------------- GEMV (M <= 8)
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("M", [1, 4])
+def test_gemv_tiny_linear(r, M):
+    note(f"gemv tiny r={r} M={M}")
+    m = quantized("tiny_linear", 256, 512, 512)
+    xb = inputs.activations_bf16("tiny_linear", M, 512)
+    plane = mq.pack(m["q_d"], r)
+    y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], 512, 256, 512, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 512, r), f"tiny r{r} M{M}")
+
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gemv_ragged(r, group, M):
+    # N not a multiple of 16, K not a multiple of 256, several chunks at M = 8
+    n, k = 301, (1152 if group == 128 else 576)
+    g = k if group == "K" else 128
+    note(f"gemv ragged r={r} group={g} M={M}")
+    m = quantized("tiny_linear", n, k, g, matrix=7)
+    xb = inputs.activations_bf16("tiny_linear", M, k, matrix=7)
+    plane = mq.pack(m["q_d"], r)
+    y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"ragged r{r} g{g} M{M}")
+
+
+@pytest.mark.parametrize("r", [4, 2])
+def test_gemv_long_k_chunked(r):
+    # K = 16384 at M = 8 needs four activation chunks in LDS
+    n, k, M = 48, 16384, 8
+    note(f"gemv chunked r={r}")
+    for g in (k, 128):
+        m = quantized("tiny_linear", n, k, g, matrix=9)
+        xb = inputs.activations_bf16("tiny_linear", M, k, matrix=9, heavy_channels=8)
+        plane = mq.pack(m["q_d"], r)
+        y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+        torch.cuda.synchronize()
+        compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"chunked r{r} g{g}")
+
+
+def _sample_rows(n, count=384, seed=0):
+    rg = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, n - 1], rg.choice(n, count, replace=False)]))
+    return rows
+
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+def test_gemv_gemma_mlp_full_size(r):
+    """Decode GEMV at the Gemma-2-9B MLP shapes, in one grouped launch as the
+    benchmark runs it; sampled rows against the oracle."""
+    note(f"gemma mlp grouped r={r}")
+    mats, probs, xs = [], [], []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        m = dict(quantized("gemma9b_mlp", n, k, k, matrix=i, outlier_frac=1e-3))
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        m["plane"] = mq.pack(m["q_d"], r)
+        m["y"] = torch.empty((1, n), dtype=torch.float32, device=dev())
+        m["xb"] = xb
+        mats.append(m)
+        probs.append({"packed": m["plane"], "alpha": m["alpha_d"], "zero": m["zero_d"],
+                      "x": x_device(xb), "y": m["y"], "N": n, "K": k, "group": k})
+    mq.gemv_grouped(probs, r, 1)
+    torch.cuda.synchronize()
+    for i, m in enumerate(mats):
+        rows = _sample_rows(m["N"], seed=i)
+        ref = oracle.linear(m["xb"], m["q"][rows], m["alpha"][rows], m["zero"][rows], m["K"], r)
+        compare(m["y"][:, rows], ref, f"gemma mat{i} r{r}")
+
+
+def test_gemv_deterministic():
+    note("gemv determinism")
+    m = quantized("tiny_linear", 512, 4096, 4096, matrix=3)
+    xb = inputs.activations_bf16("tiny_linear", 2, 4096, matrix=3)
+    plane = mq.pack(m["q_d"], 2)
+    y1 = mq.gemv(plane, 2, m["alpha_d"], m["zero_d"], 4096, 512, 4096, x_device(xb))
+    y2 = mq.gemv(plane, 2, m["alpha_d"], m["zero_d"], 4096, 512, 4096, x_device(xb))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_error_enqueues_nothing():
+    note("error path")
+    m = quantized("tiny_linear", 64, 512, 512)
+    plane = mq.pack(m["q_d"], 4)
+    xb = x_device(inputs.activations_bf16("tiny_linear", 1, 512))
+    y = torch.full((1, 64), 7.0, device=dev())
+    with pytest.raises(mq.MQError):
+        mq.gemv(plane, 3, m["alpha_d"], m["zero_d"], 512, 64, 512, xb, out=y)
+    with pytest.raises(mq.MQError):
+        mq.gemv(plane, 4, m["alpha_d"], m["zero_d"], 100, 64, 512, xb, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ---------------------------------------------------------------- GEMM (M > 8)
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [9, 16, 64, 130])
+def test_gemm_small(r, group, M):
+    n, k = 200, (640 if group == "K" else 768)
+    g = k if group == "K" else 128
+    note(f"gemm small r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=5)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=5, heavy_channels=8)
+    plane = mq.pack(m["q_d"], r)
+    y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+
+
+@pytest.mark.parametrize("r", [4, 2])
+@pytest.mark.parametrize("M", [16, 64])
+@pytest.mark.parametrize("shape", inputs.MISTRAL_SMALL_SHAPES)
+def test_gemm_mistral_small_full_size(r, M, shape):
+    n, k = shape
+    note(f"gemm mistral small r={r} M={M} {shape}")
+    m = quantized("mistral_small", n, k, 128, matrix=shape[0] // 4096)
+    xb = inputs.activations_bf16("mistral_small", M, k, heavy_channels=8)
+    plane = mq.pack(m["q_d"], r)
+    y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, 256)
+    ref = oracle.linear(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], 128, r)
+    compare(y[:, rows], ref, f"mistral small r{r} M{M} {shape}")
+
+
+@pytest.mark.parametrize("r", [4, 2, 8])
+def test_gemm_prefill_full_size(r):
+    M, k, n = inputs.PREFILL_SHAPE
+    note(f"gemm prefill r={r}")
+    m = quantized("prefill", n, k, 128)
+    xb = inputs.activations_bf16("prefill", M, k)
+    plane = mq.pack(m["q_d"], r)
+    y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    cols = _sample_rows(n, 128)
+    ref = oracle.linear(xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], 128, r)
+    compare(y[:, cols], ref, f"prefill r{r}")
+
+
+# ---------------------------------------------------------------- Mix'n'Match
+
+def _small_stack(rs, H=256, Hkv=64, F=512, group_kind="K"):
+    shapes = {"q": (H, H), "k": (Hkv, H), "v": (Hkv, H), "o": (H, H),
+              "up": (F, H), "gate": (F, H), "down": (H, F)}
+    host, devl = [], []
+    for li, r in enumerate(rs):
+        hl, dl = {"r": r}, {"r": r}
+        for mi, name in enumerate(oracle.LAYER_LINEARS):
+            n, k = shapes[name]
+            g = k if group_kind == "K" else 128
+            m = quantized("mistral_stack", n, k, g, layer=li, matrix=mi)
+            hl[name] = {"q": m["q"], "alpha": m["alpha"], "zero": m["zero"], "group": g}
+            dl[name] = {"packed": mq.pack(m["q_d"], r), "alpha": m["alpha_d"],
+                        "zero": m["zero_d"], "N": n, "K": k, "group": g}
+        host.append(hl)
+        devl.append(dl)
+    return host, devl
+
+
+def _bf16_bits_of_f32(t):
+    return t.float().to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("group_kind", ["K", 128])
+@pytest.mark.parametrize("M", [1, 2])
+def test_mixnmatch_small_stack(group_kind, M):
+    rs = [8, 4, 2, 4, 8]
+    note(f"mixnmatch small group={group_kind} M={M}")
+    host, devl = _small_stack(rs, group_kind=group_kind)
+    arr = mq.make_layers(devl)
+    H = 256
+    xb = inputs.activations_bf16("mistral_stack", M, H)
+    h0 = oracle.float_from_bf16_bits(xb)
+    ws = torch.empty(mq.mixnmatch_workspace_bytes(arr, M), dtype=torch.uint8, device=dev())
+    off = mq.mixnmatch_workspace_offsets(mq.make_layers(devl[0:1]), M)
+
+    # teacher-forced: one layer at a time from the GPU's own residual stream
+    h = torch.from_numpy(h0.astype(np.float32)).to(dev())
+    for li in range(len(rs)):
+        h_in = h.clone()
+        one = mq.make_layers(devl[li:li + 1])
+        mq.mixnmatch_forward(one, h, ws)
+        torch.cuda.synchronize()
+        L = host[li]
+        a_bits = ws[off[0]:off[0] + M * H * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+        a_bits = a_bits.reshape(M, H)
+        # the GPU's normalized input matches the definition on its own h
+        hin = h_in.double().cpu().numpy()
+        want_a = oracle.bf16_bits_from_float(oracle.rms_normalize(hin))
+        mism = np.count_nonzero(a_bits != want_a)
+        assert mism <= max(2, a_bits.size // 200), f"layer {li}: {mism} bf16 rounding differences"
+
+        def fetch(i, n):
+            return ws[off[i]:off[i] + M * n * 4].view(torch.float32).reshape(M, n)
+
+        outs = {"q": fetch(1, H), "k": fetch(2, 64), "v": fetch(3, 64), "up": fetch(4, 512),
+                "gate": fetch(5, 512)}
+        for name, y in outs.items():
+            p = L[name]
+            compare(y, oracle.linear(a_bits, p["q"], p["alpha"], p["zero"], p["group"], L["r"]),
+                    f"layer {li} {name}")
+        qb = _bf16_bits_of_f32(outs["q"])
+        ug = (outs["up"] * outs["gate"])
+        ugb = _bf16_bits_of_f32(ug)
+        o = fetch(6, H)
+        d = fetch(7, H)
+        compare(o, oracle.linear(qb, L["o"]["q"], L["o"]["alpha"], L["o"]["zero"],
+                                 L["o"]["group"], L["r"]), f"layer {li} o")
+        compare(d, oracle.linear(ugb, L["down"]["q"], L["down"]["alpha"], L["down"]["zero"],
+                                 L["down"]["group"], L["r"]), f"layer {li} down")
+        h_ref = hin + o.double().cpu().numpy() + d.double().cpu().numpy()
+        compare(h, h_ref, f"layer {li} residual")
+
+    # end to end: all layers in one call, against the float64 stack
+    h = torch.from_numpy(h0.astype(np.float32)).to(dev())
+    mq.mixnmatch_forward(arr, h, ws)
+    torch.cuda.synchronize()
+    compare(h, oracle.mixnmatch_forward(host, xb), "stack end-to-end")
