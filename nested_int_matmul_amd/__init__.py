@@ -187,6 +187,27 @@ def gemv_grouped(problems, r: int, M: int, stream=None):
     _check(lib().mq_gemv_grouped(arr, len(problems), r, M, _stream(stream)), "mq_gemv_grouped")
 
 
+class GemvGroupedPlan:
+    """A prepared mq_gemv_grouped call: the problem array is marshalled once,
+    each call is a single C call (for launch-rate-bound decode loops).  The
+    caller keeps every tensor alive while the plan is in use."""
+
+    def __init__(self, problems, r: int, M: int, stream=None):
+        self.arr = (GemvProblem * len(problems))()
+        for i, p in enumerate(problems):
+            self.arr[i] = GemvProblem(p["packed"].data_ptr(), p["alpha"].data_ptr(),
+                                      p["zero"].data_ptr(), _bits16(p["x"]).data_ptr(),
+                                      p["y"].data_ptr(), p["N"], p["K"], p["group"])
+        self.count, self.r, self.M = len(problems), r, M
+        self.stream = _stream(stream)
+        self.fn = lib().mq_gemv_grouped
+
+    def __call__(self):
+        st = self.fn(self.arr, self.count, self.r, self.M, self.stream)
+        if st != MQ_OK:
+            raise MQError(st, "mq_gemv_grouped")
+
+
 def gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:
     return int(lib().mq_gemm_workspace_bytes(M, N, K, group))
 

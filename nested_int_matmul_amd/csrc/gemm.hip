@@ -13,9 +13,9 @@
 // Tiling (gfx950, v_mfma_f32_32x32x16_bf16): A = activations (32 rows of m x
 // 16 k), B = unpacked weights (16 k x 32 rows of n), D = y tile [m][n].  A
 // workgroup of 4 waves computes a BM x BN tile; each K iteration covers 128
-// codes (one scale group): the activation tile (bf16, permuted to the
-// unpacked operand order) and the packed weight tile are staged in LDS, the
-// next tile's global loads are issued before the current tile's MFMAs.
+// codes (one scale group): the activation tile (bf16, natural order) and the
+// packed weight tile are staged in LDS, the next tile's global loads are
+// issued before the current tile's MFMAs.
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -32,7 +32,6 @@ struct Gm {
   static constexpr int XS = kBK + kXsPad;         // staged x row stride (elements)
   static constexpr int WROW = kBK * R / 8;        // packed bytes per row per iteration
   static constexpr int WS = WROW + 16;            // staged weight row stride (bytes)
-  static constexpr int PB = XPerm<R>::PB;
   // x tile loads: BM rows x 128 codes = BM * 16 vectors of 8 bf16
   static constexpr int XV = BM * 16 / THREADS;    // 16-byte vectors per thread
   static constexpr int WV = BN * WROW / 16 / THREADS;  // 16-byte packed vectors per thread
@@ -40,7 +39,7 @@ struct Gm {
   static_assert((BN * WROW / 16) % THREADS == 0 && WV >= 1, "w tile split");
 };
 
-// Position in the staged (permuted) activation tile of the 8 values that lane
+// Position in the staged activation tile of the 8 values that lane
 // slot s feeds at k-step kk (16 codes per k-step), and the packed byte offset
 // of the matching weight word(s).
 template <int R>
@@ -74,7 +73,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
   const int iters = (K + kBK - 1) / kBK;
 
   // ---- per-thread staging assignment
-  // x: thread covers XV consecutive 16-byte vectors of one row (PB | 8*XV)
+  // x: thread covers XV consecutive 16-byte vectors of one row
   const int xvec0 = tid * C::XV;             // first vector index in [0, BM*16)
   const int xrow = xvec0 / 16, xcol = (xvec0 % 16) * 8;
   const bool xrow_ok = (m0 + xrow) < M;
@@ -101,30 +100,15 @@ __global__ void __launch_bounds__(64 * WM * WN)
   };
   float xsum_run = 0.f;  // per-channel: running sum of this thread's x values
   auto lstore = [&]() {
-    // activations: permute inside PB blocks, sum
-    uint32_t v16[C::XV * 8];
+    // activations: stored as loaded (natural k order), summed
     float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < C::XV; ++v)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v16[8 * v + 2 * e] = xreg[v][e] & 0xffffu;
-        v16[8 * v + 2 * e + 1] = xreg[v][e] >> 16;
-      }
-#pragma unroll
-    for (int e = 0; e < C::XV * 8; ++e) s += bf16_to_f32(v16[e]);
-    uint32_t o[C::XV * 4];
-#pragma unroll
-    for (int b = 0; b < C::XV * 8 / C::PB; ++b)
-#pragma unroll
-      for (int q = 0; q < C::PB / 2; ++q)
-        o[b * C::PB / 2 + q] = v16[b * C::PB + XPerm<R>::src(2 * q)] |
-                               (v16[b * C::PB + XPerm<R>::src(2 * q + 1)] << 16);
+    const uint32_t ones = 0x3F803F80u;
     u32x4* dst = reinterpret_cast<u32x4*>(xs + xrow * C::XS + xcol);
 #pragma unroll
     for (int v = 0; v < C::XV; ++v) {
-      u32x4 w4 = {o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]};
-      dst[v] = w4;
+      dst[v] = xreg[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = dot2_bf16(xreg[v][e], ones, s);
     }
     // threads of one row: 16 / XV of them; reduce their sums
     constexpr int TPR = 16 / C::XV;

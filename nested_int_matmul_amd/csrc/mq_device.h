@@ -14,13 +14,14 @@
 // point: alpha * (2^(8-r) * u - (z + 256)).  For r = 8 the byte is converted
 // through fp32 (exact: every integer below 256 is a bf16), u = t.
 //
-// The order in which one 32-bit word of a packed plane is spread over MFMA
-// operand registers is fixed per r; the activations are staged in LDS in the
-// same order ("permuted"), so both operands of every product agree on k.
-//   r = 4: a word holds 8 indices; operand pairs are (0,4) (1,5) (2,6) (3,7).
-//   r = 2: a word holds 16 indices; pairs (j, j+8) for j = 0..7, the first
-//          four pairs form one 8-element operand, the last four the next.
-//   r = 8: natural order.
+// Plane layout: a 32-bit word holds 32/r consecutive indices, the even-
+// positioned ones in its low 16 bits and the odd-positioned ones in its high
+// 16 bits.  Shifting the word so that field j of both halves lands under the
+// mask puts indices 2j and 2j+1 into the two bf16 halves of one register, so
+// unpacked operands come out in natural k order and the activations are used
+// as stored.
+//   r = 4: a word = one 8-element operand;  r = 2: a word = two operands
+//   (elements 0..7, then 8..15);  r = 8: two words = one operand.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -66,37 +67,101 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Constants of the unpack held in registers: gfx9 VOP3 instructions take no
+// literal operand, so (w & mask) | magic is one v_and_or_b32 only when mask
+// and magic sit in registers.
+struct UnpackK {
+  uint32_t m4, one4, m2, one2, m2a, one2a, m2b;
+  __device__ __forceinline__ static UnpackK make() {
+    UnpackK k{0x00780078u, 0x41804180u, 0x00600060u, 0x40804080u,
+              0x00060006u, 0x42804280u, 0x00180018u};
+    asm volatile("" : "+v"(k.m4), "+v"(k.one4), "+v"(k.m2), "+v"(k.one2), "+v"(k.m2a),
+                 "+v"(k.one2a), "+v"(k.m2b));
+    return k;
+  }
+};
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
 // --- r = 4: one word (8 indices) -> one 8-element operand, order 0,4,1,5,2,6,3,7
-__device__ __forceinline__ bf16x8 unpack_r4(uint32_t w) {
-  const uint32_t m = 0x00780078u, one = 0x41804180u;  // bf16 16.0 in both halves
-  uint32_t p0 = ((w << 3) & m) | one;
-  uint32_t p1 = ((w >> 1) & m) | one;
-  uint32_t p2 = ((w >> 5) & m) | one;
-  uint32_t p3 = ((w >> 9) & m) | one;
+//     (bf16 16.0 in both halves; 16 + t)
+__device__ __forceinline__ bf16x8 unpack_r4(uint32_t w, const UnpackK& k) {
+  uint32_t p0 = and_or(w << 3, k.m4, k.one4);
+  uint32_t p1 = and_or(w >> 1, k.m4, k.one4);
+  uint32_t p2 = and_or(w >> 5, k.m4, k.one4);
+  uint32_t p3 = and_or(w >> 9, k.m4, k.one4);
   return as_bf16x8(p0, p1, p2, p3);
 }
+__device__ __forceinline__ bf16x8 unpack_r4(uint32_t w) { return unpack_r4(w, UnpackK::make()); }
 
 // --- r = 2: one word (16 indices) -> two 8-element operands (h = 0, 1)
 //     h = 0: order 0,8,1,9,2,10,3,11 ; h = 1: order 4,12,5,13,6,14,7,15
+//     (bf16 4.0 in both halves; 4 + t)
 template <int H>
-__device__ __forceinline__ bf16x8 unpack_r2(uint32_t w) {
-  const uint32_t m = 0x00600060u, one = 0x40804080u;  // bf16 4.0 in both halves
+__device__ __forceinline__ bf16x8 unpack_r2(uint32_t w, const UnpackK& k) {
   if (H == 0) {
-    uint32_t p0 = ((w << 5) & m) | one;
-    uint32_t p1 = ((w << 3) & m) | one;
-    uint32_t p2 = ((w << 1) & m) | one;
-    uint32_t p3 = ((w >> 1) & m) | one;
+    uint32_t p0 = and_or(w << 5, k.m2, k.one2);
+    uint32_t p1 = and_or(w << 3, k.m2, k.one2);
+    uint32_t p2 = and_or(w << 1, k.m2, k.one2);
+    uint32_t p3 = and_or(w >> 1, k.m2, k.one2);
     return as_bf16x8(p0, p1, p2, p3);
   } else {
-    uint32_t p0 = ((w >> 3) & m) | one;
-    uint32_t p1 = ((w >> 5) & m) | one;
-    uint32_t p2 = ((w >> 7) & m) | one;
-    uint32_t p3 = ((w >> 9) & m) | one;
+    uint32_t p0 = and_or(w >> 3, k.m2, k.one2);
+    uint32_t p1 = and_or(w >> 5, k.m2, k.one2);
+    uint32_t p2 = and_or(w >> 7, k.m2, k.one2);
+    uint32_t p3 = and_or(w >> 9, k.m2, k.one2);
+    return as_bf16x8(p0, p1, p2, p3);
+  }
+}
+template <int H>
+__device__ __forceinline__ bf16x8 unpack_r2(uint32_t w) { return unpack_r2<H>(w, UnpackK::make()); }
+
+// --- r = 2 with three magics (12 instead of 16 operations per word).  Same
+//     registers as unpack_r2; fields sitting at bits (1,2), (3,4) or (5,6) of
+//     a half after one shift use the bf16 constants 64, 16 or 4, so the
+//     operand is u = offset + t with a per-register offset: registers 0..3 of
+//     an operand (elements 2q, 2q+1) carry 64, 16, 4, 4.  The caller removes
+//     sum_k offset(k) * x[k] (R2MOffset) in fp32.
+struct R2MOffset {
+  __device__ __forceinline__ static float of_reg(int q) {  // q = register 0..3 of an operand
+    return (q & 3) == 0 ? 64.f : ((q & 3) == 1 ? 16.f : 4.f);
+  }
+  // bf16 pair (offset, offset) of register q, for v_dot2 sums
+  __device__ __forceinline__ static uint32_t pair_bits(int q) {
+    return (q & 3) == 0 ? 0x42804280u : ((q & 3) == 1 ? 0x41804180u : 0x40804080u);
+  }
+};
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+template <int H>
+__device__ __forceinline__ bf16x8 unpack_r2m(uint32_t w, const UnpackK& k) {
+  if (H == 0) {
+    const uint32_t w1 = w << 1;
+    uint32_t p0 = and_or(w1, k.m2a, k.one2a);
+    uint32_t p1 = and_or(w1, k.m2b, k.one4);
+    uint32_t p2 = and_or(w1, k.m2, k.one2);
+    uint32_t p3 = and_or(w >> 1, k.m2, k.one2);
+    return as_bf16x8(p0, p1, p2, p3);
+  } else {
+    const uint32_t w2 = w >> 7;
+    uint32_t p0 = and_or(w2, k.m2a, k.one2a);
+    uint32_t p1 = and_or(w2, k.m2b, k.one4);
+    uint32_t p2 = and_or(w2, k.m2, k.one2);
+    uint32_t p3 = and_or(w >> 9, k.m2, k.one2);
     return as_bf16x8(p0, p1, p2, p3);
   }
 }
 
-// --- r = 8: two words (8 bytes) -> one operand, natural order
+// --- r = 8: two words (8 bytes) -> one operand.  A word holds elements
+//     (e0, e2) in bytes 0, 1 and (e1, e3) in bytes 2, 3.
 __device__ __forceinline__ uint32_t bf16_pair_of_bytes(uint32_t lo, uint32_t hi) {
   // lo, hi < 256: the fp32 value is exact and its upper half is the bf16.
   uint32_t a = __float_as_uint((float)lo);
@@ -104,24 +169,12 @@ __device__ __forceinline__ uint32_t bf16_pair_of_bytes(uint32_t lo, uint32_t hi)
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 __device__ __forceinline__ bf16x8 unpack_r8(uint32_t w0, uint32_t w1) {
-  uint32_t p0 = bf16_pair_of_bytes(w0 & 0xffu, (w0 >> 8) & 0xffu);
-  uint32_t p1 = bf16_pair_of_bytes((w0 >> 16) & 0xffu, w0 >> 24);
-  uint32_t p2 = bf16_pair_of_bytes(w1 & 0xffu, (w1 >> 8) & 0xffu);
-  uint32_t p3 = bf16_pair_of_bytes((w1 >> 16) & 0xffu, w1 >> 24);
+  uint32_t p0 = bf16_pair_of_bytes(w0 & 0xffu, (w0 >> 16) & 0xffu);
+  uint32_t p1 = bf16_pair_of_bytes((w0 >> 8) & 0xffu, w0 >> 24);
+  uint32_t p2 = bf16_pair_of_bytes(w1 & 0xffu, (w1 >> 16) & 0xffu);
+  uint32_t p3 = bf16_pair_of_bytes((w1 >> 8) & 0xffu, w1 >> 24);
   return as_bf16x8(p0, p1, p2, p3);
 }
-
-// Activation permutation inside a block of PB = (r == 2 ? 16 : 8) values:
-// position p of the staged block holds source element perm(p).
-template <int R>
-struct XPerm {
-  static constexpr int PB = (R == 2) ? 16 : 8;
-  __device__ __forceinline__ static int src(int p) {
-    if (R == 8) return p;
-    if (R == 4) return (p >> 1) + ((p & 1) << 2);
-    return ((p >> 3) << 2) + ((p >> 1) & 3) + ((p & 1) << 3);
-  }
-};
 
 // fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {

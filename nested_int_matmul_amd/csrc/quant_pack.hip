@@ -72,10 +72,13 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, 
 
 // ---------------------------------------------------------------------------
 // mq_pack: t = min((q + 2^(7-r)) >> (8-r), 2^r - 1) (t = q for r = 8), i.e.
-// round half up of q / 2^(8-r) followed by the clamp of Eq. 6; 8/r indices
-// per byte, index i of a byte in bits [i*r, i*r + r).  Rows need no special
-// handling: K is a multiple of 64, so the flat packing of the [N, K] array is
-// the row-by-row packing.  Each thread writes 16 output bytes (one
+// round half up of q / 2^(8-r) followed by the clamp of Eq. 6.  Layout: each
+// 32-bit word holds 32/r consecutive indices, those at even positions in the
+// low 16 bits and those at odd positions in the high 16 bits, the j-th of a
+// half in bits [j*r, j*r + r) of that half (so that one AND-OR per register
+// yields operand pairs of consecutive k, see mq_device.h).  Rows need no
+// special handling: K is a multiple of 64, so the flat packing of the [N, K]
+// array is the row-by-row packing.  Each thread writes 16 output bytes (one
 // 128-bit store) from 128/r input bytes; the loop is grid-strided.
 // ---------------------------------------------------------------------------
 template <int R>
@@ -105,7 +108,8 @@ __global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ cod
         const int flat = w * PER_WORD + e;  // input byte index within this thread's span
         const uint32_t word = in[flat / 16][(flat / 4) & 3];
         const uint32_t q = (word >> (8 * (flat & 3))) & 0xffu;
-        acc |= slice_byte<R>(q) << (e * R);
+        const int field = (e & 1) ? 16 + (e >> 1) * R : (e >> 1) * R;
+        acc |= slice_byte<R>(q) << field;
       }
       o[w] = acc;
     }

@@ -147,24 +147,31 @@ def pack_indices(t, r: int) -> np.ndarray:
     """Pack r-bit indices t [N, K] into bytes [N, K*r/8].
 
     LAYOUT (a reading; the pages define values, not storage): rows stay rows;
-    within a row, byte j holds the 8/r consecutive elements j*8/r + i,
-    i = 0 .. 8/r - 1, element i in bits [i*r, i*r + r) (little-endian fields).
-    r must divide 8 and K must be a multiple of 8/r.
+    each row is cut into 32-bit words of 32/r consecutive elements.  Inside a
+    word, the elements at even positions 0, 2, 4, ... fill the low 16 bits and
+    the elements at odd positions 1, 3, 5, ... fill the high 16 bits; in each
+    half, the j-th of them occupies bits [j*r, j*r + r) of that half.  Words
+    are stored little-endian.  K must be a multiple of 32/r.
     """
     if r not in (1, 2, 4, 8):
         raise ValueError("byte-aligned packing needs r in {1,2,4,8}")
     t = np.asarray(t, dtype=np.int64)
     n, k = t.shape
-    per = 8 // r
-    if k % per:
-        raise ValueError("K must be a multiple of 8/r")
+    per_word = 32 // r
+    half = 16 // r
+    if k % per_word:
+        raise ValueError("K must be a multiple of 32/r")
     if t.min(initial=0) < 0 or t.max(initial=0) >= 2 ** r:
         raise ValueError("index out of range for r bits")
-    fields = t.reshape(n, k // per, per)
-    out = np.zeros((n, k // per), dtype=np.int64)
-    for i in range(per):
-        out |= fields[:, :, i] << (i * r)
-    return out.astype(np.uint8)
+    elems = t.reshape(n, k // per_word, per_word)
+    word = np.zeros((n, k // per_word), dtype=np.int64)
+    for j in range(half):
+        word |= elems[:, :, 2 * j] << (j * r)            # even position 2j: low half
+        word |= elems[:, :, 2 * j + 1] << (16 + j * r)   # odd position 2j+1: high half
+    out = np.zeros((n, k // per_word, 4), dtype=np.uint8)
+    for b in range(4):
+        out[:, :, b] = (word >> (8 * b)) & 0xFF          # little-endian bytes
+    return out.reshape(n, k * r // 8)
 
 
 def unpack_indices(packed, r: int, k: int) -> np.ndarray:
@@ -172,13 +179,19 @@ def unpack_indices(packed, r: int, k: int) -> np.ndarray:
     if r not in (1, 2, 4, 8):
         raise ValueError("byte-aligned packing needs r in {1,2,4,8}")
     p = np.asarray(packed, dtype=np.int64)
-    per = 8 // r
     n = p.shape[0]
-    if p.shape[1] * per != k:
+    per_word = 32 // r
+    half = 16 // r
+    if p.shape[1] * 8 != k * r or k % per_word:
         raise ValueError("packed width does not match K")
+    b = p.reshape(n, k // per_word, 4)
+    word = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16) | (b[:, :, 3] << 24)
     mask = (1 << r) - 1
-    fields = [(p >> (i * r)) & mask for i in range(per)]
-    return np.stack(fields, axis=2).reshape(n, k)
+    out = np.zeros((n, k // per_word, per_word), dtype=np.int64)
+    for j in range(half):
+        out[:, :, 2 * j] = (word >> (j * r)) & mask
+        out[:, :, 2 * j + 1] = (word >> (16 + j * r)) & mask
+    return out.reshape(n, k)
 
 
 def pack_codes(q, r: int) -> np.ndarray:

@@ -193,15 +193,23 @@ def test_constant_vector():
 
 # ---------------------------------------------------------------- packing
 
-def test_hand_packing():
+def test_hand_slice_indices():
     h = _hand()
     q = np.array([[int(v) for v in h["q"][0]]])
     for row in h["t"]:
         r = int(row[0])
         assert oracle.slice_index(q, r)[0].tolist() == [int(v) for v in row[1:]]
-    for row in h["packed"]:
-        r = int(row[0])
-        assert oracle.pack_codes(q, r)[0].tolist() == [int(v, 16) for v in row[1:]]
+
+
+def test_hand_packed_words():
+    for line in open(os.path.join(GOLDEN, "pack_layout.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, right = line.split(";")
+        vals = [int(v) for v in left.split()]
+        r, t = vals[0], np.array([vals[1:]])
+        assert oracle.pack_indices(t, r)[0].tolist() == [int(b, 16) for b in right.split()]
+        assert oracle.unpack_indices(oracle.pack_indices(t, r), r, t.shape[1]).tolist() == t.tolist()
 
 
 @pytest.mark.parametrize("r", [1, 2, 4, 8])
@@ -209,13 +217,14 @@ def test_pack_bit_layout_and_roundtrip(r):
     rg = np.random.default_rng(r)
     t = rg.integers(0, 2 ** r, size=(3, 64))
     p = oracle.pack_indices(t, r)
-    per = 8 // r
+    per_word = 32 // r
     for n in range(3):
-        for j in range(64 // per):
-            byte = 0
-            for i in range(per):
-                byte += int(t[n, j * per + i]) * 2 ** (i * r)
-            assert p[n, j] == byte
+        for w in range(64 // per_word):
+            e = [int(v) for v in t[n, w * per_word:(w + 1) * per_word]]
+            word = 0
+            for j in range(per_word // 2):
+                word += e[2 * j] * 2 ** (j * r) + e[2 * j + 1] * 2 ** (16 + j * r)
+            assert p[n, 4 * w:4 * w + 4].tolist() == list(word.to_bytes(4, "little"))
     assert np.array_equal(oracle.unpack_indices(p, r, 64), t)
 
 
