@@ -44,6 +44,7 @@ struct Sk {
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
 constexpr int kSkinnyWaves = 4;   // waves per workgroup
+constexpr int kStageBatch = 2;    // fp32 activation loads in flight per thread while staging
 
 template <int R>
 __device__ __forceinline__ bf16x8 unpack_op(const uint32_t* d, int i, const UnpackK& k) {
@@ -155,7 +156,7 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
     }
   }
 
-  const int Kpad = ((K + 255) / 256) * 256;
+  const int Kpad = ((K + 511) / 512) * 512;
   const int nchunks = (Kpad + kc - 1) / kc;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};  // per-channel: raw sum; grouped: running scaled total
@@ -168,6 +169,7 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
   // all lanes read activations: columns past M duplicate column M - 1 (ignored)
   const int xcol = col < M ? col : M - 1;
 
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x0, (uint32_t)((int64_t)M * K * 2));
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(P.alpha, (uint32_t)((int64_t)N * G * 4));
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(P.zero, (uint32_t)((int64_t)N * G * 4));
 
@@ -188,17 +190,60 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
     auto loff = [&](int st) -> uint32_t {
       return st < hi ? cbase + (uint32_t)(st * (C::STEP * R / 8)) : 0x80000000u;
     };
-    // ---- first DEPTH weight loads of this chunk, before staging x
     typename LD::T buf[C::DEPTH];
+    __syncthreads();
+    // ---- stage x[:, ck0 : ck0 + clen) as stored, then form the per-128 sums
+    //      of x and of offset * x (v_dot2 against constant bf16 pairs).
+    constexpr int PB = C::PB;
+    if (P.xmode == kXBf16) {
+      // bf16 activations: buffer-to-LDS loads, one 1 KiB piece per wave
+      // instruction; columns past K read as zeros through the bounds check.
+      const int pieces = clen / 512;  // per row
+      for (int pc = wave; pc < M * pieces; pc += kSkinnyWaves) {
+        const int m = pc / pieces, j = pc - m * pieces;
+        const int k = ck0 + j * 512 + lane * 8;
+        const uint32_t off = k < K ? (uint32_t)((m * K + k) * 2) : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (__attribute__((address_space(3))) void*)(xs + (size_t)m * xstride + j * 512), 16,
+            off, 0, 0, 0);
+      }
+    } else {
+      // fp32 sources (rounded to bf16 on the way): through registers, up to
+      // kStageBatch loads in flight per thread
+      const int bpr = clen / PB;
+      const int total = M * bpr;
+      const int nthr = blockDim.x;
+      for (int b0 = 0; b0 < total; b0 += kStageBatch * nthr) {
+        u32x4 w4[kStageBatch];
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j) {
+          const int b = b0 + j * nthr + threadIdx.x;
+          u32x4 z4 = {0u, 0u, 0u, 0u};
+          w4[j] = z4;
+          if (b < total) {
+            const int m = b / bpr;
+            const int kb = (b - m * bpr) * PB;
+            if (ck0 + kb < K) w4[j] = load_x8(P, m, ck0 + kb);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j) {
+          const int b = b0 + j * nthr + threadIdx.x;
+          if (b < total) {
+            const int m = b / bpr;
+            const int kb = (b - m * bpr) * PB;
+            *reinterpret_cast<u32x4*>(xs + (size_t)m * xstride + kb) = w4[j];
+          }
+        }
+      }
+    }
+    // ---- first DEPTH weight loads of this chunk, issued behind the staging
+    //      loads so that waiting for the activations does not wait for them
 #pragma unroll
     for (int j = 0; j < C::DEPTH; ++j) buf[j] = LD::load(wr, loff(lo + j));
-
     __syncthreads();
-    // ---- stage x[:, ck0 : ck0 + clen) as stored, and per-128 sums of x and
-    //      of offset * x (v_dot2 against constant bf16 pairs)
     {
-      constexpr int PB = C::PB;
-      const int bpr = clen / PB;  // blocks per row in this chunk
+      const int bpr = clen / PB;
       const int total = M * bpr;
       const uint32_t ones = 0x3F803F80u;
       for (int b0 = 0; b0 < total; b0 += blockDim.x) {
@@ -208,9 +253,7 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
         if (b < total) {
           m = b / bpr;
           kb = (b - m * bpr) * PB;
-          u32x4 w4 = {0u, 0u, 0u, 0u};
-          if (ck0 + kb < K) w4 = load_x8(P, m, ck0 + kb);
-          *reinterpret_cast<u32x4*>(xs + (size_t)m * xstride + kb) = w4;
+          const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + kb);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             s = dot2_bf16(w4[q], ones, s);
@@ -260,7 +303,6 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
         const int st = base + j;
         uint32_t d[C::V / 4];
         LD::words(buf[j], d);
-        buf[j] = LD::load(wr, loff(st + C::DEPTH));
         const uint16_t* xp = xrow + st * C::STEP;
         if (st < hi) {
         if constexpr (GROUPED) {
@@ -299,6 +341,8 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
           }
         }
         }
+        // refill this slot after its last use, so the buffer stays in place
+        buf[j] = LD::load(wr, loff(st + C::DEPTH));
       }
     }
   }
@@ -353,18 +397,18 @@ hipError_t launch_skinny(SkinnyArgs& args, int r, bool grouped, hipStream_t stre
   const int waves = kSkinnyWaves;
   const int M = args.M;
   const int step = step_codes(r, grouped);
-  // activation chunk: at most 64 KiB of staged bf16, a multiple of 256 codes
+  // activation chunk: at most 64 KiB of staged bf16, a multiple of 512 codes
   int kmax = 0;
   for (int i = 0; i < args.count; ++i) kmax = args.p[i].K > kmax ? args.p[i].K : kmax;
-  const int kpad_max = ((kmax + 255) / 256) * 256;
-  int kc = (32768 / M) / 256 * 256;
+  const int kpad_max = ((kmax + 511) / 512) * 512;
+  int kc = (32768 / M) / 512 * 512;
   if (kc > kpad_max) kc = kpad_max;
   args.kc = kc;
   // split of K: at least ~12 load steps per wave
   int steps_per_wave[kMaxProblems];
   for (int i = 0; i < args.count; ++i) {
     SkinnyProblem& p = args.p[i];
-    const int kpad = ((p.K + 255) / 256) * 256;
+    const int kpad = ((p.K + 511) / 512) * 512;
     const int steps = kpad / step;
     const int spg = grouped ? 128 / step : 1;
     const int units = steps / spg;
