@@ -265,6 +265,7 @@ static hipError_t launch_r(const uint8_t* packed, const float* alpha, const floa
 hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                        int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        void*, hipStream_t s) {
+  if (M >= 256) return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, s);
   switch (r) {
     case 2: return launch_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
     case 4: return launch_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);

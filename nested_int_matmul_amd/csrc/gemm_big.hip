@@ -1,0 +1,324 @@
+// Large-batch product (prefill-sized M) against r-bit planes on bf16 matrix
+// cores:
+//   y[m, n] = sum_g alpha[n, g] * (2^(8-r) * sum_{k in g} x[m, k] u[n, k]
+//                                   - (z[n, g] + shift) * sum_{k in g} x[m, k])
+// with u the exact bf16 operand of the index t (mq_device.h), which equals
+// sum_k x[m, k] (S(q[n, k], r) - z[n, g]) alpha[n, g]
+// ("Matryoshka Quantization" explainer, §3.4: Eq. 6 and Eq. 1).
+//
+// Tiling (gfx950, v_mfma_f32_32x32x16_bf16, A = activations, B = weights):
+//  - a workgroup of 8 waves computes a 256 x 256 tile of y; each wave owns a
+//    128 (m) x 64 (n) sub-tile = 4 x 2 blocks of 32 x 32 (128 fp32
+//    accumulators per lane);
+//  - each K iteration covers 64 codes: the activation tile (256 x 64 bf16) and
+//    the packed weight tile (256 rows x 64 codes) are brought into LDS with
+//    buffer-to-LDS loads, double-buffered, one barrier per iteration; the
+//    activation tile is XOR-swizzled in 16-byte chunks so that the operand
+//    reads of 8 consecutive rows hit distinct banks;
+//  - one accumulator set carries all groups: at the end of group g it holds
+//    C_g = P_g + (running total) / a_g in units of 1/a_g (a_g = alpha * 2^(8-r));
+//    the group's zero-point term is subtracted in those units and the set is
+//    rescaled to the next group's units by alpha_g / alpha_{g+1}
+//    (two VALU operations per accumulator per group, and the accumulator
+//    stays centred, which keeps fp32 cancellation small);
+//  - the per-group row sums of x come from the staged tiles (v_dot2);
+//  - tiles are mapped to XCDs so that the workgroups of one XCD share
+//    activation rows (its L2 keeps them).
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+namespace big {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int WAVES = 8, THREADS = 64 * WAVES;
+constexpr int MB = 4, NB = 2;               // 32x32 blocks per wave (m, n)
+constexpr int XT_BYTES = BM * BK * 2;       // staged activation tile
+template <int R>
+struct Cfg {
+  static constexpr int WROW = BK * R / 8;   // packed bytes per weight row per iteration
+  static constexpr int WT_BYTES = BN * WROW;
+  static constexpr int LDS = 2 * XT_BYTES + 2 * WT_BYTES + BM * 4;
+};
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int R, bool GROUPED>
+__global__ void __launch_bounds__(THREADS)
+    gemm_big_kernel(const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
+                    const float* __restrict__ zero, const uint16_t* __restrict__ x,
+                    float* __restrict__ y, int M, int N, int K, int group, int mt, int nt) {
+  using C = Cfg<R>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* xs0 = smem;                                  // [2][BM][128 B] swizzled
+  unsigned char* ws0 = smem + 2 * XT_BYTES;                   // [2][BN][WROW]
+  float* sxg = reinterpret_cast<float*>(smem + 2 * XT_BYTES + 2 * C::WT_BYTES);  // [BM]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+
+  // ---- tile of this workgroup: the workgroups of one XCD (id % 8) walk
+  //      consecutive tiles in m-major order so that they share activations
+  int t = blockIdx.x;
+  const int T = mt * nt;
+  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int m0 = (t / nt) * BM, n0 = (t % nt) * BN;
+
+  const int rowbytes = K * R / 8;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((int64_t)N * rowbytes));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  const int G = K / group;
+  const int iters = K / BK;
+  constexpr int IPG = 128 / BK;  // iterations per group of 128 (grouped)
+  const UnpackK uk = UnpackK::make();
+
+  // ---- per-iteration staging (buffer-to-LDS, 1 KiB per wave instruction)
+  auto stage = [&](int it, int buf) {
+    const int k0 = it * BK;
+    unsigned char* xs = xs0 + buf * XT_BYTES;
+#pragma unroll
+    for (int q = 0; q < BM * 128 / 1024 / WAVES; ++q) {
+      const int rb = (wave * (BM * 128 / 1024 / WAVES) + q) * 8;  // first row of this piece
+      const int row = rb + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);                       // logical 16-byte chunk
+      const int m = m0 + row;
+      const uint32_t off = m < M ? (uint32_t)(((int64_t)m * K + k0 + c * 8) * 2) : 0x80000000u;
+      lds_dma16(xr, xs + rb * 128, off);
+    }
+    unsigned char* ws = ws0 + buf * C::WT_BYTES;
+    constexpr int WPIECES = C::WT_BYTES / 1024;
+    for (int q = wave; q < WPIECES; q += WAVES) {
+      const int byte = q * 1024 + lane * 16;
+      const int row = byte / C::WROW, col = byte % C::WROW;
+      const int n = n0 + row;
+      const uint32_t off =
+          n < N ? (uint32_t)n * (uint32_t)rowbytes + (uint32_t)(k0 * R / 8 + col) : 0x80000000u;
+      lds_dma16(wr, ws + q * 1024, off);
+    }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int l32 = lane & 31, s = lane >> 5;
+  // per-lane weight columns and their scales for the current group
+  int ncol[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) ncol[j] = n0 + wn * 64 + j * 32 + l32;
+  // columns past N read the last row's scales (unconditional loads; those
+  // outputs are not stored)
+  int nld[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) nld[j] = ncol[j] < N ? ncol[j] : N - 1;
+  auto scale = [&](int j, int g) -> float { return alpha[(int64_t)nld[j] * G + g]; };
+  auto zraw = [&](int j, int g) -> float { return zero[(int64_t)nld[j] * G + g]; };
+
+  // row sums of x: thread (row = tid / 2, half = tid % 2) sums 32 codes per iteration
+  const int srow = tid >> 1, shalf = tid & 1;
+  float srun = 0.f;
+  const uint32_t ones = 0x3F803F80u;
+
+  // scale factors of the next group transition, loaded one iteration ahead
+  // (before that iteration's staging loads, so using them never waits for
+  // the staging)
+  float cz[NB], rho[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    cz[j] = 0.f;
+    rho[j] = 1.f;
+  }
+
+  // the first group's update reads these (cz = 0): keep them finite
+  if (GROUPED && shalf == 0) sxg[srow] = 0.f;
+  stage(0, 0);
+  // one trip of the outer loop = one group of 128 codes = IPG iterations
+#pragma unroll 1
+  for (int it0 = 0; it0 < iters; it0 += IPG) {
+#pragma unroll
+    for (int it2 = 0; it2 < IPG; ++it2) {
+      const int it = it0 + it2;
+      if (!GROUPED && it >= iters) break;  // per-channel K may end mid-pair
+      const int buf = it & 1;
+      __syncthreads();  // staging of `it` complete (vmcnt waited by the compiler), buf^1 free
+      // raw scales of the group ending with this trip and of the next one,
+      // issued before the staging loads so that using them never waits for those
+      float a0n[NB], a1n[NB], z0n[NB];
+      const bool prep = GROUPED && it2 == IPG - 1 && it + 1 < iters;
+      if (prep) {
+        const int g = it / IPG;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          a0n[j] = scale(j, g);
+          a1n[j] = scale(j, g + 1);
+          z0n[j] = zraw(j, g);
+        }
+      }
+      if (it + 1 < iters) stage(it + 1, buf ^ 1);
+
+      // ---- row sums of this tile's activations
+      {
+        const unsigned char* xs = xs0 + buf * XT_BYTES;
+        float sp = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int c = shalf * 4 + c4;
+          const u32x4 w =
+              *reinterpret_cast<const u32x4*>(xs + srow * 128 + ((c ^ (srow & 7)) * 16));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sp = dot2_bf16(w[e], ones, sp);
+        }
+        sp += __shfl_xor(sp, 1);
+        srun += sp;
+        if (GROUPED && it2 == IPG - 1) {
+          if (shalf == 0) sxg[srow] = srun;
+          srun = 0.f;
+        }
+      }
+
+      // ---- 4 k-steps of MFMAs; on the first iteration of a group (after the
+      //      first), each block first takes the previous group's zero-point
+      //      term and moves to this group's units (cz = 0, rho = 1 before)
+      const unsigned char* xs = xs0 + buf * XT_BYTES;
+      const unsigned char* ws = ws0 + buf * C::WT_BYTES;
+      uint32_t wv[NB][R];  // this lane's packed bytes of the iteration (4R bytes) per n-block
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const unsigned char* p = ws + (wn * 64 + j * 32 + l32) * C::WROW + s * (4 * R);
+        if (R == 2) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+          wv[j][0] = v[0]; wv[j][1] = v[1];
+        } else {
+#pragma unroll
+          for (int h = 0; h < R / 4; ++h) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * h);
+            wv[j][4 * h + 0] = v[0]; wv[j][4 * h + 1] = v[1];
+            wv[j][4 * h + 2] = v[2]; wv[j][4 * h + 3] = v[3];
+          }
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 a[MB], b[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int row = wm * 128 + i * 32 + l32;
+          const int c = 4 * s + kk;
+          const u32x4 v =
+              *reinterpret_cast<const u32x4*>(xs + row * 128 + ((c ^ (row & 7)) * 16));
+          a[i] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (R == 4) b[j] = unpack_r4(wv[j][kk], uk);
+          else if (R == 2) b[j] = (kk & 1) ? unpack_r2<1>(wv[j][kk >> 1], uk)
+                                           : unpack_r2<0>(wv[j][kk >> 1], uk);
+          else b[j] = unpack_r8(wv[j][2 * kk], wv[j][2 * kk + 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          f32x4 sv[4];
+          if (GROUPED && it2 == 0 && kk == 0) {
+#pragma unroll
+            for (int eq = 0; eq < 4; ++eq)
+              sv[eq] = *reinterpret_cast<const f32x4*>(sxg + wm * 128 + i * 32 + eq * 8 + s * 4);
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            if (GROUPED && it2 == 0 && kk == 0) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const float av0 = acc[i][j][e];
+                acc[i][j][e] = rho[j] * (av0 - cz[j] * sv[e >> 2][e & 3]);
+              }
+            }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+      if (prep) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          cz[j] = (z0n[j] + Enc<R>::kOffsetShift) * (1.0f / Enc<R>::kStep);
+          rho[j] = a0n[j] / a1n[j];
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: last group's (or the only group's) zero-point term and scale
+  if (!GROUPED && shalf == 0) sxg[srow] = srun;
+  __syncthreads();
+  const int glast = G - 1;
+  float av[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    cz[j] = (zraw(j, glast) + Enc<R>::kOffsetShift) * (1.0f / Enc<R>::kStep);
+    av[j] = scale(j, glast) * Enc<R>::kStep;
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int eq = 0; eq < 4; ++eq) {
+      const int row = wm * 128 + i * 32 + eq * 8 + s * 4;
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(sxg + row);
+#pragma unroll
+      for (int e3 = 0; e3 < 4; ++e3) {
+        const int m = m0 + row + e3;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (ncol[j] >= N) continue;
+          const float v = av[j] * (acc[i][j][eq * 4 + e3] - cz[j] * sv[e3]);
+          y[(int64_t)m * N + ncol[j]] = v;
+        }
+      }
+    }
+}
+
+}  // namespace big
+
+template <int R>
+static hipError_t launch_big_r(const uint8_t* packed, const float* alpha, const float* zero,
+                               int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                               float* y, hipStream_t s) {
+  using namespace big;
+  const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + BN - 1) / BN);
+  const size_t lds = Cfg<R>::LDS;
+  static bool attr[2] = {false, false};  // benign race: idempotent attribute calls
+  const bool grouped = group != K;
+  const void* fn = grouped ? (const void*)gemm_big_kernel<R, true> : (const void*)gemm_big_kernel<R, false>;
+  if (!attr[grouped]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr[grouped] = true;
+  }
+  dim3 grid((unsigned)(mt * nt)), block(THREADS);
+  if (grouped)
+    hipLaunchKernelGGL((gemm_big_kernel<R, true>), grid, block, lds, s, packed, alpha, zero, x, y,
+                       (int)M, (int)N, (int)K, (int)group, mt, nt);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<R, false>), grid, block, lds, s, packed, alpha, zero, x, y,
+                       (int)M, (int)N, (int)K, (int)group, mt, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_big(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                           int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                           float* y, hipStream_t s) {
+  switch (r) {
+    case 2: return launch_big_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
+    case 4: return launch_big_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);
+    default: return launch_big_r<8>(packed, alpha, zero, group, N, K, x, M, y, s);
+  }
+}
+
+}  // namespace mq

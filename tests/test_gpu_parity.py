@@ -163,7 +163,7 @@ def test_error_enqueues_nothing():
 
 @pytest.mark.parametrize("r", [8, 4, 2])
 @pytest.mark.parametrize("group", ["K", 128])
-@pytest.mark.parametrize("M", [9, 16, 64, 130])
+@pytest.mark.parametrize("M", [9, 16, 64, 130, 300])
 def test_gemm_small(r, group, M):
     n, k = 200, (640 if group == "K" else 768)
     g = k if group == "K" else 128
