@@ -1,0 +1,371 @@
+// Small-batch product (9 <= M <= 64 activation rows) against r-bit planes:
+//   y[m, n] = sum_k x[m, k] (S(q[n, k], r) - z[n, g]) alpha[n, g]
+// ("Matryoshka Quantization" explainer, §3.4: Eq. 6 slicing, Eq. 1
+// dequantization).  At these M the product still streams the planes out of
+// HBM (every packed byte is used M times, on the matrix cores).
+//
+// Design (gfx950, v_mfma_f32_32x32x16_bf16, A = activations, B = weights):
+//  - A workgroup owns a panel of 32 * NW weight rows (one 32-row block per
+//    wave) and a slice of K of at most 1024 codes.  The activations of that
+//    slice (all M rows, padded to 32 * MB) are brought into LDS once with
+//    buffer-to-LDS loads; the per-128 sums of x are formed from LDS.
+//  - Each lane streams 16 contiguous packed bytes of one weight row per step
+//    straight into registers (no LDS for weights: every row has one reader),
+//    DEPTH steps ahead of use, and unpacks them into exact bf16 integers
+//    (mq_device.h).  One unpacked operand feeds MB matrix-core products.
+//  - alpha and z of the panel's groups are staged in LDS with the
+//    activations; group-128 scales are applied at each group end in fp32
+//    (y += alpha 2^(8-r) P_g - alpha (z + shift) sum_g x), per-channel scales
+//    once at the end.
+//  - When K is split over several workgroups, each writes its fp32 partial
+//    tile to the workspace and a second kernel sums the slices in a fixed
+//    order (deterministic).
+#include <algorithm>
+
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+namespace panel {
+
+constexpr int kMaxWaves = 8;
+constexpr int kKSliceMax = 1024;  // codes of K per workgroup (activations resident in LDS)
+constexpr int kXPadE = 8;         // bf16 padding per staged activation row
+constexpr int DEPTH = 8;          // weight loads in flight per lane
+
+template <int R>
+struct Pc {
+  static constexpr int CPL = 16 * 8 / R;    // codes per lane per step (16 bytes)
+  static constexpr int STEP = 2 * CPL;      // codes per row per step (two lane slots)
+  static constexpr int MFMAS = CPL / 8;     // 16-deep products per step per m-block
+  static constexpr int SPG = 128 / STEP;    // steps per group of 128
+};
+
+struct Args {
+  const uint8_t* packed;
+  const float* alpha;
+  const float* zero;
+  const uint16_t* x;
+  float* y;     // output [M, N] (one K slice) or the partial slices [S][M][N]
+  int M, N, K, G;
+  int kslice;   // codes of K per workgroup (multiple of 512)
+};
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int R>
+__device__ __forceinline__ bf16x8 unpack_b(const uint32_t* d, int i, const UnpackK& k) {
+  if (R == 4) return unpack_r4(d[i], k);
+  if (R == 2) return (i & 1) ? unpack_r2<1>(d[i >> 1], k) : unpack_r2<0>(d[i >> 1], k);
+  return unpack_r8(d[2 * i], d[2 * i + 1]);
+}
+
+template <int R, int MB, int NW, bool GROUPED>
+__global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
+  using C = Pc<R>;
+  constexpr int ROWS = 32 * MB;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, s = lane >> 5;
+  const int M = a.M, N = a.N, K = a.K, G = a.G;
+  const int k0 = (int)blockIdx.y * a.kslice;
+  const int klen = min(a.kslice, K - k0);
+  const int kpad = (klen + 511) & ~511;           // staged codes (zeros past K)
+  const int ngl = (klen + 127) >> 7;              // groups of 128 in the slice
+  const int steps = (klen + C::STEP - 1) / C::STEP;
+  const int xstride = a.kslice + kXPadE;          // elements
+
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [ROWS][xstride]
+  float* sxs = reinterpret_cast<float*>(smem + (size_t)ROWS * xstride * 2);      // [ngl][ROWS]
+  float* azs = sxs + (kKSliceMax / 128) * ROWS;                                  // [2][NW*32][8]
+
+  const int n0 = (int)blockIdx.x * NW * 32;
+  const int n = n0 + wave * 32 + l32;  // weight row of this lane
+  const int rowbytes = K * R / 8;
+  const uint32_t plane = (uint32_t)((int64_t)N * rowbytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.packed, plane);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)M * K * 2));
+
+  // ---- scales of the panel: per-channel in registers; group-128 staged in
+  //      LDS as [alpha | zero][row][group of the slice] (loads issued first,
+  //      unconditionally: entries past N or past the slice read entry 0)
+  float pa = 0.f, pz = 0.f;
+  float ga4[4], gz4[4];
+  if (!GROUPED) {
+    const int nc = n < N ? n : N - 1;
+    pa = a.alpha[nc];
+    pz = a.zero[nc];
+  } else {
+    const int g0 = k0 >> 7;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + e * 64 * NW;  // NW*32 rows x 8 groups, 4 entries per thread
+      const int rr = idx >> 3, gg = idx & 7;
+      const int nn = n0 + rr;
+      const bool ok = nn < N && gg < ngl;
+      const int64_t off = ok ? (int64_t)nn * G + g0 + gg : 0;
+      const float av = a.alpha[off], zv = a.zero[off];
+      ga4[e] = ok ? av : 0.f;
+      gz4[e] = ok ? zv : 0.f;
+    }
+  }
+
+  // ---- activations of the slice: one 1 KiB piece (512 codes of one row)
+  //      per wave instruction
+  {
+    const int pieces = kpad >> 9;  // per row
+    for (int pc = wave; pc < ROWS * pieces; pc += NW) {
+      const int m = pc / pieces, j = pc - m * pieces;
+      const int k = k0 + j * 512 + lane * 8;
+      const uint32_t off = (m < M && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
+      lds_dma16(xr, xs + (size_t)m * xstride + j * 512, off);
+    }
+  }
+
+  // ---- first DEPTH weight loads (behind the staging loads)
+  const uint32_t row_off = n < N ? (uint32_t)n * (uint32_t)rowbytes : plane;
+  const uint32_t base_off = row_off + (uint32_t)((k0 + s * C::CPL) * R / 8);
+  auto loff = [&](int st) -> uint32_t {
+    return st < steps ? base_off + (uint32_t)(st * (C::STEP * R / 8)) : 0x80000000u;
+  };
+  u32x4 buf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) buf[j] = buf_load16(wr, loff(j));
+
+  if (GROUPED) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + e * 64 * NW;
+      azs[idx] = ga4[e];
+      azs[NW * 32 * 8 + idx] = gz4[e];
+    }
+  }
+  __syncthreads();
+
+  // ---- per-128 sums of the staged activations: thread -> (row, 8 codes),
+  //      16 consecutive threads cover one group
+  {
+    const uint32_t ones = 0x3F803F80u;
+    const int cpr = kpad >> 3;             // 8-code chunks per row
+    const int total = ROWS * cpr;
+    for (int b = tid; b < total; b += 64 * NW) {
+      const int m = b / cpr, c = b - m * cpr;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + c * 8);
+      float sp = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sp = dot2_bf16(w[q], ones, sp);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) sp += __shfl_xor(sp, off);
+      if ((c & 15) == 0 && (c >> 4) < ngl) sxs[(c >> 4) * ROWS + m] = sp;
+    }
+  }
+  __syncthreads();
+
+  // ---- stream the slice
+  const UnpackK uk = UnpackK::make();
+  f32x16 acc[MB], part[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc[mb][e] = 0.f;
+      part[mb][e] = 0.f;
+    }
+  const uint16_t* xa = xs + (size_t)l32 * xstride + s * C::CPL;
+  const float* az_row = azs + (wave * 32 + l32) * 8;
+  // group-128: each group's products accumulate onto -cz * sum_g x, with
+  // cz = (z + shift) / 2^(8-r), so that at the group's end
+  // part = sum_g x u - cz sum_g x and y += alpha 2^(8-r) part
+  auto start_group = [&](int gl) {
+    const float cz = (az_row[NW * 32 * 8 + gl] + Enc<R>::kOffsetShift) * (1.0f / Enc<R>::kStep);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int eq = 0; eq < 4; ++eq) {
+        const f32x4 sv =
+            *reinterpret_cast<const f32x4*>(sxs + gl * ROWS + mb * 32 + eq * 8 + s * 4);
+#pragma unroll
+        for (int e3 = 0; e3 < 4; ++e3) part[mb][eq * 4 + e3] = -cz * sv[e3];
+      }
+  };
+  if (GROUPED) start_group(0);
+
+#pragma unroll 1
+  for (int base = 0; base < steps; base += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      const int st = base + j;
+      if (st < steps) {
+        const uint32_t d[4] = {buf[j][0], buf[j][1], buf[j][2], buf[j][3]};
+        const uint16_t* xp = xa + st * C::STEP;
+#pragma unroll
+        for (int i = 0; i < C::MFMAS; ++i) {
+          const bf16x8 b = unpack_b<R>(d, i, uk);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(xp + (size_t)mb * 32 * xstride + 8 * i);
+            const bf16x8 av = __builtin_bit_cast(bf16x8, v);
+            if (GROUPED) {
+              part[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, part[mb], 0, 0, 0);
+            } else {
+              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[mb], 0, 0, 0);
+            }
+          }
+        }
+        if (GROUPED && (j % C::SPG) == C::SPG - 1) {
+          const int gl = st / C::SPG;
+          const float av = az_row[gl] * Enc<R>::kStep;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mb][e] = fmaf(av, part[mb][e], acc[mb][e]);
+          start_group(gl + 1 < ngl ? gl + 1 : gl);
+        }
+      }
+      // refill this slot after its last use
+      buf[j] = buf_load16(wr, loff(st + DEPTH));
+    }
+  }
+
+  // ---- epilogue: lane holds column n, rows mb*32 + eq*8 + s*4 + e3
+  float* out = a.y + (size_t)blockIdx.y * M * N;
+  if (n < N) {
+    float ep_a = 0.f, ep_b = 0.f;
+    if (!GROUPED) {
+      ep_a = pa * Enc<R>::kStep;
+      ep_b = pa * (pz + Enc<R>::kOffsetShift);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int eq = 0; eq < 4; ++eq) {
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+        if (!GROUPED) {
+          for (int gl = 0; gl < ngl; ++gl)
+            tot += *reinterpret_cast<const f32x4*>(sxs + gl * ROWS + mb * 32 + eq * 8 + s * 4);
+        }
+#pragma unroll
+        for (int e3 = 0; e3 < 4; ++e3) {
+          const int m = mb * 32 + eq * 8 + s * 4 + e3;
+          if (m < M) {
+            const float v = GROUPED ? acc[mb][eq * 4 + e3]
+                                    : ep_a * acc[mb][eq * 4 + e3] - ep_b * tot[e3];
+            out[(size_t)m * N + n] = v;
+          }
+        }
+      }
+  }
+}
+
+// y = sum over S slices of the partial tiles, in slice order.
+__global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ part,
+                                                     float* __restrict__ y, int64_t count,
+                                                     int S) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t n4 = count >> 2;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    f32x4 v = reinterpret_cast<const f32x4*>(part)[i];
+    for (int sl = 1; sl < S; ++sl) v += reinterpret_cast<const f32x4*>(part + sl * count)[i];
+    reinterpret_cast<f32x4*>(y)[i] = v;
+  }
+  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += stride) {
+    float v = part[i];
+    for (int sl = 1; sl < S; ++sl) v += part[sl * count + i];
+    y[i] = v;
+  }
+}
+
+}  // namespace panel
+
+// ---------------------------------------------------------------------------
+// Host planning
+// ---------------------------------------------------------------------------
+
+struct PanelPlan {
+  int nw, kslice, slices, panels;
+};
+
+static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  PanelPlan p;
+  p.nw = 8;
+  p.panels = (int)((N + 32 * p.nw - 1) / (32 * p.nw));
+  // K slice: the largest multiple of 512 (at most 1024) that still gives at
+  // least ~1.5 workgroups per compute unit
+  p.kslice = panel::kKSliceMax;
+  while (p.kslice > 512 && (int64_t)p.panels * ((K + p.kslice - 1) / p.kslice) < 384)
+    p.kslice -= 512;
+  p.slices = (int)((K + p.kslice - 1) / p.kslice);
+  return p;
+}
+
+size_t panel_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const PanelPlan p = plan_panel(M, N, K);
+  return p.slices > 1 ? (size_t)p.slices * M * N * 4 : 0;
+}
+
+template <int R, int MB, bool GROUPED>
+static hipError_t launch_panel_t(const panel::Args& a, const PanelPlan& p, hipStream_t s) {
+  constexpr int NW = 8;
+  const size_t lds = (size_t)32 * MB * (p.kslice + panel::kXPadE) * 2 +
+                     (size_t)(panel::kKSliceMax / 128) * 32 * MB * 4 + (size_t)2 * NW * 32 * 8 * 4;
+  static bool attr = false;  // benign race: idempotent attribute call
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)panel::panel_kernel<R, MB, NW, GROUPED>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((panel::panel_kernel<R, MB, NW, GROUPED>), dim3(p.panels, p.slices),
+                     dim3(64 * NW), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                             int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                             float* y, void* workspace, hipStream_t s) {
+  const PanelPlan p = plan_panel(M, N, K);
+  panel::Args a;
+  a.packed = packed;
+  a.alpha = alpha;
+  a.zero = zero;
+  a.x = x;
+  a.y = p.slices > 1 ? static_cast<float*>(workspace) : y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.G = (int)(K / group);
+  a.kslice = p.kslice;
+  const bool grouped = group != K;
+  const int mb = M > 32 ? 2 : 1;
+  hipError_t e;
+  switch (r * 4 + (mb - 1) * 2 + (grouped ? 1 : 0)) {
+    case 8: e = launch_panel_t<2, 1, false>(a, p, s); break;
+    case 9: e = launch_panel_t<2, 1, true>(a, p, s); break;
+    case 10: e = launch_panel_t<2, 2, false>(a, p, s); break;
+    case 11: e = launch_panel_t<2, 2, true>(a, p, s); break;
+    case 16: e = launch_panel_t<4, 1, false>(a, p, s); break;
+    case 17: e = launch_panel_t<4, 1, true>(a, p, s); break;
+    case 18: e = launch_panel_t<4, 2, false>(a, p, s); break;
+    case 19: e = launch_panel_t<4, 2, true>(a, p, s); break;
+    case 32: e = launch_panel_t<8, 1, false>(a, p, s); break;
+    case 33: e = launch_panel_t<8, 1, true>(a, p, s); break;
+    case 34: e = launch_panel_t<8, 2, false>(a, p, s); break;
+    default: e = launch_panel_t<8, 2, true>(a, p, s); break;
+  }
+  if (e != hipSuccess || p.slices == 1) return e;
+  const int64_t count = M * N;
+  const int blocks = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 2048);
+  hipLaunchKernelGGL(panel::reduce_slices, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const float*>(workspace), y, count, p.slices);
+  return hipGetLastError();
+}
+
+}  // namespace mq

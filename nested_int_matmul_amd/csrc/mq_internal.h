@@ -47,6 +47,10 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_
                        hipStream_t stream);
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+size_t panel_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                             int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                             float* y, void* workspace, hipStream_t s);
 hipError_t launch_gemm_big(const uint8_t* packed, int r, const float* alpha, const float* zero,
                            int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            float* y, hipStream_t s);
