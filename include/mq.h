@@ -131,10 +131,23 @@ typedef struct mq_gemv_problem {
  * in one launch (for example the three matrices of a feed-forward block, or
  * the projections that share one input).  Same definitions, constraints and
  * result as calling mq_gemv on each problem; outputs must not overlap.
- * 1 <= count <= 8.
+ * 1 <= count <= 16.
  */
 mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int64_t M,
                           void* stream);
+
+/*
+ * mq_gemv_mixed: as mq_gemv_grouped, but problem i is sliced to its own
+ * precision r[i] (2, 4 or 8): several precisions of one stored int8 model
+ * served in one launch ("Matryoshka Quantization" explainer, §3.4
+ * "Mix'n'Match and Interpolative Slicing": any r, chosen per consumer, from
+ * the same codes).  Each result equals mq_gemv on that problem at r[i].
+ *   r  host array of `count` precisions, read during the call only
+ * Problems with per-channel and group-128 scales may be mixed; they take one
+ * launch per granularity.  1 <= count <= 16.
+ */
+mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
+                        void* stream);
 
 /*
  * mq_gemm: the same product for any number of activation rows M >= 1 (small

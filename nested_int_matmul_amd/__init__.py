@@ -28,7 +28,8 @@ STATUS_NAMES = {
 # Every exported symbol of include/mq.h.
 EXPORTS = (
     "mq_status_string", "mq_last_hip_error", "mq_version", "mq_packed_bytes",
-    "mq_quantize", "mq_pack", "mq_gemv", "mq_gemv_grouped", "mq_gemm_workspace_bytes",
+    "mq_quantize", "mq_pack", "mq_gemv", "mq_gemv_grouped", "mq_gemv_mixed",
+    "mq_gemm_workspace_bytes",
     "mq_gemm", "mq_mixnmatch_workspace_bytes", "mq_mixnmatch_workspace_offsets",
     "mq_mixnmatch_forward",
 )
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
     L.mq_gemv.argtypes = [vp, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp]
     L.mq_gemv_grouped.restype = i32
     L.mq_gemv_grouped.argtypes = [ctypes.POINTER(GemvProblem), i32, i32, i64, vp]
+    L.mq_gemv_mixed.restype = i32
+    L.mq_gemv_mixed.argtypes = [ctypes.POINTER(GemvProblem), ctypes.POINTER(ctypes.c_int), i32,
+                                i64, vp]
     L.mq_gemm_workspace_bytes.restype = sz
     L.mq_gemm_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.mq_gemm.restype = i32
@@ -177,35 +181,46 @@ def gemv(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, s
     return out
 
 
-def gemv_grouped(problems, r: int, M: int, stream=None):
-    """problems: list of dicts with packed, alpha, zero, x, y (tensors), N, K, group."""
+def _problem_array(problems):
     arr = (GemvProblem * len(problems))()
     for i, p in enumerate(problems):
         arr[i] = GemvProblem(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
                              _bits16(p["x"]).data_ptr(), p["y"].data_ptr(), p["N"], p["K"],
                              p["group"])
-    _check(lib().mq_gemv_grouped(arr, len(problems), r, M, _stream(stream)), "mq_gemv_grouped")
+    return arr
+
+
+def gemv_grouped(problems, r, M: int, stream=None):
+    """problems: list of dicts with packed, alpha, zero, x, y (tensors), N, K, group.
+    r: one precision for all (mq_gemv_grouped) or a list, one per problem
+    (mq_gemv_mixed)."""
+    GemvGroupedPlan(problems, r, M, stream)()
 
 
 class GemvGroupedPlan:
-    """A prepared mq_gemv_grouped call: the problem array is marshalled once,
-    each call is a single C call (for launch-rate-bound decode loops).  The
-    caller keeps every tensor alive while the plan is in use."""
+    """A prepared mq_gemv_grouped / mq_gemv_mixed call: the problem array is
+    marshalled once, each call is a single C call (for launch-rate-bound
+    decode loops).  r is an int (same for all) or a list (one per problem).
+    The caller keeps every tensor alive while the plan is in use."""
 
-    def __init__(self, problems, r: int, M: int, stream=None):
-        self.arr = (GemvProblem * len(problems))()
-        for i, p in enumerate(problems):
-            self.arr[i] = GemvProblem(p["packed"].data_ptr(), p["alpha"].data_ptr(),
-                                      p["zero"].data_ptr(), _bits16(p["x"]).data_ptr(),
-                                      p["y"].data_ptr(), p["N"], p["K"], p["group"])
-        self.count, self.r, self.M = len(problems), r, M
+    def __init__(self, problems, r, M: int, stream=None):
+        self.arr = _problem_array(problems)
+        self.count, self.M = len(problems), M
         self.stream = _stream(stream)
-        self.fn = lib().mq_gemv_grouped
+        if isinstance(r, (list, tuple)):
+            if len(r) != len(problems):
+                raise ValueError("one r per problem")
+            self.rs = (ctypes.c_int * len(r))(*r)
+            self.fn, self.name = lib().mq_gemv_mixed, "mq_gemv_mixed"
+            self.args = (self.arr, self.rs, self.count, self.M, self.stream)
+        else:
+            self.fn, self.name = lib().mq_gemv_grouped, "mq_gemv_grouped"
+            self.args = (self.arr, self.count, int(r), self.M, self.stream)
 
     def __call__(self):
-        st = self.fn(self.arr, self.count, self.r, self.M, self.stream)
+        st = self.fn(*self.args)
         if st != MQ_OK:
-            raise MQError(st, "mq_gemv_grouped")
+            raise MQError(st, self.name)
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:

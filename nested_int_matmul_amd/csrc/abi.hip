@@ -61,9 +61,40 @@ mq_status check_product(const uint8_t* packed, int r, const float* alpha, const 
   return MQ_OK;
 }
 
-mq_status skinny_run(mq::SkinnyArgs& a, int r, bool grouped, hipStream_t stream) {
-  hipError_t e = mq::launch_skinny(a, r, grouped, stream);
+mq_status skinny_run(mq::SkinnyArgs& a, bool grouped, hipStream_t stream) {
+  hipError_t e = mq::launch_skinny(a, grouped, stream);
   return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+// Validate every problem, then one launch per scale granularity present.
+mq_status gemv_products(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
+                        hipStream_t stream) {
+  if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
+  int n_grouped = 0;
+  for (int i = 0; i < count; ++i) {
+    const mq_gemv_problem& p = problems[i];
+    mq_status s = check_product(p.packed, r[i], p.alpha, p.zero, p.group, p.N, p.K, p.x, p.y);
+    if (s != MQ_OK) return s;
+    n_grouped += (p.group != p.K) ? 1 : 0;
+  }
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool grouped = pass == 1;
+    if (grouped ? n_grouped == 0 : n_grouped == count) continue;
+    mq::SkinnyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.M = (int)M;
+    for (int i = 0; i < count; ++i) {
+      const mq_gemv_problem& p = problems[i];
+      if ((p.group != p.K) != grouped) continue;
+      a.p[a.count++] = mq::SkinnyProblem{p.packed, p.alpha, p.zero, p.x, nullptr, p.y, (int)p.N,
+                                         (int)p.K, (int)p.group, mq::kXBf16, r[i], 0, 0, 0, 0};
+    }
+    s = skinny_run(a, grouped, stream);
+    if (s != MQ_OK) return s;
+  }
+  return MQ_OK;
 }
 
 }  // namespace
@@ -133,41 +164,24 @@ mq_status mq_gemv(const uint8_t* packed, int r, const float* alpha, const float*
   a.count = 1;
   a.M = (int)M;
   a.p[0] = mq::SkinnyProblem{packed, alpha, zero, x, nullptr, y, (int)N, (int)K, (int)group,
-                             mq::kXBf16, 0, 0, 0, 0};
-  return skinny_run(a, r, group != K, (hipStream_t)stream);
+                             mq::kXBf16, r, 0, 0, 0, 0};
+  return skinny_run(a, group != K, (hipStream_t)stream);
 }
 
 mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int64_t M,
                           void* stream) {
   if (!problems) return MQ_ERR_NULL;
   if (count < 1 || count > mq::kMaxProblems) return MQ_ERR_SHAPE;
-  if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
-  int n_grouped = 0;
-  for (int i = 0; i < count; ++i) {
-    const mq_gemv_problem& p = problems[i];
-    mq_status s = check_product(p.packed, r, p.alpha, p.zero, p.group, p.N, p.K, p.x, p.y);
-    if (s != MQ_OK) return s;
-    n_grouped += (p.group != p.K) ? 1 : 0;
-  }
-  mq_status s = check_device();
-  if (s != MQ_OK) return s;
-  // One launch per scale granularity present.
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool grouped = pass == 1;
-    if (grouped ? n_grouped == 0 : n_grouped == count) continue;
-    mq::SkinnyArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.M = (int)M;
-    for (int i = 0; i < count; ++i) {
-      const mq_gemv_problem& p = problems[i];
-      if ((p.group != p.K) != grouped) continue;
-      a.p[a.count++] = mq::SkinnyProblem{p.packed, p.alpha, p.zero, p.x, nullptr, p.y, (int)p.N,
-                                         (int)p.K, (int)p.group, mq::kXBf16, 0, 0, 0, 0};
-    }
-    s = skinny_run(a, r, grouped, (hipStream_t)stream);
-    if (s != MQ_OK) return s;
-  }
-  return MQ_OK;
+  int rs[mq::kMaxProblems];
+  for (int i = 0; i < count; ++i) rs[i] = r;
+  return gemv_products(problems, rs, count, M, (hipStream_t)stream);
+}
+
+mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
+                        void* stream) {
+  if (!problems || !r) return MQ_ERR_NULL;
+  if (count < 1 || count > mq::kMaxProblems) return MQ_ERR_SHAPE;
+  return gemv_products(problems, r, count, M, (hipStream_t)stream);
 }
 
 size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
@@ -243,7 +257,7 @@ void stack_offsets(const StackDims& d, int64_t M, size_t* off, size_t* total) {
 }
 
 // Run the problems of one launch, split by scale granularity.
-mq_status run_mixed(mq::SkinnyProblem* probs, int count, int r, int64_t M, hipStream_t s) {
+mq_status run_mixed(mq::SkinnyProblem* probs, int count, int64_t M, hipStream_t s) {
   for (int pass = 0; pass < 2; ++pass) {
     const bool grouped = pass == 1;
     mq::SkinnyArgs a;
@@ -252,15 +266,16 @@ mq_status run_mixed(mq::SkinnyProblem* probs, int count, int r, int64_t M, hipSt
     for (int i = 0; i < count; ++i)
       if ((probs[i].group != probs[i].K) == grouped) a.p[a.count++] = probs[i];
     if (a.count == 0) continue;
-    mq_status st = skinny_run(a, r, grouped, s);
+    mq_status st = skinny_run(a, grouped, s);
     if (st != MQ_OK) return st;
   }
   return MQ_OK;
 }
 
-mq::SkinnyProblem prob(const mq_linear& l, const void* x0, const void* x1, int xmode, float* y) {
+mq::SkinnyProblem prob(const mq_linear& l, int r, const void* x0, const void* x1, int xmode,
+                       float* y) {
   return mq::SkinnyProblem{l.packed, l.alpha, l.zero, x0, x1, y, (int)l.N, (int)l.K,
-                           (int)l.group, xmode, 0, 0, 0, 0};
+                           (int)l.group, xmode, r, 0, 0, 0, 0};
 }
 
 }  // namespace
@@ -312,16 +327,16 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, i
   if (e != hipSuccess) return hip_fail(e);
   for (int i = 0; i < n_layers; ++i) {
     const mq_layer& L = layers[i];
-    mq::SkinnyProblem p1[5] = {prob(L.q, a, nullptr, mq::kXBf16, q),
-                               prob(L.k, a, nullptr, mq::kXBf16, k),
-                               prob(L.v, a, nullptr, mq::kXBf16, v),
-                               prob(L.up, a, nullptr, mq::kXBf16, u),
-                               prob(L.gate, a, nullptr, mq::kXBf16, g)};
-    s = run_mixed(p1, 5, L.r, M, st);
+    mq::SkinnyProblem p1[5] = {prob(L.q, L.r, a, nullptr, mq::kXBf16, q),
+                               prob(L.k, L.r, a, nullptr, mq::kXBf16, k),
+                               prob(L.v, L.r, a, nullptr, mq::kXBf16, v),
+                               prob(L.up, L.r, a, nullptr, mq::kXBf16, u),
+                               prob(L.gate, L.r, a, nullptr, mq::kXBf16, g)};
+    s = run_mixed(p1, 5, M, st);
     if (s != MQ_OK) return s;
-    mq::SkinnyProblem p2[2] = {prob(L.o, q, nullptr, mq::kXF32, o),
-                               prob(L.down, u, g, mq::kXF32Prod, dd)};
-    s = run_mixed(p2, 2, L.r, M, st);
+    mq::SkinnyProblem p2[2] = {prob(L.o, L.r, q, nullptr, mq::kXF32, o),
+                               prob(L.down, L.r, u, g, mq::kXF32Prod, dd)};
+    s = run_mixed(p2, 2, M, st);
     if (s != MQ_OK) return s;
     // the last layer leaves its own input a in the workspace
     e = mq::launch_residual_rmsnorm(h, o, dd, i + 1 < n_layers ? a : nullptr, M, d.H, st);

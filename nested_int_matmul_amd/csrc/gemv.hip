@@ -102,17 +102,12 @@ struct LoadT<8> {
   }
 };
 
+// One workgroup's share of problem pi, at slice precision R.
 template <int R, bool GROUPED>
-__global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyArgs args) {
+__device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi) {
   using C = Sk<R, GROUPED>;
   using LD = LoadT<C::V>;
   extern __shared__ __align__(16) unsigned char smem[];
-
-  // ---- locate this workgroup's problem and row blocks
-  int pi = 0;
-#pragma unroll 1
-  for (int i = 1; i < args.count; ++i)
-    if ((int)blockIdx.x >= args.p[i].tile0) pi = i;
   const SkinnyProblem& P = args.p[pi];
   const int M = args.M;
   const int K = P.K, N = P.N;
@@ -371,6 +366,20 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyA
   }
 }
 
+// The problems of a launch may differ in r (one launch can serve several
+// precisions of one stored model); each workgroup runs its problem's body.
+template <bool GROUPED>
+__global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyArgs args) {
+  int pi = 0;
+#pragma unroll 1
+  for (int i = 1; i < args.count; ++i)
+    if ((int)blockIdx.x >= args.p[i].tile0) pi = i;
+  const int r = args.p[pi].r;
+  if (r == 8) skinny_body<8, GROUPED>(args, pi);
+  else if (r == 4) skinny_body<4, GROUPED>(args, pi);
+  else skinny_body<2, GROUPED>(args, pi);
+}
+
 // ---------------------------------------------------------------------------
 // Host planning
 // ---------------------------------------------------------------------------
@@ -379,24 +388,23 @@ static int step_codes(int r, bool grouped) {
   return 4 * V * 8 / r;
 }
 
-template <int R, bool GROUPED>
+template <bool GROUPED>
 static hipError_t launch_t(const SkinnyArgs& a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)skinny_kernel<R, GROUPED>,
+    hipError_t e = hipFuncSetAttribute((const void*)skinny_kernel<GROUPED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   int tiles = a.p[a.count - 1].tile0 + a.p[a.count - 1].tiles;
-  hipLaunchKernelGGL((skinny_kernel<R, GROUPED>), dim3(tiles), dim3(64 * kSkinnyWaves), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<GROUPED>), dim3(tiles), dim3(64 * kSkinnyWaves), lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_skinny(SkinnyArgs& args, int r, bool grouped, hipStream_t stream) {
+hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
   const int waves = kSkinnyWaves;
   const int M = args.M;
-  const int step = step_codes(r, grouped);
   // activation chunk: at most 64 KiB of staged bf16, a multiple of 512 codes
   int kmax = 0;
   for (int i = 0; i < args.count; ++i) kmax = args.p[i].K > kmax ? args.p[i].K : kmax;
@@ -408,6 +416,7 @@ hipError_t launch_skinny(SkinnyArgs& args, int r, bool grouped, hipStream_t stre
   int steps_per_wave[kMaxProblems];
   for (int i = 0; i < args.count; ++i) {
     SkinnyProblem& p = args.p[i];
+    const int step = step_codes(p.r, grouped);
     const int kpad = ((p.K + 511) / 512) * 512;
     const int steps = kpad / step;
     const int spg = grouped ? 128 / step : 1;
@@ -438,14 +447,7 @@ hipError_t launch_skinny(SkinnyArgs& args, int r, bool grouped, hipStream_t stre
   const int gpc = kc / 128;
   const size_t lds = (size_t)M * (kc + kXPad) * 2 +
                      (size_t)(2 * M * gpc + 2 * kSkinnyMaxM) * 4 + (size_t)waves * 16 * M * 4;
-  switch (r * 2 + (grouped ? 1 : 0)) {
-    case 4: return launch_t<2, false>(args, lds, stream);
-    case 5: return launch_t<2, true>(args, lds, stream);
-    case 8: return launch_t<4, false>(args, lds, stream);
-    case 9: return launch_t<4, true>(args, lds, stream);
-    case 16: return launch_t<8, false>(args, lds, stream);
-    default: return launch_t<8, true>(args, lds, stream);
-  }
+  return grouped ? launch_t<true>(args, lds, stream) : launch_t<false>(args, lds, stream);
 }
 
 }  // namespace mq

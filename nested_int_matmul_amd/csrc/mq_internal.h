@@ -13,7 +13,7 @@ enum XMode : int {
   kXF32Prod = 2,  // x0 * x1 (fp32 product), rounded to bf16 on load
 };
 
-constexpr int kMaxProblems = 8;
+constexpr int kMaxProblems = 16;
 constexpr int kSkinnyMaxM = 8;
 
 struct SkinnyProblem {
@@ -24,6 +24,7 @@ struct SkinnyProblem {
   const void* x1;
   float* y;
   int N, K, group, xmode;
+  int r;         // slice precision of this problem (2, 4 or 8)
   int ks;        // waves sharing one 16-row block (split of K)
   int rbpw;      // 16-row blocks per workgroup (rbpw * ks == waves per workgroup)
   int tiles;     // workgroups of this problem
@@ -38,8 +39,9 @@ struct SkinnyArgs {
 };
 
 // Host-side planning + launch of the skinny (M <= 8) kernel.  `probs` hold the
-// pointers and shapes; tiling fields are filled in here.
-hipError_t launch_skinny(SkinnyArgs& args, int r, bool grouped, hipStream_t stream);
+// pointers, shapes and r; tiling fields are filled in here.  All problems of
+// one launch share the scale granularity (grouped or per-channel).
+hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream);
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* codes,
                            float* alpha, float* zero, hipStream_t stream);

@@ -83,7 +83,12 @@ def test_gemm_and_grouped_validation(L):
     probs = (mq.GemvProblem * 2)()
     assert L.mq_gemv_grouped(probs, 2, 4, 1, NULL) == 1
     assert L.mq_gemv_grouped(probs, 0, 4, 1, NULL) == 2
-    assert L.mq_gemv_grouped(probs, 9, 4, 1, NULL) == 2
+    assert L.mq_gemv_grouped(probs, 17, 4, 1, NULL) == 2
+    rs = (ctypes.c_int * 2)(4, 2)
+    assert L.mq_gemv_mixed(probs, rs, 2, 1, NULL) == 1
+    assert L.mq_gemv_mixed(probs, None, 2, 1, NULL) == 1
+    assert L.mq_gemv_mixed(probs, rs, 0, 1, NULL) == 2
+    assert L.mq_gemv_mixed(probs, rs, 17, 1, NULL) == 2
 
 
 def test_mixnmatch_validation(L):

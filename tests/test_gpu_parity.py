@@ -134,6 +134,56 @@ def test_gemv_gemma_mlp_full_size(r):
         compare(m["y"][:, rows], ref, f"gemma mat{i} r{r}")
 
 
+def test_gemv_mixed_precisions_one_launch():
+    """mq_gemv_mixed: the three Gemma MLP matrices at r = 8, 4 and 2 (nine
+    products) in one launch, as the benchmark runs them; sampled rows of
+    every product against the oracle at its own r."""
+    note("gemma mlp mixed r=8,4,2 one launch")
+    mats, probs, rs = [], [], []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        m = dict(quantized("gemma9b_mlp", n, k, k, matrix=i, outlier_frac=1e-3))
+        m["xb"] = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        mats.append(m)
+    outs = []
+    for r in (8, 4, 2):
+        for i, m in enumerate(mats):
+            y = torch.empty((1, m["N"]), dtype=torch.float32, device=dev())
+            probs.append({"packed": mq.pack(m["q_d"], r), "alpha": m["alpha_d"],
+                          "zero": m["zero_d"], "x": x_device(m["xb"]), "y": y, "N": m["N"],
+                          "K": m["K"], "group": m["K"]})
+            rs.append(r)
+            outs.append((i, r, y))
+    mq.gemv_grouped(probs, rs, 1)
+    torch.cuda.synchronize()
+    for i, r, y in outs:
+        m = mats[i]
+        rows = _sample_rows(m["N"], 128, seed=10 * i + r)
+        ref = oracle.linear(m["xb"], m["q"][rows], m["alpha"][rows], m["zero"][rows], m["K"], r)
+        compare(y[:, rows], ref, f"mixed mat{i} r{r}")
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_gemv_mixed_granularities(M):
+    """Per-channel and group-128 problems at different r in one call."""
+    note(f"gemv mixed granularities M={M}")
+    cases = [(200, 768, "K", 2), (136, 1024, 128, 8), (72, 512, 128, 4), (300, 640, "K", 4)]
+    probs, rs, refs = [], [], []
+    for j, (n, k, g, r) in enumerate(cases):
+        gg = k if g == "K" else 128
+        m = quantized("tiny_linear", n, k, gg, matrix=20 + j)
+        xb = inputs.activations_bf16("tiny_linear", M, k, matrix=20 + j)
+        y = torch.empty((M, n), dtype=torch.float32, device=dev())
+        probs.append({"packed": mq.pack(m["q_d"], r), "alpha": m["alpha_d"], "zero": m["zero_d"],
+                      "x": x_device(xb), "y": y, "N": n, "K": k, "group": gg})
+        rs.append(r)
+        refs.append((y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], gg, r), f"case{j} r{r}"))
+    mq.gemv_grouped(probs, rs, M)
+    torch.cuda.synchronize()
+    for y, ref, what in refs:
+        compare(y, ref, what)
+
+
 def test_gemv_deterministic():
     note("gemv determinism")
     m = quantized("tiny_linear", 512, 4096, 4096, matrix=3)
