@@ -29,7 +29,6 @@ namespace mq {
 
 namespace panel {
 
-constexpr int kMaxWaves = 8;
 constexpr int kKSliceMax = 1024;  // codes of K per workgroup (activations resident in LDS)
 constexpr int kXPadE = 8;         // bf16 padding per staged activation row
 constexpr int DEPTH = 8;          // weight loads in flight per lane
@@ -297,11 +296,10 @@ static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
   PanelPlan p;
   p.nw = 8;
   p.panels = (int)((N + 32 * p.nw - 1) / (32 * p.nw));
-  // K slice: the largest multiple of 512 (at most 1024) that still gives at
-  // least ~1.5 workgroups per compute unit
+  // K slice: the largest the activations allow in LDS (1024 codes): longer
+  // workgroups and fewer partial slices measured faster than more, shorter
+  // ones at the Mistral shapes (M = 16 and 64)
   p.kslice = panel::kKSliceMax;
-  while (p.kslice > 512 && (int64_t)p.panels * ((K + p.kslice - 1) / p.kslice) < 384)
-    p.kslice -= 512;
   p.slices = (int)((K + p.kslice - 1) / p.kslice);
   return p;
 }
