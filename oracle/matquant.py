@@ -143,6 +143,13 @@ def slice_value_noclamp(q, r: int) -> np.ndarray:
 # Storage of a sliced plane (the pages fix values only; this is the layout)
 # --------------------------------------------------------------------------
 
+# r = 3 and r = 6 ("interpolative" precisions between the nested 2/4/8, served
+# from the same codes: [MQX] "Mix'n'Match and Interpolative Slicing") are not
+# byte-aligned.  Their index t is stored as two planes of the word layout
+# below: the high bits t >> r_lo, then the low bits t & (2^r_lo - 1).
+SPLIT_WIDTHS = {3: (2, 1), 6: (4, 2)}  # r -> (r_hi, r_lo)
+
+
 def pack_indices(t, r: int) -> np.ndarray:
     """Pack r-bit indices t [N, K] into bytes [N, K*r/8].
 
@@ -152,9 +159,24 @@ def pack_indices(t, r: int) -> np.ndarray:
     the elements at odd positions 1, 3, 5, ... fill the high 16 bits; in each
     half, the j-th of them occupies bits [j*r, j*r + r) of that half.  Words
     are stored little-endian.  K must be a multiple of 32/r.
+
+    LAYOUT for r = 3 and r = 6 (also a reading): the N*K*r/8 bytes are two
+    planes back to back, first the r_hi-bit plane of t >> r_lo for all rows,
+    then the r_lo-bit plane of t & (2^r_lo - 1) for all rows (each as above;
+    (r_hi, r_lo) = (2, 1) for r = 3 and (4, 2) for r = 6).  The result is that
+    byte sequence viewed as [N, K*r/8]; its rows are not the weight rows.
     """
+    if r in SPLIT_WIDTHS:
+        t = np.asarray(t, dtype=np.int64)
+        n, k = t.shape
+        if t.min(initial=0) < 0 or t.max(initial=0) >= 2 ** r:
+            raise ValueError("index out of range for r bits")
+        r_hi, r_lo = SPLIT_WIDTHS[r]
+        hi = pack_indices(t >> r_lo, r_hi)
+        lo = pack_indices(t & ((1 << r_lo) - 1), r_lo)
+        return np.concatenate([hi.reshape(-1), lo.reshape(-1)]).reshape(n, k * r // 8)
     if r not in (1, 2, 4, 8):
-        raise ValueError("byte-aligned packing needs r in {1,2,4,8}")
+        raise ValueError("packing needs r in {1,2,3,4,6,8}")
     t = np.asarray(t, dtype=np.int64)
     n, k = t.shape
     per_word = 32 // r
@@ -176,8 +198,19 @@ def pack_indices(t, r: int) -> np.ndarray:
 
 def unpack_indices(packed, r: int, k: int) -> np.ndarray:
     """Inverse of pack_indices: bytes [N, K*r/8] -> indices int64 [N, K]."""
+    if r in SPLIT_WIDTHS:
+        p = np.asarray(packed, dtype=np.int64)
+        n = p.shape[0]
+        if p.shape[1] * 8 != k * r:
+            raise ValueError("packed width does not match K")
+        r_hi, r_lo = SPLIT_WIDTHS[r]
+        flat = p.reshape(-1)
+        cut = n * k * r_hi // 8
+        hi = unpack_indices(flat[:cut].reshape(n, k * r_hi // 8), r_hi, k)
+        lo = unpack_indices(flat[cut:].reshape(n, k * r_lo // 8), r_lo, k)
+        return (hi << r_lo) | lo
     if r not in (1, 2, 4, 8):
-        raise ValueError("byte-aligned packing needs r in {1,2,4,8}")
+        raise ValueError("packing needs r in {1,2,3,4,6,8}")
     p = np.asarray(packed, dtype=np.int64)
     n = p.shape[0]
     per_word = 32 // r

@@ -212,6 +212,46 @@ def test_hand_packed_words():
         assert oracle.unpack_indices(oracle.pack_indices(t, r), r, t.shape[1]).tolist() == t.tolist()
 
 
+def test_hand_packed_split_planes():
+    for line in open(os.path.join(GOLDEN, "pack_layout_split.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, right = line.split(";")
+        vals = [int(v) for v in left.split()]
+        r, n, k = vals[:3]
+        t = np.array(vals[3:]).reshape(n, k)
+        got = oracle.pack_indices(t, r)
+        assert got.shape == (n, k * r // 8)
+        assert got.reshape(-1).tolist() == [int(b, 16) for b in right.split()]
+        assert oracle.unpack_indices(got, r, k).tolist() == t.tolist()
+
+
+@pytest.mark.parametrize("r", [3, 6])
+def test_split_planes_roundtrip_and_sizes(r):
+    rg = np.random.default_rng(40 + r)
+    t = rg.integers(0, 2 ** r, size=(5, 128))
+    p = oracle.pack_indices(t, r)
+    assert p.shape == (5, 128 * r // 8)
+    assert np.array_equal(oracle.unpack_indices(p, r, 128), t)
+    with pytest.raises(ValueError):
+        oracle.pack_indices(np.full((1, 64), 2 ** r), r)
+
+
+def test_interpolated_precisions_sit_between_their_neighbours():
+    # r = 3 and r = 6 are plain Eq. 6 slices: multiples of 2^(8-r) in range,
+    # idempotent, and containing the value sets of the coarser slices
+    for r in (3, 6):
+        s = oracle.slice_value(ALL_CODES, r)
+        assert np.all(s % 2 ** (8 - r) == 0) and s.min() == 0
+        assert s.max() == (2 ** r - 1) * 2 ** (8 - r)
+        assert np.array_equal(oracle.slice_value(s, r), s)
+    assert set(oracle.slice_value(ALL_CODES, 2)) <= set(oracle.slice_value(ALL_CODES, 3))
+    assert set(oracle.slice_value(ALL_CODES, 3)) <= set(oracle.slice_value(ALL_CODES, 6))
+    # ties round up (the rule in words): q = 16 -> 32 at r = 3, q = 2 -> 4 at r = 6
+    assert oracle.slice_value(np.array([16, 15, 2, 1]), 3).tolist() == [32, 0, 0, 0]
+    assert oracle.slice_value(np.array([2, 1, 6, 5]), 6).tolist() == [4, 0, 8, 4]
+
+
 @pytest.mark.parametrize("r", [1, 2, 4, 8])
 def test_pack_bit_layout_and_roundtrip(r):
     rg = np.random.default_rng(r)
@@ -273,7 +313,7 @@ def _exact_linear(x_bits, q, a, z, group, r):
     return out
 
 
-@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
 @pytest.mark.parametrize("group", [4, 8])
 def test_linear_exact_rationals(r, group):
     rg = np.random.default_rng(100 + r + group)
