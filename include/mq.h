@@ -47,7 +47,7 @@ typedef enum mq_status {
   MQ_OK = 0,
   MQ_ERR_NULL = 1,      /* a required pointer is NULL                          */
   MQ_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)       */
-  MQ_ERR_PRECISION = 3, /* r is not 2, 4 or 8                                  */
+  MQ_ERR_PRECISION = 3, /* r is not 2, 3, 4, 6 or 8 (or not served at that M) */
   MQ_ERR_GROUP = 4,     /* group is neither K nor 128                          */
   MQ_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                    */
   MQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than required          */
@@ -66,7 +66,7 @@ int mq_last_hip_error(void);
 const char* mq_version(void);
 
 /* Bytes of one packed r-bit plane of an [N, K] matrix: N * K * r / 8.
- * Returns 0 for r not in {2, 4, 8} or negative sizes. */
+ * Returns 0 for r not in {2, 3, 4, 6, 8} or negative sizes. */
 size_t mq_packed_bytes(int64_t N, int64_t K, int r);
 
 /*
@@ -88,13 +88,21 @@ mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group,
 /*
  * mq_pack: slice stored codes to r bits and pack them (Eq. 6; the explainer's
  * §2 and "The Bit-Slicing Operator": a lower-precision model is extracted from
- * the one stored int8 model by slicing).  Writes, for every code,
+ * the one stored int8 model by slicing; r = 3 and 6 are the interpolated
+ * precisions of "Mix'n'Match and Interpolative Slicing").  Writes, for every
+ * code,
  *   t = min((q + 2^(7-r)) >> (8-r), 2^r - 1)   (r < 8),   t = q   (r = 8),
- * the index with S(q, r) = t * 2^(8-r), packed 8/r per byte: byte j of a row
- * holds elements j*8/r + i in bits [i*r, i*r + r) (little-endian fields).
+ * the index with S(q, r) = t * 2^(8-r).
+ * Layout (r = 2, 4, 8): each row is cut into little-endian 32-bit words of
+ * 32/r consecutive indices; the indices at even positions fill the low 16
+ * bits, those at odd positions the high 16 bits, the j-th of a half in bits
+ * [j*r, j*r + r) of that half.
+ * Layout (r = 3, 6): two planes back to back, each in the layout above: first
+ * t >> r_lo for all rows (width r - r_lo), then t & (2^r_lo - 1) for all rows
+ * (width r_lo = 1 for r = 3, 2 for r = 6).
  *   codes   uint8 [N, K]
- *   packed  uint8 [N, K*r/8] (output), 16-byte aligned
- * Sizes: N >= 1, K >= 64, K % 64 == 0; r in {2, 4, 8}.
+ *   packed  uint8, N*K*r/8 bytes (output), 16-byte aligned
+ * Sizes: N >= 1, K >= 64, K % 64 == 0; r in {2, 3, 4, 6, 8}.
  */
 mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
                   void* stream);
@@ -110,7 +118,8 @@ mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* pa
  *   alpha, zero  fp32 [N, K/group]
  *   x       bf16 bits [M, K], 16-byte aligned
  *   y       fp32 [M, N] (output), 16-byte aligned
- * Sizes: 1 <= M <= 8, N >= 1, K >= 64, K % 64 == 0, K <= 65536.
+ * Sizes: 1 <= M <= 8, N >= 1, K >= 64, K % 64 == 0, K <= 65536;
+ * r in {2, 3, 4, 6, 8}.
  */
 mq_status mq_gemv(const uint8_t* packed, int r, const float* alpha, const float* zero,
                   int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
@@ -138,7 +147,7 @@ mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int
 
 /*
  * mq_gemv_mixed: as mq_gemv_grouped, but problem i is sliced to its own
- * precision r[i] (2, 4 or 8): several precisions of one stored int8 model
+ * precision r[i] (2, 3, 4, 6 or 8): several precisions of one stored int8 model
  * served in one launch ("Matryoshka Quantization" explainer, §3.4
  * "Mix'n'Match and Interpolative Slicing": any r, chosen per consumer, from
  * the same codes).  Each result equals mq_gemv on that problem at r[i].
@@ -153,6 +162,7 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
  * mq_gemm: the same product for any number of activation rows M >= 1 (small
  * batches and prefill), on bf16 matrix cores with fp32 accumulation.  Same
  * definitions and layouts as mq_gemv; M <= 8 takes the mq_gemv kernel.
+ * r = 3 and r = 6 are served for M <= 8 only (MQ_ERR_PRECISION above).
  *   workspace  device scratch of at least mq_gemm_workspace_bytes(M, N, K, group)
  *              bytes (may be NULL when that is 0), 256-byte aligned
  * Sizes: M >= 1, N >= 1, K >= 64, K % 64 == 0, K <= 65536.
@@ -185,7 +195,7 @@ typedef struct mq_linear {
 } mq_linear;
 
 typedef struct mq_layer {
-  int r; /* 2, 4 or 8 */
+  int r; /* 2, 3, 4, 6 or 8 */
   mq_linear q, k, v, o, up, gate, down;
 } mq_layer;
 

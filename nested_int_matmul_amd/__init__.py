@@ -158,7 +158,8 @@ def quantize(w, group: int, stream=None):
 
 
 def pack(codes, r: int, out=None, stream=None):
-    """Slice uint8 codes [N, K] to r bits and pack: uint8 [N, K*r/8]."""
+    """Slice uint8 codes [N, K] to r bits and pack: uint8 [N, K*r/8] (for
+    r = 3 and 6 the two sub-planes are back to back in that byte array)."""
     import torch
 
     n, k = codes.shape

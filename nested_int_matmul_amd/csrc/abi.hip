@@ -36,7 +36,7 @@ mq_status check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_r(int r) { return r == 2 || r == 4 || r == 8; }
+bool valid_r(int r) { return r == 2 || r == 3 || r == 4 || r == 6 || r == 8; }
 
 constexpr int64_t kMaxK = 65536;
 constexpr int64_t kMaxPlaneBytes = (int64_t)1 << 31;
@@ -66,7 +66,25 @@ mq_status skinny_run(mq::SkinnyArgs& a, bool grouped, hipStream_t stream) {
   return e == hipSuccess ? MQ_OK : hip_fail(e);
 }
 
-// Validate every problem, then one launch per scale granularity present.
+// One launch per (scale granularity, precision set) present among the problems.
+mq_status run_mixed(mq::SkinnyProblem* probs, int count, int64_t M, hipStream_t s) {
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool grouped = (pass & 1) != 0, split = (pass & 2) != 0;
+    mq::SkinnyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.M = (int)M;
+    for (int i = 0; i < count; ++i)
+      if ((probs[i].group != probs[i].K) == grouped && mq::split_precision(probs[i].r) == split)
+        a.p[a.count++] = probs[i];
+    if (a.count == 0) continue;
+    mq_status st = skinny_run(a, grouped, s);
+    if (st != MQ_OK) return st;
+  }
+  return MQ_OK;
+}
+
+// Validate every problem, then launch them (one launch per granularity and
+// precision set present).
 mq_status gemv_products(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
                         hipStream_t stream) {
   if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
@@ -79,22 +97,14 @@ mq_status gemv_products(const mq_gemv_problem* problems, const int* r, int count
   }
   mq_status s = check_device();
   if (s != MQ_OK) return s;
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool grouped = pass == 1;
-    if (grouped ? n_grouped == 0 : n_grouped == count) continue;
-    mq::SkinnyArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.M = (int)M;
-    for (int i = 0; i < count; ++i) {
-      const mq_gemv_problem& p = problems[i];
-      if ((p.group != p.K) != grouped) continue;
-      a.p[a.count++] = mq::SkinnyProblem{p.packed, p.alpha, p.zero, p.x, nullptr, p.y, (int)p.N,
-                                         (int)p.K, (int)p.group, mq::kXBf16, r[i], 0, 0, 0, 0};
-    }
-    s = skinny_run(a, grouped, stream);
-    if (s != MQ_OK) return s;
+  mq::SkinnyProblem probs[mq::kMaxProblems];
+  for (int i = 0; i < count; ++i) {
+    const mq_gemv_problem& p = problems[i];
+    probs[i] = mq::SkinnyProblem{p.packed, p.alpha, p.zero, p.x, nullptr, p.y, (int)p.N,
+                                 (int)p.K, (int)p.group, mq::kXBf16, r[i], 0, 0, 0, 0};
   }
-  return MQ_OK;
+  (void)n_grouped;
+  return run_mixed(probs, count, M, stream);
 }
 
 }  // namespace
@@ -194,6 +204,8 @@ mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float*
   mq_status s = check_product(packed, r, alpha, zero, group, N, K, x, y);
   if (s != MQ_OK) return s;
   if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+  // the split precisions have the decode kernel only
+  if (M > mq::kSkinnyMaxM && mq::split_precision(r)) return MQ_ERR_PRECISION;
   const size_t need = mq::gemm_workspace_bytes(M, N, K, group);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MQ_ERR_WORKSPACE;
   s = check_device();
@@ -257,21 +269,6 @@ void stack_offsets(const StackDims& d, int64_t M, size_t* off, size_t* total) {
 }
 
 // Run the problems of one launch, split by scale granularity.
-mq_status run_mixed(mq::SkinnyProblem* probs, int count, int64_t M, hipStream_t s) {
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool grouped = pass == 1;
-    mq::SkinnyArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.M = (int)M;
-    for (int i = 0; i < count; ++i)
-      if ((probs[i].group != probs[i].K) == grouped) a.p[a.count++] = probs[i];
-    if (a.count == 0) continue;
-    mq_status st = skinny_run(a, grouped, s);
-    if (st != MQ_OK) return st;
-  }
-  return MQ_OK;
-}
-
 mq::SkinnyProblem prob(const mq_linear& l, int r, const void* x0, const void* x1, int xmode,
                        float* y) {
   return mq::SkinnyProblem{l.packed, l.alpha, l.zero, x0, x1, y, (int)l.N, (int)l.K,

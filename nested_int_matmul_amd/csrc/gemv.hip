@@ -33,8 +33,13 @@ namespace mq {
 
 template <int R, bool GROUPED>
 struct Sk {
+  // r = 3 and r = 6 planes are split in a high-bit and a low-bit plane
+  static constexpr bool SPLIT = (R == 3 || R == 6);
+  static constexpr int RL = R == 6 ? 2 : 1;               // split: low-plane width
+  static constexpr int RH = R - RL;                       // split: high-plane width
   static constexpr int V = (R == 2 && GROUPED) ? 8 : 16;  // bytes per lane per step
-  static constexpr int CPL = V * 8 / R;                   // codes per lane per step
+  static constexpr int CPL = SPLIT ? 32 : V * 8 / R;      // codes per lane per step
+  static constexpr int HB = CPL * RH / 8, LB = CPL * RL / 8;  // split: bytes per lane per step
   static constexpr int STEP = 4 * CPL;                    // codes per row per step
   static constexpr int MFMAS = CPL / 8;                   // MFMAs per step
   static constexpr int SPG = GROUPED ? 128 / STEP : 1;    // steps per group of 128
@@ -44,16 +49,18 @@ struct Sk {
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
 constexpr int kSkinnyWaves = 4;   // waves per workgroup
-constexpr int kStageBatch = 2;    // fp32 activation loads in flight per thread while staging
 
 template <int R>
-__device__ __forceinline__ bf16x8 unpack_op(const uint32_t* d, int i, const UnpackK& k) {
+__device__ __forceinline__ bf16x8 unpack_op(const uint32_t* d, int i, const UnpackK& k,
+                                            const UnpackK36& k36) {
   if (R == 4) return unpack_r4(d[i], k);
   if (R == 2) return (i & 1) ? unpack_r2m<1>(d[i >> 1], k) : unpack_r2m<0>(d[i >> 1], k);
+  if (R == 6) return unpack_r6(d[i], d[4 + (i >> 1)], i & 1, k36);  // 4 high, 2 low words
+  if (R == 3) return unpack_r3(d[i >> 1], d[2], i, k36);             // 2 high, 1 low word
   return unpack_r8(d[2 * i], d[2 * i + 1]);
 }
 
-
+constexpr int kStageBatch = 2;    // fp32 activation loads in flight per thread while staging
 
 // Load 8 activation values of row m starting at column k (k < K, 8 | K) as
 // four words of bf16 pairs, rounding fp32 sources to bf16 (nearest even).
@@ -79,26 +86,68 @@ __device__ __forceinline__ u32x4 load_x8(const SkinnyProblem& p, int m, int k) {
   return w;
 }
 
-template <int V>
+// Per-step weight loads of a lane: one bounds-checked load (r = 2, 4, 8) or
+// one from each plane of a split (r = 3, 6); `words` flattens them.
+template <int R, int V>
 struct LoadT;
-template <>
-struct LoadT<16> {
+template <int R>
+struct LoadT<R, 16> {
   typedef u32x4 T;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static constexpr int NW = 4;
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t) {
     return buf_load16(r, off);
   }
   __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
     d[0] = t[0]; d[1] = t[1]; d[2] = t[2]; d[3] = t[3];
   }
 };
-template <>
-struct LoadT<8> {
+template <int R>
+struct LoadT<R, 8> {
   typedef u32x2 T;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static constexpr int NW = 2;
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t) {
     return buf_load8(r, off);
   }
   __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
     d[0] = t[0]; d[1] = t[1];
+  }
+};
+struct Split6 {  // 16 high bytes (32 four-bit fields) + 8 low bytes (32 two-bit fields)
+  u32x4 h;
+  u32x2 l;
+};
+struct Split3 {  // 8 high bytes (32 two-bit fields) + 4 low bytes (32 one-bit fields)
+  u32x2 h;
+  uint32_t l;
+};
+template <>
+struct LoadT<6, 0> {
+  typedef Split6 T;
+  static constexpr int NW = 6;
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t oh, uint32_t ol) {
+    T t;
+    t.h = buf_load16(r, oh);
+    t.l = buf_load8(r, ol);
+    return t;
+  }
+  __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
+    d[0] = t.h[0]; d[1] = t.h[1]; d[2] = t.h[2]; d[3] = t.h[3];
+    d[4] = t.l[0]; d[5] = t.l[1];
+  }
+};
+template <>
+struct LoadT<3, 0> {
+  typedef Split3 T;
+  static constexpr int NW = 3;
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t oh, uint32_t ol) {
+    T t;
+    t.h = buf_load8(r, oh);
+    t.l = buf_load4(r, ol);
+    return t;
+  }
+  __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
+    d[0] = t.h[0]; d[1] = t.h[1];
+    d[2] = t.l;
   }
 };
 
@@ -106,7 +155,7 @@ struct LoadT<8> {
 template <int R, bool GROUPED>
 __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi) {
   using C = Sk<R, GROUPED>;
-  using LD = LoadT<C::V>;
+  using LD = LoadT<R, C::SPLIT ? 0 : C::V>;
   extern __shared__ __align__(16) unsigned char smem[];
   const SkinnyProblem& P = args.p[pi];
   const int M = args.M;
@@ -135,7 +184,12 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   const int col = lane & 15, slot = lane >> 4;
   const int n_ld = row0 + col;  // row this lane loads (A operand row)
   // rows past N: point the load past the plane so it returns zeros
-  const uint32_t row_off = (n_ld < N) ? (uint32_t)n_ld * (uint32_t)rowbytes : plane_bytes;
+  // split planes: rows of the high plane, then rows of the low plane
+  const uint32_t hrow = (uint32_t)(K * C::RH / 8), lrow = (uint32_t)(K * C::RL / 8);
+  const uint32_t row_off =
+      (n_ld < N) ? (uint32_t)n_ld * (C::SPLIT ? hrow : (uint32_t)rowbytes) : plane_bytes;
+  const uint32_t row_off_lo =
+      (n_ld < N) ? (uint32_t)N * hrow + (uint32_t)n_ld * lrow : plane_bytes;
 
   // per-channel epilogue operands, fetched now: thread t writes row
   // rr = t % rows_wg of the tile, for m = t / rows_wg, + blockDim / rows_wg, ...
@@ -161,6 +215,8 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     sxot[threadIdx.x] = 0.f;
   }
   const UnpackK uk = UnpackK::make();
+  UnpackK36 uk36;
+  if constexpr (C::SPLIT) uk36 = UnpackK36::make();
   // all lanes read activations: columns past M duplicate column M - 1 (ignored)
   const int xcol = col < M ? col : M - 1;
 
@@ -179,11 +235,18 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       lo = __builtin_amdgcn_readfirstlane((units * ks / KS) * C::SPG);
       hi = __builtin_amdgcn_readfirstlane((units * (ks + 1) / KS) * C::SPG);
     }
-    const uint32_t cbase = row_off + (uint32_t)(ck0 * R / 8 + slot * C::V);
-    // offset of step st for this lane; steps past the range read past the
+    // offsets of step st for this lane; steps past the range read past the
     // plane (bounds check returns zeros), so the loop has no branches
+    const uint32_t cbase =
+        C::SPLIT ? row_off + (uint32_t)((ck0 + slot * C::CPL) * C::RH / 8)
+                 : row_off + (uint32_t)(ck0 * R / 8 + slot * C::V);
+    const uint32_t cbase_lo = row_off_lo + (uint32_t)((ck0 + slot * C::CPL) * C::RL / 8);
     auto loff = [&](int st) -> uint32_t {
-      return st < hi ? cbase + (uint32_t)(st * (C::STEP * R / 8)) : 0x80000000u;
+      return st < hi ? cbase + (uint32_t)(st * (C::STEP * (C::SPLIT ? C::RH : R) / 8))
+                     : 0x80000000u;
+    };
+    auto loff_lo = [&](int st) -> uint32_t {
+      return st < hi ? cbase_lo + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
     };
     typename LD::T buf[C::DEPTH];
     __syncthreads();
@@ -235,7 +298,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     // ---- first DEPTH weight loads of this chunk, issued behind the staging
     //      loads so that waiting for the activations does not wait for them
 #pragma unroll
-    for (int j = 0; j < C::DEPTH; ++j) buf[j] = LD::load(wr, loff(lo + j));
+    for (int j = 0; j < C::DEPTH; ++j) buf[j] = LD::load(wr, loff(lo + j), loff_lo(lo + j));
     __syncthreads();
     {
       const int bpr = clen / PB;
@@ -254,7 +317,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
             s = dot2_bf16(w4[q], ones, s);
             if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q), so);
           }
-          if (R == 4) so = 16.f * s;
+          if (R != 2) so = (float)Enc<R>::kOffset * s;
         }
         // sum over the 16 consecutive blocks of one group of 128
 #pragma unroll
@@ -296,7 +359,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
       for (int j = 0; j < C::DEPTH; ++j) {
         const int st = base + j;
-        uint32_t d[C::V / 4];
+        uint32_t d[LD::NW];
         LD::words(buf[j], d);
         const uint16_t* xp = xrow + st * C::STEP;
         if (st < hi) {
@@ -305,7 +368,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
             for (int i = 0; i < C::MFMAS; ++i) {
               const u32x4 w = *reinterpret_cast<const u32x4*>(xp + 8 * i);
-              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk),
+              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36),
                                                              __builtin_bit_cast(bf16x8, w), part,
                                                              0, 0, 0);
             }
@@ -330,14 +393,14 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
           for (int i = 0; i < C::MFMAS; ++i) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(xp + 8 * i);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk),
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36),
                                                            __builtin_bit_cast(bf16x8, w), part,
                                                            0, 0, 0);
           }
         }
         }
         // refill this slot after its last use, so the buffer stays in place
-        buf[j] = LD::load(wr, loff(st + C::DEPTH));
+        buf[j] = LD::load(wr, loff(st + C::DEPTH), loff_lo(st + C::DEPTH));
       }
     }
   }
@@ -368,37 +431,46 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 
 // The problems of a launch may differ in r (one launch can serve several
 // precisions of one stored model); each workgroup runs its problem's body.
-template <bool GROUPED>
+// The byte-aligned precisions (2, 4, 8) and the split ones (3, 6) are two
+// kernels, so that the registers of one set do not limit the other's occupancy.
+template <bool GROUPED, bool SPLIT>
 __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyArgs args) {
   int pi = 0;
 #pragma unroll 1
   for (int i = 1; i < args.count; ++i)
     if ((int)blockIdx.x >= args.p[i].tile0) pi = i;
   const int r = args.p[pi].r;
-  if (r == 8) skinny_body<8, GROUPED>(args, pi);
-  else if (r == 4) skinny_body<4, GROUPED>(args, pi);
-  else skinny_body<2, GROUPED>(args, pi);
+  if constexpr (SPLIT) {
+    if (r == 6) skinny_body<6, GROUPED>(args, pi);
+    else skinny_body<3, GROUPED>(args, pi);
+  } else {
+    if (r == 8) skinny_body<8, GROUPED>(args, pi);
+    else if (r == 4) skinny_body<4, GROUPED>(args, pi);
+    else skinny_body<2, GROUPED>(args, pi);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Host planning
 // ---------------------------------------------------------------------------
 static int step_codes(int r, bool grouped) {
+  if (r == 3 || r == 6) return Sk<6, false>::STEP;  // 32 codes per lane for both
   const int V = (r == 2 && grouped) ? 8 : 16;
   return 4 * V * 8 / r;
 }
 
-template <bool GROUPED>
+template <bool GROUPED, bool SPLIT>
 static hipError_t launch_t(const SkinnyArgs& a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)skinny_kernel<GROUPED>,
+    hipError_t e = hipFuncSetAttribute((const void*)skinny_kernel<GROUPED, SPLIT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   int tiles = a.p[a.count - 1].tile0 + a.p[a.count - 1].tiles;
-  hipLaunchKernelGGL((skinny_kernel<GROUPED>), dim3(tiles), dim3(64 * kSkinnyWaves), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(tiles), dim3(64 * kSkinnyWaves), lds, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -447,7 +519,10 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
   const int gpc = kc / 128;
   const size_t lds = (size_t)M * (kc + kXPad) * 2 +
                      (size_t)(2 * M * gpc + 2 * kSkinnyMaxM) * 4 + (size_t)waves * 16 * M * 4;
-  return grouped ? launch_t<true>(args, lds, stream) : launch_t<false>(args, lds, stream);
+  const bool split = args.p[0].r == 3 || args.p[0].r == 6;
+  if (split)
+    return grouped ? launch_t<true, true>(args, lds, stream) : launch_t<false, true>(args, lds, stream);
+  return grouped ? launch_t<true, false>(args, lds, stream) : launch_t<false, false>(args, lds, stream);
 }
 
 }  // namespace mq

@@ -54,11 +54,13 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// Offset u - t of the operand encoding, and the zero-point shift it implies.
+// Offset u - t of the operand encoding, and the zero-point shift it implies
+// (u * 2^(8-r) = S + shift).
 template <int R>
 struct Enc {
-  static constexpr float kOffsetShift = (R == 8) ? 0.0f : 256.0f;  // z' = z + shift
-  static constexpr float kStep = (float)(1 << (8 - R));            // 2^(8-r)
+  static constexpr int kOffset = R == 8 ? 0 : (R == 4 ? 16 : (R == 2 ? 4 : 128));
+  static constexpr float kStep = (float)(1 << (8 - R));                 // 2^(8-r)
+  static constexpr float kOffsetShift = (float)kOffset * kStep;         // z' = z + shift
 };
 
 // bf16x2 from a 32-bit word of two bf16 patterns.
@@ -174,6 +176,48 @@ __device__ __forceinline__ bf16x8 unpack_r8(uint32_t w0, uint32_t w1) {
   uint32_t p2 = bf16_pair_of_bytes(w1 & 0xffu, (w1 >> 16) & 0xffu);
   uint32_t p3 = bf16_pair_of_bytes((w1 >> 8) & 0xffu, w1 >> 24);
   return as_bf16x8(p0, p1, p2, p3);
+}
+
+// --- r = 6 and r = 3: the index is stored as two planes (high bits t >> r_lo
+//     in the word layout of width r - r_lo, low bits in that of width r_lo).
+//     The two fields are assembled at bits [0, r) of each half under the bf16
+//     constant 128, whose mantissa unit is 1: u = 128 + t, exact.
+struct UnpackK36 {
+  uint32_t mhi6, mlo6, mhi3, mlo3, one128;
+  __device__ __forceinline__ static UnpackK36 make() {
+    UnpackK36 k{0x003C003Cu, 0x00030003u, 0x00060006u, 0x00010001u, 0x43004300u};
+    asm volatile("" : "+v"(k.mhi6), "+v"(k.mlo6), "+v"(k.mhi3), "+v"(k.mlo3), "+v"(k.one128));
+    return k;
+  }
+};
+
+__device__ __forceinline__ uint32_t shift_signed(uint32_t w, int s) {  // s > 0: right
+  return s >= 0 ? (w >> s) : (w << (-s));
+}
+
+// r = 6, operand i (elements 8i .. 8i+7 of a lane's 32): hi = the 4-bit word
+// of those 8 elements, lo = the 2-bit word of elements 16*(i/2) .. +16.
+__device__ __forceinline__ bf16x8 unpack_r6(uint32_t hi, uint32_t lo, int i_odd,
+                                            const UnpackK36& k) {
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t l = and_or(lo >> (2 * j + 8 * i_odd), k.mlo6, k.one128);
+    p[j] = and_or(shift_signed(hi, 4 * j - 2), k.mhi6, l);
+  }
+  return as_bf16x8(p[0], p[1], p[2], p[3]);
+}
+// r = 3, operand i of a lane's 32 elements: hi = the 2-bit word of elements
+// 16*(i/2) .. +16, lo = the 1-bit word of the lane's 32 elements.
+__device__ __forceinline__ bf16x8 unpack_r3(uint32_t hi, uint32_t lo, int i,
+                                            const UnpackK36& k) {
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t l = and_or(lo >> (4 * i + j), k.mlo3, k.one128);
+    p[j] = and_or(shift_signed(hi, 2 * (4 * (i & 1) + j) - 1), k.mhi3, l);
+  }
+  return as_bf16x8(p[0], p[1], p[2], p[3]);
 }
 
 // fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).

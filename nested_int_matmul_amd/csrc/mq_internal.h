@@ -40,8 +40,10 @@ struct SkinnyArgs {
 
 // Host-side planning + launch of the skinny (M <= 8) kernel.  `probs` hold the
 // pointers, shapes and r; tiling fields are filled in here.  All problems of
-// one launch share the scale granularity (grouped or per-channel).
+// one launch share the scale granularity (grouped or per-channel) and the
+// precision set: {2, 4, 8} or {3, 6} (split planes).
 hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream);
+inline bool split_precision(int r) { return r == 3 || r == 6; }
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* codes,
                            float* alpha, float* zero, hipStream_t stream);

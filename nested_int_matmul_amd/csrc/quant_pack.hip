@@ -118,8 +118,77 @@ __global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ cod
   }
 }
 
+// r = 3 and r = 6: the index t is split into its high bits t >> r_lo (a plane
+// of width r - r_lo) and its low bits (width r_lo = 1 or 2), each packed in
+// the word layout above; the high plane of all rows comes first, then the low
+// plane.  Each thread takes 128 / r_hi consecutive codes: 16 bytes of the high
+// plane and 16 * r_lo / r_hi bytes of the low plane.
+template <int R>
+__global__ void __launch_bounds__(256) pack_split_kernel(const u32x4* __restrict__ codes,
+                                                         uint8_t* __restrict__ out,
+                                                         int64_t n_thr, int64_t lo_base) {
+  constexpr int RL = R == 6 ? 2 : 1, RH = R - RL;
+  constexpr int CODES = 128 / RH;  // codes per thread
+  constexpr int IN16 = CODES / 16;
+  constexpr int LW = CODES * RL / 32;  // low-plane words per thread (2 for both)
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_thr;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    u32x4 in[IN16];
+#pragma unroll
+    for (int j = 0; j < IN16; ++j) in[j] = __builtin_nontemporal_load(codes + i * IN16 + j);
+    auto index_of = [&](int flat) -> uint32_t {
+      const uint32_t word = in[flat / 16][(flat / 4) & 3];
+      return slice_byte<R>((word >> (8 * (flat & 3))) & 0xffu);
+    };
+    uint32_t h[4], l[LW];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t acc = 0;
+      constexpr int PER_WORD = 32 / RH;
+#pragma unroll
+      for (int e = 0; e < PER_WORD; ++e) {
+        const int field = (e & 1) ? 16 + (e >> 1) * RH : (e >> 1) * RH;
+        acc |= (index_of(w * PER_WORD + e) >> RL) << field;
+      }
+      h[w] = acc;
+    }
+#pragma unroll
+    for (int w = 0; w < LW; ++w) {
+      uint32_t acc = 0;
+      constexpr int PER_WORD = 32 / RL;
+#pragma unroll
+      for (int e = 0; e < PER_WORD; ++e) {
+        const int field = (e & 1) ? 16 + (e >> 1) * RL : (e >> 1) * RL;
+        acc |= (index_of(w * PER_WORD + e) & ((1u << RL) - 1u)) << field;
+      }
+      l[w] = acc;
+    }
+    u32x4 hv = {h[0], h[1], h[2], h[3]};
+    u32x2 lv = {l[0], l[1]};
+    *reinterpret_cast<u32x4*>(out + i * 16) = hv;
+    *reinterpret_cast<u32x2*>(out + lo_base + i * (LW * 4)) = lv;
+  }
+}
+
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
                        hipStream_t stream) {
+  if (r == 3 || r == 6) {
+    const int rh = r == 6 ? 4 : 2;
+    const int64_t codes_per_thr = 128 / rh;
+    const int64_t n_thr = N * K / codes_per_thr;
+    int64_t blocks = (n_thr + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (blocks < 1) blocks = 1;
+    const int64_t lo_base = N * K * rh / 8;
+    const u32x4* in = reinterpret_cast<const u32x4*>(codes);
+    if (r == 6)
+      hipLaunchKernelGGL(pack_split_kernel<6>, dim3((unsigned)blocks), dim3(256), 0, stream, in,
+                         packed, n_thr, lo_base);
+    else
+      hipLaunchKernelGGL(pack_split_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, in,
+                         packed, n_thr, lo_base);
+    return hipGetLastError();
+  }
   const int64_t out_bytes = N * K * r / 8;
   const int64_t n16 = out_bytes / 16;
   int64_t blocks = (n16 + 255) / 256;

@@ -41,7 +41,8 @@ def test_status_strings_and_sizes(L):
     assert L.mq_status_string(99).decode() == "unknown mq_status"
     assert L.mq_version().decode().startswith("mq ")
     assert L.mq_packed_bytes(14336, 3584, 2) == 14336 * 3584 // 4
-    assert L.mq_packed_bytes(10, 64, 3) == 0
+    assert L.mq_packed_bytes(10, 64, 3) == 10 * 64 * 3 // 8
+    assert L.mq_packed_bytes(10, 64, 5) == 0
     assert L.mq_gemm_workspace_bytes(2048, 14336, 4096, 128) >= 0
 
 
@@ -52,7 +53,7 @@ P1 = ctypes.c_void_p(0x10001)
 
 def test_pack_validation(L):
     assert L.mq_pack(NULL, 4, 64, 4, P16, NULL) == 1
-    assert L.mq_pack(P16, 4, 64, 3, P16, NULL) == 3
+    assert L.mq_pack(P16, 4, 64, 5, P16, NULL) == 3
     assert L.mq_pack(P16, 4, 65, 4, P16, NULL) == 2
     assert L.mq_pack(P16, 0, 64, 4, P16, NULL) == 2
     assert L.mq_pack(P1, 4, 64, 4, P16, NULL) == 5
@@ -68,7 +69,7 @@ def test_gemv_validation(L):
 
     assert call(p=NULL) == 1
     assert call(y=NULL) == 1
-    assert call(r=3) == 3
+    assert call(r=5) == 3
     assert call(K=96, g=96) == 2
     assert call(g=32) == 4
     assert call(K=192, g=128) == 4

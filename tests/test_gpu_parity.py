@@ -38,7 +38,7 @@ def test_quantize_bit_exact(shape, group, outliers):
     assert np.array_equal(zero.cpu().numpy().view(np.uint32), z.view(np.uint32))
 
 
-@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
 def test_pack_all_codes_bit_exact(r):
     note(f"pack all codes r={r}")
     q = np.tile(np.arange(256, dtype=np.uint8), (7, 4))          # [7, 1024], every code
@@ -51,7 +51,7 @@ def test_pack_all_codes_bit_exact(r):
     assert np.array_equal(t, oracle.slice_index(q, r))
 
 
-@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
 def test_pack_gemma_down_full_size(r):
     note(f"pack gemma down full r={r}")
     m = quantized("gemma9b_mlp", 3584, 14336, 14336, matrix=2, outlier_frac=1e-3)
@@ -62,7 +62,7 @@ def test_pack_gemma_down_full_size(r):
 
 # ---------------------------------------------------------------- GEMV (M <= 8)
 
-@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
 @pytest.mark.parametrize("M", [1, 4])
 def test_gemv_tiny_linear(r, M):
     note(f"gemv tiny r={r} M={M}")
@@ -74,7 +74,7 @@ def test_gemv_tiny_linear(r, M):
     compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 512, r), f"tiny r{r} M{M}")
 
 
-@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
 @pytest.mark.parametrize("group", ["K", 128])
 @pytest.mark.parametrize("M", [1, 3, 8])
 def test_gemv_ragged(r, group, M):
@@ -110,7 +110,7 @@ def _sample_rows(n, count=384, seed=0):
     return rows
 
 
-@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
 def test_gemv_gemma_mlp_full_size(r):
     """Decode GEMV at the Gemma-2-9B MLP shapes, in one grouped launch as the
     benchmark runs it; sampled rows against the oracle."""
@@ -167,7 +167,8 @@ def test_gemv_mixed_precisions_one_launch():
 def test_gemv_mixed_granularities(M):
     """Per-channel and group-128 problems at different r in one call."""
     note(f"gemv mixed granularities M={M}")
-    cases = [(200, 768, "K", 2), (136, 1024, 128, 8), (72, 512, 128, 4), (300, 640, "K", 4)]
+    cases = [(200, 768, "K", 2), (136, 1024, 128, 8), (72, 512, 128, 4), (300, 640, "K", 4),
+             (96, 1024, 128, 6), (160, 576, "K", 3), (64, 1280, 128, 3), (40, 448, "K", 6)]
     probs, rs, refs = [], [], []
     for j, (n, k, g, r) in enumerate(cases):
         gg = k if g == "K" else 128
@@ -182,6 +183,14 @@ def test_gemv_mixed_granularities(M):
     torch.cuda.synchronize()
     for y, ref, what in refs:
         compare(y, ref, what)
+
+
+def test_gemm_split_precision_needs_decode_shape():
+    m = quantized("tiny_linear", 64, 512, 512)
+    plane = mq.pack(m["q_d"], 6)
+    xb = x_device(inputs.activations_bf16("tiny_linear", 9, 512))
+    with pytest.raises(mq.MQError):
+        mq.gemm(plane, 6, m["alpha_d"], m["zero_d"], 512, 64, 512, xb)
 
 
 def test_gemv_deterministic():
@@ -202,7 +211,7 @@ def test_error_enqueues_nothing():
     xb = x_device(inputs.activations_bf16("tiny_linear", 1, 512))
     y = torch.full((1, 64), 7.0, device=dev())
     with pytest.raises(mq.MQError):
-        mq.gemv(plane, 3, m["alpha_d"], m["zero_d"], 512, 64, 512, xb, out=y)
+        mq.gemv(plane, 5, m["alpha_d"], m["zero_d"], 512, 64, 512, xb, out=y)
     with pytest.raises(mq.MQError):
         mq.gemv(plane, 4, m["alpha_d"], m["zero_d"], 100, 64, 512, xb, out=y)
     torch.cuda.synchronize()
@@ -280,11 +289,12 @@ def _bf16_bits_of_f32(t):
     return t.float().to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+@pytest.mark.parametrize("rs", [(8, 4, 2, 4, 8), (6, 3, 8)])
 @pytest.mark.parametrize("group_kind", ["K", 128])
 @pytest.mark.parametrize("M", [1, 2])
-def test_mixnmatch_small_stack(group_kind, M):
-    rs = [8, 4, 2, 4, 8]
-    note(f"mixnmatch small group={group_kind} M={M}")
+def test_mixnmatch_small_stack(group_kind, M, rs):
+    rs = list(rs)
+    note(f"mixnmatch small group={group_kind} M={M} r={rs}")
     host, devl = _small_stack(rs, group_kind=group_kind)
     arr = mq.make_layers(devl)
     H = 256
