@@ -11,12 +11,15 @@ from .matquant import (  # noqa: F401
     bf16_bits_from_float,
     bf16_round,
     dequant,
+    dequant_extra_precision,
     dequant_rows,
     effective_bits,
     float_from_bf16_bits,
     linear,
+    linear_extra_precision,
     mixnmatch_forward,
     mixnmatch_layer,
+    overflow_lists,
     pack_codes,
     pack_indices,
     quantize_minmax,

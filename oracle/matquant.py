@@ -270,6 +270,47 @@ def linear(x_bf16_bits, q, alpha, zero, group: int, r: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Extra-Precision MatQuant: the slice without the clamp (errata Eq. 8)
+# --------------------------------------------------------------------------
+
+def dequant_extra_precision(q, alpha, zero, group: int, r: int) -> np.ndarray:
+    """w_hat = (S'(q, r) - z) * alpha with S' the unclamped slice of the
+    errata Eq. 8 ([MQX] "The Bit-Slicing Operator"): 2^r + 1 levels, the top
+    one 256 ("Extra-Precision MatQuant"; [MQX] §5 "Ablation Studies and
+    Robustness Checks" on the few weights that use it).  Same alpha and z."""
+    q = np.asarray(q)
+    n, k = q.shape
+    g = k // group
+    s = slice_value_noclamp(q, r).astype(np.float64).reshape(n, g, group)
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(n, g, 1)
+    z = np.asarray(zero, dtype=np.float32).astype(np.float64).reshape(n, g, 1)
+    return ((s - z) * a).reshape(n, k)
+
+
+def linear_extra_precision(x_bf16_bits, q, alpha, zero, group: int, r: int) -> np.ndarray:
+    """y = x @ w_hat^T with the extra-precision w_hat, float64."""
+    x = float_from_bf16_bits(x_bf16_bits)
+    if x.ndim == 1:
+        x = x[None, :]
+    return x @ dequant_extra_precision(q, alpha, zero, group, r).T
+
+
+def overflow_lists(q, r: int):
+    """Positions of the codes whose unclamped slice reaches the extra level
+    256 (the only codes where Eq. 8 and Eq. 6 differ), per row in increasing
+    k: (row_ptr int64 [N + 1], col_idx int64 [nnz]).
+
+    READING (storage of the extra bit; the pages note that a custom kernel
+    would have to add it sparsely, [MQX] §5 "Critical Assessment"): the r-bit
+    plane keeps the clamped index and these lists mark where one more level
+    of 2^(8-r) is added."""
+    mask = slice_value_noclamp(q, r) == 2 ** C_BITS
+    row_ptr = np.concatenate([[0], np.cumsum(mask.sum(axis=1))]).astype(np.int64)
+    col_idx = np.nonzero(mask)[1].astype(np.int64)  # row-major: increasing k in a row
+    return row_ptr, col_idx
+
+
+# --------------------------------------------------------------------------
 # Mix'n'Match: a stack of linears, each layer at its own precision r
 # --------------------------------------------------------------------------
 

@@ -40,15 +40,17 @@ def test_ties_follow_the_rule_in_words():
         assert oracle.slice_value(int(q), int(r)) == int(s)
 
 
-def _slice_by_bits(q: int, r: int) -> int:
+def _slice_by_bits(q: int, r: int, clamp: bool = True) -> int:
     """The operator as the pages describe it in words: keep the r most
     significant bits, round up when the first discarded bit is 1, clamp to
-    the r-bit range, shift back."""
+    the r-bit range (not in the errata's unclamped form), shift back."""
     if r == 8:
         return q
     kept = q >> (8 - r)
     first_discarded = (q >> (7 - r)) & 1
-    t = min(kept + first_discarded, 2 ** r - 1)
+    t = kept + first_discarded
+    if clamp:
+        t = min(t, 2 ** r - 1)
     return t << (8 - r)
 
 
@@ -297,7 +299,31 @@ def test_hand_linear():
         assert abs(y[0, 0] - int(num) / int(den)) < 3e-7
 
 
-def _exact_linear(x_bits, q, a, z, group, r):
+def test_hand_linear_extra_precision():
+    h = _hand()
+    w = np.array([[float(v) for v in h["w"][0]]], dtype=np.float32)
+    q, a, z = oracle.quantize_minmax(w, 4)
+    x = oracle.bf16_bits_from_float(np.ones((1, 4)))
+    for r, num, den in h["ye"]:
+        y = oracle.linear_extra_precision(x, q, a, z, 4, int(r))
+        assert abs(y[0, 0] - int(num) / int(den)) < 3e-7
+
+
+@pytest.mark.parametrize("r", [2, 3, 4, 6, 8])
+def test_overflow_lists_are_the_codes_above_the_last_midpoint(r):
+    # the unclamped slice reaches 256 exactly for q >= 256 - 2^(7-r) (r < 8)
+    rg = np.random.default_rng(70 + r)
+    q = rg.integers(0, 256, size=(9, 192))
+    q[2] = 255
+    q[5] = 0
+    row_ptr, col_idx = oracle.overflow_lists(q, r)
+    assert row_ptr[0] == 0 and len(row_ptr) == 10
+    for n in range(9):
+        want = np.nonzero(q[n] >= 256 - 2 ** (7 - r))[0] if r < 8 else np.array([], int)
+        assert col_idx[row_ptr[n]:row_ptr[n + 1]].tolist() == want.tolist()
+
+
+def _exact_linear(x_bits, q, a, z, group, r, clamp=True):
     m, k = x_bits.shape
     n = q.shape[0]
     xs = [[Fraction(float(v)) for v in row] for row in oracle.float_from_bf16_bits(x_bits)]
@@ -307,7 +333,7 @@ def _exact_linear(x_bits, q, a, z, group, r):
             acc = Fraction(0)
             for kk in range(k):
                 g = kk // group
-                s = _slice_by_bits(int(q[j, kk]), r)
+                s = _slice_by_bits(int(q[j, kk]), r, clamp)
                 acc += xs[i][kk] * (s - Fraction(float(z[j, g]))) * Fraction(float(a[j, g]))
             out[i, j] = float(acc)
     return out
@@ -322,6 +348,19 @@ def test_linear_exact_rationals(r, group):
     x = oracle.bf16_bits_from_float(rg.standard_normal((3, 8)))
     got = oracle.linear(x, q, a, z, group, r)
     want = _exact_linear(x, q, a, z, group, r)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("r", [6, 4, 3, 2])
+def test_linear_extra_precision_exact_rationals(r):
+    rg = np.random.default_rng(200 + r)
+    w = (rg.standard_normal((6, 16)) * 0.02).astype(np.float32)
+    w[:, 3] = 0.2  # a column at the top of every row's range: it rounds to the extra level
+    q, a, z = oracle.quantize_minmax(w, 8)
+    assert np.any(oracle.slice_value_noclamp(q, r) == 256)
+    x = oracle.bf16_bits_from_float(rg.standard_normal((2, 16)))
+    got = oracle.linear_extra_precision(x, q, a, z, 8, r)
+    want = _exact_linear(x, q, a, z, 8, r, clamp=False)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-15)
 
 
