@@ -17,7 +17,8 @@ The same JSON line also carries:
                 (single-r launches are timed afterwards for reference);
   rows          the other steps of the path measured in the same run: pack,
                 small-batch GEMM (Mistral shapes, g128), prefill GEMM
-                (M = 2048) and the 32-layer Mix'n'Match stack;
+                (M = 2048), the 32-layer Mix'n'Match stack and the
+                Extra-Precision sparse addition (r = 2, Gemma MLP);
   cpu_baseline  the float64 CPU oracle on the same workload (host cores).
 
 Only one GPU is used; --gpus above 1 exits with a message.
@@ -242,7 +243,38 @@ def run_rows(torch, mq, inputs, dev):
     del c5, a5, z5, x5, y5
     # a5: Mix'n'Match stack, 32 Mistral-7B layers, batch 1
     rows["mixnmatch_mistral7b_32l"] = run_stack(torch, mq, inputs, dev)
+    # f2: Extra-Precision r = 2 on the Gemma MLP: the sparse addition after the plane product
+    rows["extra_precision_gemma_r2"] = run_extra(torch, mq, inputs, dev)
     return rows
+
+
+def run_extra(torch, mq, inputs, dev, r=2):
+    mats = []
+    nnz_total, codes_total = 0, 0
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=i, outlier_frac=1e-3)
+        codes, alpha, zero = mq.quantize(w, k)
+        del w
+        row_ptr, col_idx = mq.overflow_lists(codes, r)
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        x = torch.from_numpy(xb.view("int16")).to(dev)
+        y = torch.zeros((1, n), dtype=torch.float32, device=dev)
+        mats.append((row_ptr, col_idx, alpha, n, k, x, y))
+        nnz_total += col_idx.numel()
+        codes_total += n * k
+        del codes
+    torch.cuda.synchronize()
+
+    def apply_all(i):
+        for row_ptr, col_idx, alpha, n, k, x, y in mats:
+            mq.overflow_apply(row_ptr, col_idx, r, alpha, k, n, k, x, y)
+
+    us = time_loop(torch, apply_all, 50)
+    list_bits = 32.0 * (nnz_total + sum(m[3] + 1 for m in mats))
+    return {"r": r, "apply_us_3_matrices": round(us, 2), "overflow_codes": nnz_total,
+            "overflow_fraction": round(nnz_total / codes_total, 6),
+            "effective_bits": round(r + list_bits / codes_total, 4)}
 
 
 def run_stack(torch, mq, inputs, dev, n_layers=32):

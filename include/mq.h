@@ -173,6 +173,34 @@ mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float*
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Extra-Precision MatQuant: the slice without the clamp (the errata Eq. 8 of
+ * the explainer's "The Bit-Slicing Operator") has 2^r + 1 levels; the extra
+ * one, 256, is reached by the codes q >= 256 - 2^(7-r) (none at r = 8).  The
+ * r-bit plane of mq_pack keeps the clamped index; these calls list the codes
+ * at the extra level per row and add their missing 2^(8-r) * alpha * x to a
+ * product, which gives the extra-precision product ([MQX] §5 "Critical
+ * Assessment": such sparse additions need a kernel of their own).
+ *
+ * mq_overflow_rows: row_ptr int32 [N + 1] (output): row_ptr[0] = 0 and
+ *   row_ptr[n + 1] - row_ptr[n] = number of such codes in row n.
+ * mq_overflow_cols: col_idx int32 [row_ptr[N]] (output): their column k, row
+ *   by row, increasing within a row (row_ptr as written by mq_overflow_rows;
+ *   the caller reads row_ptr[N] to size col_idx).
+ * mq_overflow_apply: y[m, n] += 2^(8-r) * sum over row n's listed k of
+ *   alpha[n, k/group] * x[m, k], summed in a fixed order (deterministic).
+ *   Run after mq_gemv / mq_gemm at the same r on the same y.
+ * codes uint8 [N, K] 16-byte aligned; x bf16 bits [M, K]; y fp32 [M, N].
+ * Sizes: N >= 1, K >= 64, K % 64 == 0, K <= 65536, N * K < 2^31; M >= 1.
+ */
+mq_status mq_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int32_t* row_ptr,
+                           void* stream);
+mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
+                           const int32_t* row_ptr, int32_t* col_idx, void* stream);
+mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int r,
+                            const float* alpha, int64_t group, int64_t N, int64_t K,
+                            const uint16_t* x, int64_t M, float* y, void* stream);
+
+/*
  * Mix'n'Match stack ("Matryoshka Quantization" explainer, §3.4 "Mix'n'Match
  * and Interpolative Slicing"): a stack of layers over one stored int8 model,
  * each layer sliced to its own r.

@@ -31,7 +31,7 @@ EXPORTS = (
     "mq_quantize", "mq_pack", "mq_gemv", "mq_gemv_grouped", "mq_gemv_mixed",
     "mq_gemm_workspace_bytes",
     "mq_gemm", "mq_mixnmatch_workspace_bytes", "mq_mixnmatch_workspace_offsets",
-    "mq_mixnmatch_forward",
+    "mq_mixnmatch_forward", "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
 )
 
 
@@ -91,6 +91,12 @@ def lib() -> ctypes.CDLL:
     L.mq_gemv.argtypes = [vp, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp]
     L.mq_gemv_grouped.restype = i32
     L.mq_gemv_grouped.argtypes = [ctypes.POINTER(GemvProblem), i32, i32, i64, vp]
+    L.mq_overflow_rows.restype = i32
+    L.mq_overflow_rows.argtypes = [vp, i64, i64, i32, vp, vp]
+    L.mq_overflow_cols.restype = i32
+    L.mq_overflow_cols.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    L.mq_overflow_apply.restype = i32
+    L.mq_overflow_apply.argtypes = [vp, vp, i32, vp, i64, i64, i64, vp, i64, vp, vp]
     L.mq_gemv_mixed.restype = i32
     L.mq_gemv_mixed.argtypes = [ctypes.POINTER(GemvProblem), ctypes.POINTER(ctypes.c_int), i32,
                                 i64, vp]
@@ -222,6 +228,33 @@ class GemvGroupedPlan:
         st = self.fn(*self.args)
         if st != MQ_OK:
             raise MQError(st, self.name)
+
+
+def overflow_lists(codes, r: int, stream=None):
+    """Extra-Precision lists of a code matrix at precision r: (row_ptr int32
+    [N + 1], col_idx int32 [nnz]) on the device.  Synchronizes once to size
+    col_idx (a setup step)."""
+    import torch
+
+    n, k = codes.shape
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=codes.device)
+    _check(lib().mq_overflow_rows(_ptr(codes), n, k, r, _ptr(row_ptr), _stream(stream)),
+           "mq_overflow_rows")
+    nnz = int(row_ptr[n].item())
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=codes.device)
+    _check(lib().mq_overflow_cols(_ptr(codes), n, k, r, _ptr(row_ptr), _ptr(col_idx),
+                                  _stream(stream)), "mq_overflow_cols")
+    return row_ptr, col_idx[:nnz]
+
+
+def overflow_apply(row_ptr, col_idx, r: int, alpha, group: int, N: int, K: int, x, y,
+                   stream=None):
+    """y += the extra-precision correction (after a product at the same r)."""
+    x = _bits16(x)
+    ci = col_idx if col_idx.numel() else row_ptr  # any valid pointer when the list is empty
+    _check(lib().mq_overflow_apply(_ptr(row_ptr), _ptr(ci), r, _ptr(alpha), group, N, K, _ptr(x),
+                                   x.shape[0], _ptr(y), _stream(stream)), "mq_overflow_apply")
+    return y
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:

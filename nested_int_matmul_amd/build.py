@@ -20,7 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmq.so")
 
-SOURCES = ["quant_pack.hip", "gemv.hip", "gemm.hip", "gemm_panel.hip", "gemm_big.hip", "mixnmatch.hip", "abi.hip"]
+SOURCES = ["quant_pack.hip", "gemv.hip", "gemm.hip", "gemm_panel.hip", "gemm_big.hip",
+           "mixnmatch.hip", "extra.hip", "abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

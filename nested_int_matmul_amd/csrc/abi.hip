@@ -216,6 +216,53 @@ mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float*
   return e == hipSuccess ? MQ_OK : hip_fail(e);
 }
 
+// ---------------------------------------------------------------- Extra precision
+
+mq_status mq_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int32_t* row_ptr,
+                           void* stream) {
+  if (!codes || !row_ptr) return MQ_ERR_NULL;
+  if (!valid_r(r)) return MQ_ERR_PRECISION;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || N * K >= kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(row_ptr) & 3u)) return MQ_ERR_ALIGN;
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_overflow_rows(codes, N, K, r, row_ptr, (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
+                           const int32_t* row_ptr, int32_t* col_idx, void* stream) {
+  if (!codes || !row_ptr || !col_idx) return MQ_ERR_NULL;
+  if (!valid_r(r)) return MQ_ERR_PRECISION;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || N * K >= kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(row_ptr) & 3u) ||
+      (reinterpret_cast<uintptr_t>(col_idx) & 3u))
+    return MQ_ERR_ALIGN;
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_overflow_cols(codes, N, K, r, row_ptr, col_idx, (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int r,
+                            const float* alpha, int64_t group, int64_t N, int64_t K,
+                            const uint16_t* x, int64_t M, float* y, void* stream) {
+  if (!row_ptr || !col_idx || !alpha || !x || !y) return MQ_ERR_NULL;
+  if (!valid_r(r)) return MQ_ERR_PRECISION;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || N * K >= kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (!(group == K || (group == 128 && K % 128 == 0))) return MQ_ERR_GROUP;
+  if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+      (reinterpret_cast<uintptr_t>(y) & 3u))
+    return MQ_ERR_ALIGN;
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_overflow_apply(row_ptr, col_idx, r, alpha, group, N, K, x, M, y,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
 // ---------------------------------------------------------------- Mix'n'Match
 
 namespace {

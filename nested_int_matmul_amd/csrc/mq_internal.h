@@ -62,6 +62,15 @@ hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const f
                        int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        void* workspace, hipStream_t stream);
 
+// Extra-Precision lists and the sparse addition.
+hipError_t launch_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int* row_ptr,
+                                hipStream_t s);
+hipError_t launch_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
+                                const int* row_ptr, int* col_idx, hipStream_t s);
+hipError_t launch_overflow_apply(const int* row_ptr, const int* col_idx, int r, const float* alpha,
+                                 int64_t group, int64_t N, int64_t K, const uint16_t* x,
+                                 int64_t M, float* y, hipStream_t s);
+
 // Mix'n'Match helpers.
 hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H,
                                hipStream_t stream);

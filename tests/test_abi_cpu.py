@@ -103,3 +103,15 @@ def test_quantize_validation(L):
     assert L.mq_quantize(NULL, 4, 64, 64, P16, P16, P16, NULL) == 1
     assert L.mq_quantize(P16, 4, 64, 32, P16, P16, P16, NULL) == 4
     assert L.mq_quantize(P16, 0, 64, 64, P16, P16, P16, NULL) == 2
+
+
+def test_overflow_validation(L):
+    assert L.mq_overflow_rows(NULL, 4, 64, 2, P16, NULL) == 1
+    assert L.mq_overflow_rows(P16, 4, 64, 5, P16, NULL) == 3
+    assert L.mq_overflow_rows(P16, 4, 96, 2, P16, NULL) == 2
+    assert L.mq_overflow_cols(P16, 4, 64, 2, P16, NULL, NULL) == 1
+    assert L.mq_overflow_cols(P16, 0, 64, 2, P16, P16, NULL) == 2
+    assert L.mq_overflow_apply(P16, P16, 2, P16, 64, 4, 64, NULL, 1, P16, NULL) == 1
+    assert L.mq_overflow_apply(P16, P16, 2, P16, 32, 4, 64, P16, 1, P16, NULL) == 4
+    assert L.mq_overflow_apply(P16, P16, 2, P16, 64, 4, 64, P16, 0, P16, NULL) == 2
+    assert L.mq_overflow_apply(P16, P16, 7, P16, 64, 4, 64, P16, 1, P16, NULL) == 3

@@ -218,6 +218,63 @@ def test_error_enqueues_nothing():
     assert torch.all(y == 7.0)
 
 
+# ---------------------------------------------------------------- Extra precision
+
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
+def test_overflow_lists_bit_exact(r):
+    note(f"overflow lists r={r}")
+    m = quantized("gemma9b_mlp", 300, 1536, 1536, matrix=4, outlier_frac=1e-2)
+    q = m["q"].copy()
+    q[7] = 255                      # a full row at the extra level
+    q[8] = 0                        # an empty row
+    q[9, ::3] = 255 - (np.arange(512) % 4)   # codes around the threshold
+    row_ptr, col_idx = mq.overflow_lists(torch.from_numpy(q).to(dev()), r)
+    torch.cuda.synchronize()
+    want_ptr, want_idx = oracle.overflow_lists(q, r)
+    assert row_ptr.cpu().numpy().tolist() == want_ptr.tolist()
+    assert col_idx.cpu().numpy().tolist() == want_idx.tolist()
+
+
+@pytest.mark.parametrize("r", [6, 4, 3, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_extra_precision_product(r, group, M):
+    """plane product at r + the sparse addition = the unclamped (errata Eq. 8)
+    product of the oracle."""
+    if M > 8 and r in (3, 6):
+        pytest.skip("r = 3 and 6 are served at M <= 8 only")
+    n, k = 260, 1024
+    g = k if group == "K" else 128
+    note(f"extra precision r={r} g={g} M={M}")
+    m = quantized("gemma9b_mlp", n, k, g, matrix=6, outlier_frac=2e-2)
+    assert np.any(oracle.slice_value_noclamp(m["q"], r) == 256)
+    xb = inputs.activations_bf16("gemma9b_mlp", M, k, matrix=6)
+    plane = mq.pack(m["q_d"], r)
+    y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    row_ptr, col_idx = mq.overflow_lists(m["q_d"], r)
+    mq.overflow_apply(row_ptr, col_idx, r, m["alpha_d"], g, n, k, x_device(xb), y)
+    torch.cuda.synchronize()
+    compare(y, oracle.linear_extra_precision(xb, m["q"], m["alpha"], m["zero"], g, r),
+            f"extra r{r} g{g} M{M}")
+
+
+def test_extra_precision_gemma_up_full_size():
+    note("extra precision gemma up r=2 full size")
+    n, k = inputs.GEMMA9B_MLP["up"]
+    m = quantized("gemma9b_mlp", n, k, k, matrix=0, outlier_frac=1e-3)
+    xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=0)
+    plane = mq.pack(m["q_d"], 2)
+    y = mq.gemv(plane, 2, m["alpha_d"], m["zero_d"], k, n, k, x_device(xb))
+    row_ptr, col_idx = mq.overflow_lists(m["q_d"], 2)
+    mq.overflow_apply(row_ptr, col_idx, 2, m["alpha_d"], k, n, k, x_device(xb), y)
+    torch.cuda.synchronize()
+    want_ptr, _ = oracle.overflow_lists(m["q"], 2)
+    assert row_ptr.cpu().numpy().tolist() == want_ptr.tolist()
+    rows = _sample_rows(n, 256, seed=5)
+    ref = oracle.linear_extra_precision(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], k, 2)
+    compare(y[:, rows], ref, "extra gemma up r2")
+
+
 # ---------------------------------------------------------------- GEMM (M > 8)
 
 @pytest.mark.parametrize("r", [8, 4, 2])
