@@ -402,3 +402,58 @@ def test_mixnmatch_small_stack(group_kind, M, rs):
     mq.mixnmatch_forward(arr, h, ws)
     torch.cuda.synchronize()
     compare(h, oracle.mixnmatch_forward(host, xb), "stack end-to-end")
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+def test_gemv_maximum_k(r, group):
+    """K at the library's maximum (65536), ragged N, several activation chunks."""
+    n, k = 17, 65536
+    g = k if group == "K" else 128
+    note(f"gemv max K r={r} g={g}")
+    m = quantized("tiny_linear", n, k, g, matrix=30)
+    for M in (1, 3):
+        xb = inputs.activations_bf16("tiny_linear", M, k, matrix=30)
+        y = mq.gemv(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+        torch.cuda.synchronize()
+        compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"max K r{r} M{M}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 64, 65, 255, 256, 300])
+def test_single_row_and_minimum_k(M):
+    """N = 1 and the smallest K (64 per-channel, 128 grouped), across the M
+    ranges that route to the decode, small-batch, tiled and prefill kernels."""
+    note(f"degenerate shapes M={M}")
+    for (n, k, g) in ((1, 64, 64), (1, 128, 128), (3, 64, 64), (33, 128, 128)):
+        m = quantized("tiny_linear", n, k, g, matrix=31)
+        xb = inputs.activations_bf16("tiny_linear", M, k, matrix=31)
+        for r in (8, 2):
+            y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+            torch.cuda.synchronize()
+            compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r),
+                    f"N{n} K{k} g{g} r{r} M{M}")
+
+
+def test_constant_rows_quantize_and_product():
+    """Rows (and groups) with a single value: alpha = 1, z = -min, codes 0
+    (the reading for a zero range); quantize bit-exact, products exact."""
+    note("constant rows")
+    n, k = 40, 512
+    w = inputs.gaussian_weights("tiny_linear", n, k, matrix=32)
+    w[3] = 0.25
+    w[7] = -1.5
+    w[11, 128:256] = 0.0   # one constant group of 128
+    for g in (k, 128):
+        q, a, z = oracle.quantize_minmax(w, g)
+        codes, alpha, zero = mq.quantize(torch.from_numpy(w).to(dev()), g)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), q)
+        assert np.array_equal(alpha.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        assert np.array_equal(zero.cpu().numpy().view(np.uint32), z.view(np.uint32))
+        xb = inputs.activations_bf16("tiny_linear", 2, k, matrix=32)
+        for r in (8, 4, 2):
+            y = mq.gemv(mq.pack(codes, r), r, alpha, zero, g, n, k, x_device(xb))
+            torch.cuda.synchronize()
+            compare(y, oracle.linear(xb, q, a, z, g, r), f"constant rows g{g} r{r}")
