@@ -233,8 +233,10 @@ size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_
 /*
  * Byte offsets inside the workspace of the intermediates of the LAST layer
  * run, valid after the call's work completes: a (bf16 [M, H]), q, k, v
- * (fp32 [M, H] / [M, Hkv]), u, g (fp32 [M, F]), o, d (fp32 [M, H]).
- * offsets must have room for 8 entries, in that order.
+ * (fp32 [M, H] / [M, Hkv]), u, g (fp32 [M, F]), o, d (fp32 [M, H]),
+ * bf16(q) (bf16 [M, H]) and bf16(u * g) (bf16 [M, F]; written only when up
+ * and gate have the same group, which lets one launch compute both and their
+ * product).  offsets must have room for 10 entries, in that order.
  */
 mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, int64_t M,
                                          size_t* offsets);

@@ -298,7 +298,7 @@ def mixnmatch_workspace_bytes(layer_arr, M: int) -> int:
 
 
 def mixnmatch_workspace_offsets(layer_arr, M: int):
-    off = (ctypes.c_size_t * 8)()
+    off = (ctypes.c_size_t * 10)()
     _check(lib().mq_mixnmatch_workspace_offsets(layer_arr, len(layer_arr), M, off),
            "mq_mixnmatch_workspace_offsets")
     return list(off)

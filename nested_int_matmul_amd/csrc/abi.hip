@@ -303,12 +303,17 @@ mq_status check_stack(const mq_layer* layers, int n_layers, int64_t M, StackDims
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// a, q, k, v, u, g, o, d, bf16(q), bf16(u * g)
+constexpr int kStackBuffers = 10;
+
 void stack_offsets(const StackDims& d, int64_t M, size_t* off, size_t* total) {
   size_t o = 0;
-  const size_t sizes[8] = {(size_t)(M * d.H * 2), (size_t)(M * d.H * 4), (size_t)(M * d.Hkv * 4),
-                           (size_t)(M * d.Hkv * 4), (size_t)(M * d.F * 4), (size_t)(M * d.F * 4),
-                           (size_t)(M * d.H * 4), (size_t)(M * d.H * 4)};
-  for (int i = 0; i < 8; ++i) {
+  const size_t sizes[kStackBuffers] = {
+      (size_t)(M * d.H * 2),   (size_t)(M * d.H * 4), (size_t)(M * d.Hkv * 4),
+      (size_t)(M * d.Hkv * 4), (size_t)(M * d.F * 4), (size_t)(M * d.F * 4),
+      (size_t)(M * d.H * 4),   (size_t)(M * d.H * 4), (size_t)(M * d.H * 2),
+      (size_t)(M * d.F * 2)};
+  for (int i = 0; i < kStackBuffers; ++i) {
     off[i] = o;
     o += up256(sizes[i]);
   }
@@ -327,7 +332,7 @@ mq::SkinnyProblem prob(const mq_linear& l, int r, const void* x0, const void* x1
 size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_t M) {
   StackDims d;
   if (check_stack(layers, n_layers, M, &d) != MQ_OK) return 0;
-  size_t off[8], total;
+  size_t off[kStackBuffers], total;
   stack_offsets(d, M, off, &total);
   return total;
 }
@@ -350,7 +355,7 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, i
   if (s != MQ_OK) return s;
   if (!h) return MQ_ERR_NULL;
   if (!aligned16(h)) return MQ_ERR_ALIGN;
-  size_t off[8], total;
+  size_t off[kStackBuffers], total;
   stack_offsets(d, M, off, &total);
   if (!workspace || workspace_bytes < total) return MQ_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MQ_ERR_ALIGN;
@@ -366,20 +371,35 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, i
   float* g = reinterpret_cast<float*>(ws + off[5]);
   float* o = reinterpret_cast<float*>(ws + off[6]);
   float* dd = reinterpret_cast<float*>(ws + off[7]);
+  uint16_t* qb = reinterpret_cast<uint16_t*>(ws + off[8]);
+  uint16_t* ugb = reinterpret_cast<uint16_t*>(ws + off[9]);
 
   hipError_t e = mq::launch_rmsnorm_bf16(h, a, M, d.H, st);
   if (e != hipSuccess) return hip_fail(e);
   for (int i = 0; i < n_layers; ++i) {
     const mq_layer& L = layers[i];
+    // first launch: q (with its bf16 copy), k, v and, when up and gate share
+    // a scale granularity, the up/gate pair in the same workgroups, which
+    // also writes bf16(up * gate); the second launch then reads bf16 inputs
+    const bool pair = L.up.group == L.gate.group;
     mq::SkinnyProblem p1[5] = {prob(L.q, L.r, a, nullptr, mq::kXBf16, q),
                                prob(L.k, L.r, a, nullptr, mq::kXBf16, k),
                                prob(L.v, L.r, a, nullptr, mq::kXBf16, v),
                                prob(L.up, L.r, a, nullptr, mq::kXBf16, u),
                                prob(L.gate, L.r, a, nullptr, mq::kXBf16, g)};
-    s = run_mixed(p1, 5, M, st);
+    p1[0].ybf = qb;
+    if (pair) {
+      p1[3].packed2 = L.gate.packed;
+      p1[3].alpha2 = L.gate.alpha;
+      p1[3].zero2 = L.gate.zero;
+      p1[3].y2 = g;
+      p1[3].ybf = ugb;
+    }
+    s = run_mixed(p1, pair ? 4 : 5, M, st);
     if (s != MQ_OK) return s;
-    mq::SkinnyProblem p2[2] = {prob(L.o, L.r, q, nullptr, mq::kXF32, o),
-                               prob(L.down, L.r, u, g, mq::kXF32Prod, dd)};
+    mq::SkinnyProblem p2[2] = {prob(L.o, L.r, qb, nullptr, mq::kXBf16, o),
+                               pair ? prob(L.down, L.r, ugb, nullptr, mq::kXBf16, dd)
+                                    : prob(L.down, L.r, u, g, mq::kXF32Prod, dd)};
     s = run_mixed(p2, 2, M, st);
     if (s != MQ_OK) return s;
     // the last layer leaves its own input a in the workspace

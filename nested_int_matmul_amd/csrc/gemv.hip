@@ -161,8 +161,11 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   const int M = args.M;
   const int K = P.K, N = P.N;
   const int KS = P.ks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rb0 = ((int)blockIdx.x - P.tile0) * P.rbpw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // a pair: the workgroup's row blocks alternate between the two matrices
+  // (even: first, odd: second) over rbpw / 2 distinct 16-row blocks
+  const bool paired = P.y2 != nullptr;
+  const int rb0 = ((int)blockIdx.x - P.tile0) * (paired ? P.rbpw / 2 : P.rbpw);
 
   const int kc = args.kc;             // codes per chunk
   const int xstride = kc + kXPad;     // staged row stride (bf16 elements)
@@ -173,14 +176,18 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   float* sxt = sxos + M * g_per_chunk;      // [M] per-channel total of x
   float* sxot = sxt + kSkinnyMaxM;          // [M] per-channel total of offset * x
   float* red = sxot + kSkinnyMaxM;          // [waves*16][M]
+  float* fin = red + kSkinnyWaves * 16 * M;  // [rows_wg][M] results (pairs)
 
   const int rowbytes = K * R / 8;
   const uint32_t plane_bytes = (uint32_t)((int64_t)N * rowbytes);
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(P.packed, plane_bytes);
   const int G = K / P.group;
 
   const int rbl = wave / KS, ks = wave % KS;
-  const int row0 = (rb0 + rbl) * 16;
+  const int sel = paired ? (rbl & 1) : 0;  // which matrix this wave streams
+  const int row0 = (rb0 + (paired ? rbl >> 1 : rbl)) * 16;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(sel ? P.packed2 : P.packed, plane_bytes);
+  const float* alpha_w = sel ? P.alpha2 : P.alpha;
+  const float* zero_w = sel ? P.zero2 : P.zero;
   const int col = lane & 15, slot = lane >> 4;
   const int n_ld = row0 + col;  // row this lane loads (A operand row)
   // rows past N: point the load past the plane so it returns zeros
@@ -196,10 +203,17 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   const int rows_wg = P.rbpw * 16;
   const int ep_rr = threadIdx.x % rows_wg;
   float ep_a = 0.f, ep_b = 0.f;
+  // virtual row block of the epilogue row: for a pair, even blocks are the
+  // first matrix's and odd blocks the second's
+  auto ep_sel = [&]() __attribute__((always_inline)) { return paired ? ((ep_rr >> 4) & 1) : 0; };
+  auto ep_n = [&]() __attribute__((always_inline)) {
+    return (rb0 + (paired ? ep_rr >> 5 : ep_rr >> 4)) * 16 + (ep_rr & 15);
+  };
   if (!GROUPED) {
-    const int n = rb0 * 16 + ep_rr;
+    const int n = ep_n();
     if (n < N) {
-      const float a = P.alpha[n], z = P.zero[n];
+      const int ep_sel = paired ? ((ep_rr >> 4) & 1) : 0;
+      const float a = (ep_sel ? P.alpha2 : P.alpha)[n], z = (ep_sel ? P.zero2 : P.zero)[n];
       ep_a = a * Enc<R>::kStep;
       ep_b = a * z;
     }
@@ -221,8 +235,8 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   const int xcol = col < M ? col : M - 1;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x0, (uint32_t)((int64_t)M * K * 2));
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(P.alpha, (uint32_t)((int64_t)N * G * 4));
-  const __amdgpu_buffer_rsrc_t zr = make_rsrc(P.zero, (uint32_t)((int64_t)N * G * 4));
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(alpha_w, (uint32_t)((int64_t)N * G * 4));
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(zero_w, (uint32_t)((int64_t)N * G * 4));
 
 #pragma unroll 1
   for (int c = 0; c < nchunks; ++c) {
@@ -413,17 +427,34 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * slot + i) * M + col] = acc[i];
   }
   __syncthreads();
+  const int mstep = (int)blockDim.x / rows_wg;
   {
     const int rr = ep_rr;
     const int rbl2 = rr >> 4, row = rr & 15;
-    const int n = rb0 * 16 + rr;
-    const int mstep = (int)blockDim.x / rows_wg;
+    const int n = ep_n();
+    float* yo = ep_sel() ? P.y2 : P.y;
     if (n < N) {
       for (int m = threadIdx.x / rows_wg; m < M; m += mstep) {
         float s = 0.f;
         for (int k2 = 0; k2 < KS; ++k2) s += red[((rbl2 * KS + k2) * 16 + row) * M + m];
         if (!GROUPED) s = ep_a * (s - sxot[m]) - ep_b * sxt[m];
-        P.y[(int64_t)m * N + n] = s;
+        yo[(int64_t)m * N + n] = s;
+        if (paired) fin[rr * M + m] = s;
+        else if (P.ybf) P.ybf[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(s);
+      }
+    }
+  }
+  if (paired && P.ybf) {
+    // bf16(first * second) for the rows of this workgroup
+    __syncthreads();
+    const int half = rows_wg / 2;  // distinct rows
+    for (int t = threadIdx.x; t < half * M; t += blockDim.x) {
+      const int j = t % half, m = t / half;
+      const int rr1 = ((j >> 4) * 2) * 16 + (j & 15), rr2 = rr1 + 16;
+      const int n = (rb0 + (j >> 4)) * 16 + (j & 15);
+      if (n < N) {
+        const float v = fin[rr1 * M + m] * fin[rr2 * M + m];
+        P.ybf[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
       }
     }
   }
@@ -494,10 +525,12 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
     const int spg = grouped ? 128 / step : 1;
     const int units = steps / spg;
     int ks = 1;
-    while (ks < waves && (units / (ks * 2)) * spg >= 12) ks *= 2;
+    // a pair needs two row blocks (one per matrix) per workgroup
+    const int ks_max = p.y2 ? waves / 2 : waves;
+    while (ks < ks_max && (units / (ks * 2)) * spg >= 12) ks *= 2;
     p.ks = ks;
     p.rbpw = waves / ks;
-    const int rblocks = (p.N + 15) / 16;
+    const int rblocks = (p.N + 15) / 16 * (p.y2 ? 2 : 1);
     p.tiles = (rblocks + p.rbpw - 1) / p.rbpw;
     steps_per_wave[i] = steps / ks;
   }
@@ -518,7 +551,7 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
   }
   const int gpc = kc / 128;
   const size_t lds = (size_t)M * (kc + kXPad) * 2 +
-                     (size_t)(2 * M * gpc + 2 * kSkinnyMaxM) * 4 + (size_t)waves * 16 * M * 4;
+                     (size_t)(2 * M * gpc + 2 * kSkinnyMaxM) * 4 + (size_t)2 * waves * 16 * M * 4;
   const bool split = args.p[0].r == 3 || args.p[0].r == 6;
   if (split)
     return grouped ? launch_t<true, true>(args, lds, stream) : launch_t<false, true>(args, lds, stream);

@@ -24,12 +24,21 @@ struct SkinnyProblem {
   const void* x1;
   float* y;
   int N, K, group, xmode;
-  int r;         // slice precision of this problem (2, 4 or 8)
+  int r;         // slice precision of this problem (2, 3, 4, 6 or 8)
   int ks;        // waves sharing one 16-row block (split of K)
   int rbpw;      // 16-row blocks per workgroup (rbpw * ks == waves per workgroup)
   int tiles;     // workgroups of this problem
   int tile0;     // first workgroup index of this problem
+  // optional: a second matrix of the same shape, precision and scales layout
+  // on the same x (its rows are computed by the same workgroups), and a
+  // bf16 copy of the output: bf16(y) alone, bf16(y * y2) for a pair
+  const uint8_t* packed2;
+  const float* alpha2;
+  const float* zero2;
+  float* y2;
+  uint16_t* ybf;
 };
+
 
 struct SkinnyArgs {
   SkinnyProblem p[kMaxProblems];

@@ -332,7 +332,10 @@ def _small_stack(rs, H=256, Hkv=64, F=512, group_kind="K"):
         hl, dl = {"r": r}, {"r": r}
         for mi, name in enumerate(oracle.LAYER_LINEARS):
             n, k = shapes[name]
-            g = k if group_kind == "K" else 128
+            if group_kind == "split":  # gate per group of 128, the rest per channel
+                g = 128 if name == "gate" else k
+            else:
+                g = k if group_kind == "K" else 128
             m = quantized("mistral_stack", n, k, g, layer=li, matrix=mi)
             hl[name] = {"q": m["q"], "alpha": m["alpha"], "zero": m["zero"], "group": g}
             dl[name] = {"packed": mq.pack(m["q_d"], r), "alpha": m["alpha_d"],
@@ -347,7 +350,7 @@ def _bf16_bits_of_f32(t):
 
 
 @pytest.mark.parametrize("rs", [(8, 4, 2, 4, 8), (6, 3, 8)])
-@pytest.mark.parametrize("group_kind", ["K", 128])
+@pytest.mark.parametrize("group_kind", ["K", 128, "split"])
 @pytest.mark.parametrize("M", [1, 2])
 def test_mixnmatch_small_stack(group_kind, M, rs):
     rs = list(rs)
@@ -386,8 +389,18 @@ def test_mixnmatch_small_stack(group_kind, M, rs):
             compare(y, oracle.linear(a_bits, p["q"], p["alpha"], p["zero"], p["group"], L["r"]),
                     f"layer {li} {name}")
         qb = _bf16_bits_of_f32(outs["q"])
-        ug = (outs["up"] * outs["gate"])
-        ugb = _bf16_bits_of_f32(ug)
+        ugb = _bf16_bits_of_f32(outs["up"] * outs["gate"])
+
+        def fetch_bf16(i, n):
+            t = ws[off[i]:off[i] + M * n * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+            return t.reshape(M, n)
+
+        # the bf16 copies the first launch writes are the nearest-even
+        # roundings of its own fp32 outputs (bit-exact)
+        np.testing.assert_array_equal(fetch_bf16(8, H), qb, err_msg=f"layer {li} bf16(q)")
+        if group_kind != "split":  # up and gate paired
+            np.testing.assert_array_equal(fetch_bf16(9, 512), ugb,
+                                          err_msg=f"layer {li} bf16(u*g)")
         o = fetch(6, H)
         d = fetch(7, H)
         compare(o, oracle.linear(qb, L["o"]["q"], L["o"]["alpha"], L["o"]["zero"],
