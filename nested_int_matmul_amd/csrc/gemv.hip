@@ -25,7 +25,10 @@
 //    and z are fetched at kernel start).
 //  - Waves that share a row block split K; their partial results are summed
 //    in LDS in a fixed order (deterministic), then written as fp32.
-//  - One launch can carry up to 8 independent problems (grouped GEMV).
+//  - One launch can carry up to 16 independent problems (grouped GEMV), each
+//    at its own r; a problem may pair two matrices of one shape that share x
+//    (alternate row blocks of a workgroup), which can also write bf16 of the
+//    elementwise product of the two outputs.
 #include "mq_device.h"
 #include "mq_internal.h"
 
