@@ -10,6 +10,7 @@ from .matquant import (  # noqa: F401
     LAYER_LINEARS,
     bf16_bits_from_float,
     bf16_round,
+    bitplane_bytes_read,
     dequant,
     dequant_extra_precision,
     dequant_rows,
@@ -20,12 +21,15 @@ from .matquant import (  # noqa: F401
     mixnmatch_forward,
     mixnmatch_layer,
     overflow_lists,
+    pack_bitplanes,
     pack_codes,
     pack_indices,
     quantize_minmax,
     rms_normalize,
     slice_index,
+    slice_index_from_bitplanes,
     slice_value,
     slice_value_noclamp,
+    unpack_bitplanes,
     unpack_indices,
 )

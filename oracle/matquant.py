@@ -235,6 +235,111 @@ def pack_codes(q, r: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Bit-plane storage: one stored copy of the codes that serves every r
+# --------------------------------------------------------------------------
+
+BITPLANE_SUPERBLOCK = 512  # codes per superblock of a plane row (64 bytes)
+
+
+def pack_bitplanes(q) -> np.ndarray:
+    """The eight bit-planes of the stored codes: uint8 [8, N, K/8], plane p
+    holding bit p of every code (p = 0 is the least significant bit).
+
+    The pages store one int8 model and obtain every lower precision from its
+    most significant bits ([MQX] "The Bit-Slicing Operator"; §2 on slicing the
+    one stored model).  Stored by bit, a server at precision r reads only the
+    planes it needs.
+
+    LAYOUT (a reading; the pages define no storage): each row of a plane is cut
+    into superblocks of 512 codes (64 bytes = 16 little-endian 32-bit words);
+    word 4*s + G of a superblock holds, at bit 16*h + i, the bit of code
+    128*G + 32*s + 2*i + h of that superblock (s, G in 0..3, i in 0..15,
+    h in 0..1).  K must be a multiple of 512.
+    """
+    q = np.asarray(q)
+    if q.ndim != 2 or np.any(q < 0) or np.any(q > 255):
+        raise ValueError("codes must be a 2-D array of values in 0..255")
+    n, k = q.shape
+    if k % BITPLANE_SUPERBLOCK:
+        raise ValueError("K must be a multiple of 512")
+    qi = q.astype(np.int64)
+    out = np.zeros((8, n, k // 8), dtype=np.uint8)
+    for p in range(8):
+        bits = (qi >> p) & 1
+        words = np.zeros((n, k // 32), dtype=np.int64)
+        for sb in range(k // BITPLANE_SUPERBLOCK):
+            for s in range(4):
+                for g in range(4):
+                    w = 0
+                    for i in range(16):
+                        for h in range(2):
+                            code = sb * 512 + 128 * g + 32 * s + 2 * i + h
+                            w = w | (bits[:, code] << (16 * h + i))
+                    words[:, sb * 16 + 4 * s + g] = w
+        for b in range(4):
+            out[p, :, b::4] = (words >> (8 * b)) & 0xFF
+    return out
+
+
+def unpack_bitplanes(planes) -> np.ndarray:
+    """Inverse of pack_bitplanes: uint8 [8, N, K/8] -> codes int64 [N, K]."""
+    pl = np.asarray(planes, dtype=np.int64)
+    if pl.ndim != 3 or pl.shape[0] != 8:
+        raise ValueError("planes must be [8, N, K/8]")
+    _, n, kb = pl.shape
+    k = kb * 8
+    if k % BITPLANE_SUPERBLOCK:
+        raise ValueError("K must be a multiple of 512")
+    q = np.zeros((n, k), dtype=np.int64)
+    for p in range(8):
+        words = pl[p, :, 0::4] | (pl[p, :, 1::4] << 8) | (pl[p, :, 2::4] << 16) | (pl[p, :, 3::4] << 24)
+        for sb in range(k // BITPLANE_SUPERBLOCK):
+            for s in range(4):
+                for g in range(4):
+                    w = words[:, sb * 16 + 4 * s + g]
+                    for i in range(16):
+                        for h in range(2):
+                            code = sb * 512 + 128 * g + 32 * s + 2 * i + h
+                            q[:, code] |= ((w >> (16 * h + i)) & 1) << p
+    return q
+
+
+def slice_index_from_bitplanes(planes, r: int, extra: bool = False) -> np.ndarray:
+    """The r-bit index read from bit-planes, int64 [N, K].
+
+    The quotient q / 2^(8-r) splits into its integer part h (the r most
+    significant bits, planes 8-r .. 7) and the first discarded bit c (plane
+    7-r); rounding half up adds c ([MQX] "The Bit-Slicing Operator": the first
+    discarded bit decides the rounding).  Eq. 6 clamps h + c to 2^r - 1, which
+    matters only when h is all ones and c = 1; with extra=True the clamp is
+    left out (the errata Eq. 8, Extra-Precision MatQuant) and the index can be
+    2^r.  At r = 8 nothing is discarded: the index is q."""
+    if not 1 <= r <= C_BITS:
+        raise ValueError("r must be in 1..8")
+    pl = np.asarray(planes, dtype=np.int64)
+    _, n, kb = pl.shape
+    bits = [None] * 8
+    q = unpack_bitplanes(pl)
+    for p in range(8):
+        bits[p] = (q >> p) & 1
+    h = np.zeros((n, kb * 8), dtype=np.int64)
+    for j in range(r):
+        h = h + (bits[C_BITS - r + j] << j)
+    if r == C_BITS:
+        return h
+    c = bits[C_BITS - 1 - r]
+    t = h + c
+    if not extra:
+        t = np.minimum(t, 2 ** r - 1)
+    return t
+
+
+def bitplane_bytes_read(n: int, k: int, r: int) -> int:
+    """Bytes of planes a server at r reads: r + 1 planes (all 8 at r = 8)."""
+    return n * (k // 8) * (min(r + 1, C_BITS))
+
+
+# --------------------------------------------------------------------------
 # Dequantization and the matrix product
 # --------------------------------------------------------------------------
 

@@ -228,6 +228,77 @@ def test_hand_packed_split_planes():
         assert oracle.unpack_indices(got, r, k).tolist() == t.tolist()
 
 
+def _golden_bitplane_cases():
+    for line in open(os.path.join(GOLDEN, "pack_layout_bitplanes.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, right = line.split(";")
+        head, codes = left.split("|")
+        n, k = (int(v) for v in head.split())
+        q = np.zeros((n, k), dtype=np.int64)
+        for item in codes.split():
+            where, v = item.split("=")
+            row, cols = where.split(",")
+            lo, _, hi = cols.partition("-")
+            q[int(row), int(lo):int(hi or lo) + 1] = int(v)
+        want = np.zeros((8, n, k // 8), dtype=np.uint8)
+        for item in right.split():
+            where, v = item.split("=")
+            plane, byte = (int(x) for x in where.split(":"))
+            want[plane].reshape(-1)[byte] = int(v, 16)
+        yield q, want
+
+
+def test_hand_packed_bitplanes():
+    cases = list(_golden_bitplane_cases())
+    assert len(cases) == 3
+    for q, want in cases:
+        got = oracle.pack_bitplanes(q)
+        assert got.shape == want.shape and got.dtype == np.uint8
+        assert np.array_equal(got, want)
+        assert np.array_equal(oracle.unpack_bitplanes(got), q)
+
+
+def test_bitplanes_roundtrip_and_shape_checks():
+    rg = np.random.default_rng(77)
+    q = rg.integers(0, 256, size=(3, 1024))
+    pl = oracle.pack_bitplanes(q)
+    assert pl.shape == (8, 3, 128)
+    assert np.array_equal(oracle.unpack_bitplanes(pl), q)
+    # plane p holds exactly the set bits p of the codes (population counts agree)
+    for p in range(8):
+        assert int(np.unpackbits(pl[p]).sum()) == int(((q >> p) & 1).sum())
+    with pytest.raises(ValueError):
+        oracle.pack_bitplanes(np.zeros((1, 256), dtype=np.int64))  # K not a multiple of 512
+
+
+@pytest.mark.parametrize("extra", [False, True])
+def test_slice_from_bitplanes_brute_force(extra):
+    # every code at every r, through the planes (integer part + first discarded
+    # bit) against Eq. 6 (clamped) or the errata Eq. 8 (unclamped) evaluated
+    # as rounded quotients
+    q = np.tile(ALL_CODES, 2).reshape(1, 512)
+    pl = oracle.pack_bitplanes(q)
+    for r in range(1, 9):
+        t = oracle.slice_index_from_bitplanes(pl, r, extra=extra)
+        if extra:
+            want = oracle.slice_value_noclamp(q, r) // 2 ** (8 - r)
+        else:
+            want = oracle.slice_index(q, r)
+        assert np.array_equal(t, want), r
+    # the unclamped index exceeds 2^r - 1 for exactly 2^(7-r) codes (r < 8)
+    for r in range(1, 8):
+        t = oracle.slice_index_from_bitplanes(oracle.pack_bitplanes(ALL_CODES.reshape(1, 256).repeat(2, 1)), r, extra=True)
+        assert int((t == 2 ** r).sum()) == 2 * 2 ** (7 - r)
+
+
+def test_bitplane_bytes_read():
+    # r + 1 planes of N*K/8 bytes; all eight at r = 8
+    assert oracle.bitplane_bytes_read(14336, 3584, 2) == 3 * 14336 * 3584 // 8
+    assert oracle.bitplane_bytes_read(14336, 3584, 4) == 5 * 14336 * 3584 // 8
+    assert oracle.bitplane_bytes_read(14336, 3584, 8) == 14336 * 3584
+
+
 @pytest.mark.parametrize("r", [3, 6])
 def test_split_planes_roundtrip_and_sizes(r):
     rg = np.random.default_rng(40 + r)
