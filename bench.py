@@ -245,6 +245,8 @@ def run_rows(torch, mq, inputs, dev):
     rows["mixnmatch_mistral7b_32l"] = run_stack(torch, mq, inputs, dev)
     # f2: Extra-Precision r = 2 on the Gemma MLP: the sparse addition after the plane product
     rows["extra_precision_gemma_r2"] = run_extra(torch, mq, inputs, dev)
+    # f3: bit-plane storage, one copy served at several r
+    rows["bitplanes_gemma9b_mlp"] = run_bitplanes(torch, mq, inputs, dev)
     return rows
 
 
@@ -275,6 +277,47 @@ def run_extra(torch, mq, inputs, dev, r=2):
     return {"r": r, "apply_us_3_matrices": round(us, 2), "overflow_codes": nnz_total,
             "overflow_fraction": round(nnz_total / codes_total, 6),
             "effective_bits": round(r + list_bits / codes_total, 4)}
+
+
+def run_bitplanes(torch, mq, inputs, dev):
+    """NEXT-3: one bit-plane copy of the Gemma MLP codes served at several r
+    (and unclamped at r = 2); planes read = (r + 1)/8 of the codes (8/8 at
+    r = 8).  One launch per matrix, three per MLP."""
+    mats = []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=i, outlier_frac=1e-3)
+        codes, alpha, zero = mq.quantize(w, k)
+        del w
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        x = torch.from_numpy(xb.view("int16")).to(dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        mats.append(dict(codes=codes, alpha=alpha, zero=zero, N=n, K=k, x=x, y=y))
+    out = {}
+    down = mats[2]
+    pl_out = torch.empty((8, down["N"], down["K"] // 8), dtype=torch.uint8, device=dev)
+    us = time_loop(torch, lambda i: mq.pack_bitplanes(down["codes"], out=pl_out), 20)
+    out["pack_down_us"] = round(us, 2)
+    out["pack_down_GB/s"] = round(2 * down["N"] * down["K"] / us / 1e3, 1)
+    del pl_out
+    one = sum(m["N"] * m["K"] for m in mats)
+    ncopy = max(2, -(-ROTATE_BYTES // one))
+    planes = [[mq.pack_bitplanes(m["codes"]) for m in mats] for _ in range(ncopy)]
+    for m in mats:
+        del m["codes"]
+    torch.cuda.synchronize()
+    for r, extra in ((2, False), (2, True), (3, False), (4, False), (6, False), (8, False)):
+        def run(i):
+            for j, m in enumerate(mats):
+                mq.gemv_bitplanes(planes[i % ncopy][j], r, m["alpha"], m["zero"], m["K"], m["N"],
+                                  m["K"], m["x"], extra=extra, out=m["y"])
+        us = time_loop(torch, run, 50)
+        b = sum(min(r + 1, 8) * m["N"] * m["K"] // 8 + 8 * m["N"] + 2 * m["K"] + 4 * m["N"]
+                for m in mats)
+        out[f"r{r}" + ("_extra" if extra else "")] = {
+            "us_3_launches": round(us, 2), "bytes": b, "GB/s": round(b / us / 1e3, 1),
+            "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def run_stack(torch, mq, inputs, dev, n_layers=32):

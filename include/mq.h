@@ -201,6 +201,38 @@ mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int 
                             const uint16_t* x, int64_t M, float* y, void* stream);
 
 /*
+ * Bit-plane storage: one stored copy of the codes, as eight planes of one bit
+ * each, serving every precision r = 1..8 without repacking (the one stored
+ * int8 model of the explainer's §2 and "The Bit-Slicing Operator", read by
+ * bit).  The index of Eq. 6 is the integer part h of q / 2^(8-r) (planes
+ * 8-r .. 7) plus the first discarded bit c (plane 7-r), clamped to 2^r - 1;
+ * a server at r reads r + 1 planes, (r + 1)/8 of the bytes (all 8 at r = 8).
+ *
+ * Layout (uint8 [8][N][K/8], plane p = bit p of q): each plane row is cut
+ * into 512-code superblocks of 16 little-endian 32-bit words; word 4s + G
+ * holds at bit 16h + i the bit of code 128G + 32s + 2i + h of the superblock
+ * (s, G in 0..3, i in 0..15, h in 0..1).
+ *
+ * mq_bitplanes_bytes: N * K (0 on invalid shapes).
+ * mq_pack_bitplanes: codes uint8 [N, K] -> planes (output), both 16-byte
+ *   aligned.  Bit-exact.
+ * mq_gemv_bitplanes: the product of mq_gemv with the index read from the
+ *   planes.  extra = 1 leaves out the clamp (the errata Eq. 8,
+ *   Extra-Precision MatQuant: the index may reach 2^r, value 256) and so
+ *   needs no overflow lists; at r = 8 it changes nothing.
+ *   alpha, zero fp32 [N, K/group]; x bf16 bits [M, K] and y fp32 [M, N],
+ *   16-byte aligned.
+ * Sizes: N >= 1, K % 512 == 0, 512 <= K <= 65536, N * K <= 2^31;
+ * 1 <= M <= 8; 1 <= r <= 8; group = K or 128; extra in {0, 1}.
+ */
+size_t mq_bitplanes_bytes(int64_t N, int64_t K);
+mq_status mq_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uint8_t* planes,
+                            void* stream);
+mq_status mq_gemv_bitplanes(const uint8_t* planes, int r, int extra, const float* alpha,
+                            const float* zero, int64_t group, int64_t N, int64_t K,
+                            const uint16_t* x, int64_t M, float* y, void* stream);
+
+/*
  * Mix'n'Match stack ("Matryoshka Quantization" explainer, §3.4 "Mix'n'Match
  * and Interpolative Slicing"): a stack of layers over one stored int8 model,
  * each layer sliced to its own r.

@@ -32,6 +32,7 @@ EXPORTS = (
     "mq_gemm_workspace_bytes",
     "mq_gemm", "mq_mixnmatch_workspace_bytes", "mq_mixnmatch_workspace_offsets",
     "mq_mixnmatch_forward", "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
+    "mq_bitplanes_bytes", "mq_pack_bitplanes", "mq_gemv_bitplanes",
 )
 
 
@@ -97,6 +98,12 @@ def lib() -> ctypes.CDLL:
     L.mq_overflow_cols.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     L.mq_overflow_apply.restype = i32
     L.mq_overflow_apply.argtypes = [vp, vp, i32, vp, i64, i64, i64, vp, i64, vp, vp]
+    L.mq_bitplanes_bytes.restype = sz
+    L.mq_bitplanes_bytes.argtypes = [i64, i64]
+    L.mq_pack_bitplanes.restype = i32
+    L.mq_pack_bitplanes.argtypes = [vp, i64, i64, vp, vp]
+    L.mq_gemv_bitplanes.restype = i32
+    L.mq_gemv_bitplanes.argtypes = [vp, i32, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp]
     L.mq_gemv_mixed.restype = i32
     L.mq_gemv_mixed.argtypes = [ctypes.POINTER(GemvProblem), ctypes.POINTER(ctypes.c_int), i32,
                                 i64, vp]
@@ -255,6 +262,38 @@ def overflow_apply(row_ptr, col_idx, r: int, alpha, group: int, N: int, K: int, 
     _check(lib().mq_overflow_apply(_ptr(row_ptr), _ptr(ci), r, _ptr(alpha), group, N, K, _ptr(x),
                                    x.shape[0], _ptr(y), _stream(stream)), "mq_overflow_apply")
     return y
+
+
+def bitplanes_bytes(N: int, K: int) -> int:
+    return int(lib().mq_bitplanes_bytes(N, K))
+
+
+def pack_bitplanes(codes, out=None, stream=None):
+    """The eight bit-planes of uint8 codes [N, K]: uint8 [8, N, K/8]."""
+    import torch
+
+    n, k = codes.shape
+    if out is None:
+        out = torch.empty((8, n, k // 8), dtype=torch.uint8, device=codes.device)
+    _check(lib().mq_pack_bitplanes(_ptr(codes), n, k, _ptr(out), _stream(stream)),
+           "mq_pack_bitplanes")
+    return out
+
+
+def gemv_bitplanes(planes, r: int, alpha, zero, group: int, N: int, K: int, x, extra=False,
+                   out=None, stream=None):
+    """y = x @ dequant(S(q, r))^T read from bit-planes (unclamped slice with
+    extra=True): fp32 [M, N]."""
+    import torch
+
+    x = _bits16(x)
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _check(lib().mq_gemv_bitplanes(_ptr(planes), r, int(bool(extra)), _ptr(alpha), _ptr(zero),
+                                   group, N, K, _ptr(x), m, _ptr(out), _stream(stream)),
+           "mq_gemv_bitplanes")
+    return out
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmq.so")
 
 SOURCES = ["quant_pack.hip", "gemv.hip", "gemm.hip", "gemm_panel.hip", "gemm_big.hip",
-           "mixnmatch.hip", "extra.hip", "abi.hip"]
+           "mixnmatch.hip", "extra.hip", "bitplane.hip", "abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

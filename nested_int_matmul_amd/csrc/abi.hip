@@ -244,6 +244,50 @@ mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
   return e == hipSuccess ? MQ_OK : hip_fail(e);
 }
 
+// ---- bit-plane storage
+
+static mq_status check_bitplane_shape(int64_t N, int64_t K) {
+  if (N < 1 || K < 512 || K % 512 != 0 || K > kMaxK || N * K > kMaxPlaneBytes)
+    return MQ_ERR_SHAPE;
+  return MQ_OK;
+}
+
+size_t mq_bitplanes_bytes(int64_t N, int64_t K) {
+  return check_bitplane_shape(N, K) == MQ_OK ? (size_t)(N * K) : 0;
+}
+
+mq_status mq_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uint8_t* planes,
+                            void* stream) {
+  if (!codes || !planes) return MQ_ERR_NULL;
+  mq_status s = check_bitplane_shape(N, K);
+  if (s != MQ_OK) return s;
+  if (!aligned16(codes) || !aligned16(planes)) return MQ_ERR_ALIGN;
+  s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_pack_bitplanes(codes, N, K, planes, (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
+mq_status mq_gemv_bitplanes(const uint8_t* planes, int r, int extra, const float* alpha,
+                            const float* zero, int64_t group, int64_t N, int64_t K,
+                            const uint16_t* x, int64_t M, float* y, void* stream) {
+  if (!planes || !alpha || !zero || !x || !y) return MQ_ERR_NULL;
+  if (r < 1 || r > 8) return MQ_ERR_PRECISION;
+  if (extra != 0 && extra != 1) return MQ_ERR_PRECISION;
+  mq_status s = check_bitplane_shape(N, K);
+  if (s != MQ_OK) return s;
+  if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
+  if (!(group == K || group == 128)) return MQ_ERR_GROUP;
+  if (!aligned16(planes) || !aligned16(x) || !aligned16(y)) return MQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(zero) & 3u))
+    return MQ_ERR_ALIGN;
+  s = check_device();
+  if (s != MQ_OK) return s;
+  hipError_t e = mq::launch_gemv_bitplanes(planes, r, extra != 0, alpha, zero, group, N, K, x, M,
+                                           y, (hipStream_t)stream);
+  return e == hipSuccess ? MQ_OK : hip_fail(e);
+}
+
 mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int r,
                             const float* alpha, int64_t group, int64_t N, int64_t K,
                             const uint16_t* x, int64_t M, float* y, void* stream) {

@@ -1,0 +1,458 @@
+// Bit-plane storage: one stored copy of the 8-bit codes, kept as eight planes
+// of one bit each, serves every precision r = 1..8 without repacking.
+//
+// Slicing from planes ("Matryoshka Quantization" explainer, §3.4 "The
+// Bit-Slicing Operator"): the index of Eq. 6 is the integer part of
+// q / 2^(8-r) (the r most significant bits h, planes 8-r .. 7) plus the first
+// discarded bit c (plane 7-r: rounding half up), clamped to 2^r - 1.  The
+// clamp matters only where h is all ones and c = 1; the unclamped form (the
+// errata Eq. 8, "Extra-Precision MatQuant") keeps the extra level 2^r.  A
+// server at r reads r + 1 planes ((r + 1)/8 of the bytes; all 8 at r = 8).
+//
+// Storage (uint8 [8][N][K/8], plane p = bit p of q): each plane row is cut
+// into 512-code superblocks of 64 bytes = 16 little-endian words; word 4s + G
+// holds, at bit 16h + i, the bit of code 128G + 32s + 2i + h (s, G in 0..3,
+// i in 0..15, h in 0..1).  K is a multiple of 512.
+//
+// Product (decode, M <= 8), design for gfx950:
+//  - A wave owns 16 rows and a range of superblocks; per superblock each lane
+//    loads 16 bytes (words 4s .. 4s+3, s = lane / 16) of its row from each
+//    plane it needs, through bounds-checked buffer loads kept DEPTH
+//    superblocks ahead.  The loads of a wave cover 16 rows x 64 contiguous
+//    bytes per plane.
+//  - The index t = h + c is formed bit-sliced on whole words (32 codes per
+//    operation): a ripple carry through the h planes, with c dropped where h
+//    is all ones unless the unclamped slice is asked for.
+//  - Word G of a lane covers 32 codes of group G (128 codes); the four lanes
+//    slots together cover the group, so one v_mfma_f32_16x16x32_bf16 never
+//    mixes groups.  Bit i and bit 16 + i of a t-plane word j are moved to
+//    mantissa bit e in {4, 5, 6} and OR-ed under the exponent of
+//    2^(7 - e + j): an exact bf16 equal to 2^(7-e+j) + 2^j * bit.  All planes
+//    of a group accumulate into one fp32 accumulator that starts at minus the
+//    group's total offset (sum over planes and codes of 2^(7-e+j) * x), so it
+//    holds the group's sum of x * t; the small positions e keep the offset,
+//    and so the fp32 rounding, small.  At the group's end it is folded into
+//    the row total (with the group's alpha and z when group = 128).
+//  - Activations are staged in LDS in natural order (buffer-to-LDS loads);
+//    the same pass forms, per group of 128, the sum of x and the offset sum.
+//  - Waves that share a row block split the superblocks; their results are
+//    summed in LDS in a fixed order (deterministic).
+#include <utility>
+
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+namespace bp {
+
+constexpr int kWaves = 8;     // waves per workgroup
+constexpr int kSuper = 512;   // codes of a row per superblock (one step)
+constexpr int kXPad = 8;      // bf16 elements of padding per staged activation row
+
+template <int R, bool EXTRA>
+struct Bp {
+  static constexpr int PL = R < 8 ? R + 1 : 8;                   // planes read
+  static constexpr int FIRST = R < 8 ? 7 - R : 0;                // lowest plane read
+  static constexpr int PT = R < 8 ? (EXTRA ? R + 1 : R) : 8;     // planes of t
+  static constexpr int DEPTH = PL <= 2 ? 4 : (PL <= 3 ? 3 : 2);  // superblocks in flight
+  static constexpr float WTOT = (float)((1 << PT) - 1);          // sum of plane weights 2^j
+  static constexpr float STEP = (float)(1 << (8 - R));           // 2^(8-r)
+};
+
+// Word bit i (and 16 + i) is shifted right by bit_shift(i) (left if negative)
+// onto mantissa bit bit_pos(i) in {4, 5, 6} of the low (high) bf16 half.
+__host__ __device__ constexpr int bit_shift(int i) {
+  return i == 0 ? -4 : i < 4 ? -3 : i < 7 ? 0 : i < 10 ? 3 : i < 13 ? 6 : 9;
+}
+__host__ __device__ constexpr int bit_pos(int i) { return i - bit_shift(i); }
+
+template <int I>
+__device__ __forceinline__ uint32_t shifted(uint32_t w) {
+  constexpr int s = bit_shift(I);
+  if constexpr (s >= 0) return w >> s;
+  else return w << (-s);
+}
+
+// (w & mask) | magic, written in C so that the compiler sees every write and
+// keeps the wait states the matrix cores need between an operand's last
+// write and its read (and between that read and the operand's next write).
+// The mask sits in a vector register and the magic is a constant, so the pair
+// forms one v_and_or_b32 with the magic in a scalar register.
+__device__ __forceinline__ uint32_t and_or_c(uint32_t w, uint32_t m, uint32_t o) {
+  return (w & m) | o;
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+struct Args {
+  const uint8_t* planes;
+  const float* alpha;
+  const float* zero;
+  const uint16_t* x;
+  float* y;
+  int N, K, group, M, kc, ks;
+};
+
+template <int R, bool GROUPED, bool EXTRA>
+__global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
+  using C = Bp<R, EXTRA>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int M = P.M, K = P.K, N = P.N, KS = P.ks;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rbpw = kWaves / KS;
+  const int rb0 = (int)blockIdx.x * rbpw;
+
+  const int kc = P.kc;
+  const int xstride = kc + kXPad;
+  const int gpc = kc / 128;  // groups per chunk
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                       // [M][xstride]
+  float* sxs = reinterpret_cast<float*>(smem + (size_t)M * xstride * 2);  // [M][gpc] sum of x
+  float* sxos = sxs + M * gpc;           // [M][gpc] sum of 2^(7 - e) x
+  float* sxt = sxos + M * gpc;           // [M] total of x
+  float* red = sxt + kSkinnyMaxM;        // [kWaves * 16][M]
+
+  const uint32_t rowb = (uint32_t)K / 8;
+  const uint32_t plane_bytes = (uint32_t)N * rowb;
+  const int G = K / P.group;
+  const int rbl = wave / KS, ks = wave % KS;
+  const int row0 = (rb0 + rbl) * 16;
+  const int col = lane & 15, slot = lane >> 4;
+  const int n_ld = row0 + col;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.planes, 8u * plane_bytes);
+  // the lane's bytes of its row in the lowest plane read; rows past N read zeros
+  const uint32_t row_off = n_ld < N ? (uint32_t)C::FIRST * plane_bytes + (uint32_t)n_ld * rowb +
+                                          (uint32_t)slot * 16u
+                                    : 0x80000000u;
+
+  // per-channel epilogue operands: thread t writes row rr = t % rows_wg
+  const int rows_wg = rbpw * 16;
+  const int ep_rr = threadIdx.x % rows_wg;
+  float ep_a = 0.f, ep_b = 0.f;
+  if (!GROUPED) {
+    const int n = rb0 * 16 + ep_rr;
+    if (n < N) {
+      const float a = P.alpha[n], z = P.zero[n];
+      ep_a = a * C::STEP;
+      ep_b = a * z;
+    }
+  }
+  if (threadIdx.x < kSkinnyMaxM) sxt[threadIdx.x] = 0.f;
+
+  // masks of mantissa bits 4, 5, 6 in both halves, held in vector registers
+  uint32_t mk4 = 0x00100010u, mk5 = 0x00200020u, mk6 = 0x00400040u;
+  asm volatile("" : "+v"(mk4), "+v"(mk5), "+v"(mk6));
+  auto mask_of = [&](int e) __attribute__((always_inline)) {
+    return e == 4 ? mk4 : (e == 5 ? mk5 : mk6);
+  };
+
+  const int xcol = col < M ? col : M - 1;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x, (uint32_t)((int64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(P.alpha, (uint32_t)((int64_t)N * G * 4));
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(P.zero, (uint32_t)((int64_t)N * G * 4));
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  const int nchunks = (K + kc - 1) / kc;
+
+#pragma unroll 1
+  for (int c = 0; c < nchunks; ++c) {
+    const int ck0 = c * kc;
+    const int clen = min(kc, K - ck0);
+    const int csteps = clen / kSuper;
+    const int lo = __builtin_amdgcn_readfirstlane(csteps * ks / KS);
+    const int hi = __builtin_amdgcn_readfirstlane(csteps * (ks + 1) / KS);
+    const uint32_t cbase = row_off + (uint32_t)(ck0 / 8);
+    auto loff = [&](int st) __attribute__((always_inline)) -> uint32_t {
+      return (st < hi && row_off != 0x80000000u) ? cbase + (uint32_t)st * 64u : 0x80000000u;
+    };
+    u32x4 buf[C::DEPTH][C::PL];
+    __syncthreads();
+    // ---- stage x[:, ck0 : ck0 + clen): one 1 KiB piece per wave instruction
+    {
+      const int pieces = clen / 512;
+      for (int pc = wave; pc < M * pieces; pc += kWaves) {
+        const int m = pc / pieces, j = pc - m * pieces;
+        const int k = ck0 + j * 512 + lane * 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (__attribute__((address_space(3))) void*)(xs + (size_t)m * xstride + j * 512), 16,
+            (uint32_t)((m * K + k) * 2), 0, 0, 0);
+      }
+    }
+    // ---- first superblocks of this wave, behind the staging loads
+#pragma unroll
+    for (int d = 0; d < C::DEPTH; ++d)
+#pragma unroll
+      for (int pl = 0; pl < C::PL; ++pl) {
+        const uint32_t o = loff(lo + d);
+        buf[d][pl] = buf_load16(pr, o == 0x80000000u ? o : o + (uint32_t)pl * plane_bytes);
+      }
+    __syncthreads();
+    // ---- per group of 128: sum of x and sum of 2^(7 - e(k)) x, where
+    //      e(k) = bit_pos(((k mod 32) >> 1)) is the mantissa bit of code k
+    {
+      const int bpr = clen / 8;
+      const int total = M * bpr;
+      const uint32_t ones = 0x3F803F80u;
+      for (int b0 = 0; b0 < total; b0 += blockDim.x) {
+        const int b = b0 + threadIdx.x;
+        float s = 0.f, so = 0.f;
+        int m = 0, kb = 0;
+        if (b < total) {
+          m = b / bpr;
+          kb = (b - m * bpr) * 8;
+          const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + kb);
+          const int i0 = (kb & 31) >> 1;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float pair = dot2_bf16(w4[q], ones, 0.f);
+            s += pair;
+            so += (float)(1 << (7 - bit_pos(i0 + q))) * pair;
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          s += __shfl_xor(s, off);
+          so += __shfl_xor(so, off);
+        }
+        if (b < total && (kb % 128) == 0) {
+          sxs[m * gpc + kb / 128] = s;
+          sxos[m * gpc + kb / 128] = so;
+        }
+      }
+    }
+    __syncthreads();
+    if (!GROUPED) {
+      for (int m = wave; m < M; m += kWaves) {
+        float s = 0.f;
+        for (int gi = lane; gi < clen / 128; gi += 64) s += sxs[m * gpc + gi];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        if (lane == 0) sxt[m] += s;
+      }
+    }
+
+    // ---- stream this wave's superblocks
+    const uint16_t* xrow = xs + (size_t)xcol * xstride + slot * 32;
+#pragma unroll 1
+    for (int base = lo; base < hi; base += C::DEPTH) {
+#pragma unroll
+      for (int d = 0; d < C::DEPTH; ++d) {
+        const int st = base + d;
+        if (st < hi) {
+#pragma unroll
+          for (int Gi = 0; Gi < 4; ++Gi) {
+            // the index planes of word Gi (bit-sliced, 32 codes per word)
+            uint32_t t[C::PT];
+            if constexpr (R == 8) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) t[j] = buf[d][j][Gi];
+            } else {
+              uint32_t cy = buf[d][0][Gi];
+              if constexpr (!EXTRA) {
+                uint32_t all = buf[d][1][Gi];
+#pragma unroll
+                for (int j = 1; j < R; ++j) all &= buf[d][1 + j][Gi];
+                cy &= ~all;
+              }
+#pragma unroll
+              for (int j = 0; j < R; ++j) {
+                const uint32_t h = buf[d][1 + j][Gi];
+                t[j] = h ^ cy;
+                cy = h & cy;
+              }
+              if constexpr (EXTRA) t[R] = cy;
+            }
+            const int gl = st * 4 + Gi;  // group in the chunk
+            const float so = sxos[xcol * gpc + gl];
+            f32x4 part;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[i] = -C::WTOT * so;
+            const uint16_t* xp = xrow + st * kSuper + Gi * 128;
+            static_for<4>([&](auto mu) __attribute__((always_inline)) {
+              const u32x4 xv = *reinterpret_cast<const u32x4*>(xp + 8 * mu.value);
+              static_for<C::PT>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int i0 = 4 * decltype(mu)::value;
+                uint32_t a[4];
+                static_for<4>([&](auto qc) __attribute__((always_inline)) {
+                  constexpr int i = i0 + decltype(qc)::value;
+                  constexpr int e = bit_pos(i);
+                  constexpr uint32_t mag = (uint32_t)((134 - e + j) << 7) * 0x00010001u;
+                  a[decltype(qc)::value] = and_or_c(shifted<i>(t[j]), mask_of(e), mag);
+                });
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[0], a[1], a[2], a[3]),
+                                                               __builtin_bit_cast(bf16x8, xv),
+                                                               part, 0, 0, 0);
+              });
+            });
+            if constexpr (GROUPED) {
+              const int g = ck0 / 128 + gl;
+              const float gsx = sxs[xcol * gpc + gl];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int n = row0 + 4 * slot + i;
+                const uint32_t aoff = (n < N) ? (uint32_t)(n * G + g) * 4u : 0x80000000u;
+                const float ga = __uint_as_float(buf_load4(ar, aoff));
+                const float gz = __uint_as_float(buf_load4(zr, aoff));
+                tot[i] = tot[i] + (ga * C::STEP) * part[i] - (ga * gz) * gsx;
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) tot[i] += part[i];
+            }
+          }
+        }
+        // refill this slot after its last use
+        const uint32_t o = loff(st + C::DEPTH);
+#pragma unroll
+        for (int pl = 0; pl < C::PL; ++pl)
+          buf[d][pl] = buf_load16(pr, o == 0x80000000u ? o : o + (uint32_t)pl * plane_bytes);
+      }
+    }
+  }
+
+  // ---- sum the K splits in a fixed order, then write y
+  __syncthreads();
+  if (col < M) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * slot + i) * M + col] = tot[i];
+  }
+  __syncthreads();
+  {
+    const int rr = ep_rr;
+    const int rbl2 = rr >> 4, row = rr & 15;
+    const int n = rb0 * 16 + rr;
+    const int mstep = (int)blockDim.x / rows_wg;
+    if (n < N) {
+      for (int m = threadIdx.x / rows_wg; m < M; m += mstep) {
+        float s = 0.f;
+        for (int k2 = 0; k2 < KS; ++k2) s += red[((rbl2 * KS + k2) * 16 + row) * M + m];
+        if (!GROUPED) s = ep_a * s - ep_b * sxt[m];
+        P.y[(int64_t)m * N + n] = s;
+      }
+    }
+  }
+}
+
+// codes [N][K] -> planes [8][N][K/8]; one thread per output word of a row
+// (32 codes: 128G + 32s + 0..31 of a superblock), one word per plane.
+__global__ void __launch_bounds__(256) pack_bitplanes_kernel(const uint8_t* __restrict__ codes,
+                                                             int N, int K,
+                                                             uint8_t* __restrict__ planes) {
+  const int64_t wpr = K / 32;
+  const int64_t total = (int64_t)N * wpr;
+  const int64_t plane_words = total;
+  uint32_t* out = reinterpret_cast<uint32_t*>(planes);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / wpr;
+    const int wi = (int)(t - n * wpr);
+    const int sb = wi >> 4, s = (wi >> 2) & 3, g = wi & 3;
+    const uint8_t* src = codes + n * K + sb * kSuper + 128 * g + 32 * s;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
+    const uint32_t dw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    uint32_t w[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) w[p] = 0u;
+    // dword a holds codes 4a .. 4a+3 (byte b): code 4a + b has i = 2a + (b >> 1),
+    // h = b & 1, so its bit goes to 16h + i: b = 0 -> 2a, 1 -> 16 + 2a, 2 -> 2a + 1,
+    // 3 -> 17 + 2a
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint32_t x = (dw[a] >> p) & 0x01010101u;
+        const uint32_t y = (x & 1u) | ((x & 0x100u) << 8) | ((x >> 15) & 2u) | ((x >> 7) & 0x20000u);
+        w[p] |= y << (2 * a);
+      }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) out[p * plane_words + t] = w[p];
+  }
+}
+
+template <int R, bool GROUPED, bool EXTRA>
+static hipError_t launch_r(const Args& a, unsigned tiles, size_t lds, hipStream_t s) {
+  static bool attr_set = false;  // benign race: idempotent attribute call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)bp_gemv_kernel<R, GROUPED, EXTRA>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((bp_gemv_kernel<R, GROUPED, EXTRA>), dim3(tiles), dim3(64 * kWaves), lds, s,
+                     a);
+  return hipGetLastError();
+}
+
+template <bool GROUPED, bool EXTRA>
+static hipError_t launch_g(int r, const Args& a, unsigned tiles, size_t lds, hipStream_t s) {
+  switch (r) {
+    case 1: return launch_r<1, GROUPED, EXTRA>(a, tiles, lds, s);
+    case 2: return launch_r<2, GROUPED, EXTRA>(a, tiles, lds, s);
+    case 3: return launch_r<3, GROUPED, EXTRA>(a, tiles, lds, s);
+    case 4: return launch_r<4, GROUPED, EXTRA>(a, tiles, lds, s);
+    case 5: return launch_r<5, GROUPED, EXTRA>(a, tiles, lds, s);
+    case 6: return launch_r<6, GROUPED, EXTRA>(a, tiles, lds, s);
+    case 7: return launch_r<7, GROUPED, EXTRA>(a, tiles, lds, s);
+    default: return launch_r<8, GROUPED, false>(a, tiles, lds, s);
+  }
+}
+
+}  // namespace bp
+
+hipError_t launch_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uint8_t* planes,
+                                 hipStream_t s) {
+  const int64_t total = N * (K / 32);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(bp::pack_bitplanes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes,
+                     (int)N, (int)K, planes);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_bitplanes(const uint8_t* planes, int r, bool extra, const float* alpha,
+                                 const float* zero, int64_t group, int64_t N, int64_t K,
+                                 const uint16_t* x, int64_t M, float* y, hipStream_t s) {
+  bp::Args a;
+  a.planes = planes;
+  a.alpha = alpha;
+  a.zero = zero;
+  a.x = x;
+  a.y = y;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.group = (int)group;
+  a.M = (int)M;
+  // activation chunk: at most 32 KiB of staged bf16, a multiple of 512 codes
+  int kc = (int)((16384 / M) / bp::kSuper * bp::kSuper);
+  if (kc < bp::kSuper) kc = bp::kSuper;
+  if (kc > K) kc = (int)K;
+  a.kc = kc;
+  // split of the superblocks among the waves of a row block: enough waves in
+  // flight to cover the memory latency, at least two superblocks per wave
+  const int rblocks = (int)((N + 15) / 16);
+  const int steps = (int)(K / bp::kSuper);
+  int ks = 1;
+  while (ks < bp::kWaves && rblocks * ks < 4096 && steps / (ks * 2) >= 2) ks *= 2;
+  a.ks = ks;
+  const int rbpw = bp::kWaves / ks;
+  const unsigned tiles = (unsigned)((rblocks + rbpw - 1) / rbpw);
+  const int gpc = kc / 128;
+  const size_t lds = (size_t)M * (kc + bp::kXPad) * 2 + (size_t)(2 * M * gpc + kSkinnyMaxM) * 4 +
+                     (size_t)bp::kWaves * 16 * M * 4;
+  const bool grouped = group != K;
+  const bool ex = extra && r < 8;
+  if (grouped)
+    return ex ? bp::launch_g<true, true>(r, a, tiles, lds, s)
+              : bp::launch_g<true, false>(r, a, tiles, lds, s);
+  return ex ? bp::launch_g<false, true>(r, a, tiles, lds, s)
+            : bp::launch_g<false, false>(r, a, tiles, lds, s);
+}
+
+}  // namespace mq

@@ -83,10 +83,12 @@ struct UnpackK {
   }
 };
 
+// Written in C (not inline asm) so that the compiler sees the write and keeps
+// the wait states between it and a matrix instruction that reads the result
+// or read the register before; with m and o in registers it is one
+// v_and_or_b32.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
+  return (a & m) | o;
 }
 
 // --- r = 4: one word (8 indices) -> one 8-element operand, order 0,4,1,5,2,6,3,7

@@ -86,4 +86,11 @@ hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H
 hipError_t launch_residual_rmsnorm(float* h, const float* o, const float* d, uint16_t* a,
                                    int64_t M, int64_t H, hipStream_t stream);
 
+// Bit-plane storage (bitplane.hip).
+hipError_t launch_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uint8_t* planes,
+                                 hipStream_t s);
+hipError_t launch_gemv_bitplanes(const uint8_t* planes, int r, bool extra, const float* alpha,
+                                 const float* zero, int64_t group, int64_t N, int64_t K,
+                                 const uint16_t* x, int64_t M, float* y, hipStream_t s);
+
 }  // namespace mq

@@ -115,3 +115,24 @@ def test_overflow_validation(L):
     assert L.mq_overflow_apply(P16, P16, 2, P16, 32, 4, 64, P16, 1, P16, NULL) == 4
     assert L.mq_overflow_apply(P16, P16, 2, P16, 64, 4, 64, P16, 0, P16, NULL) == 2
     assert L.mq_overflow_apply(P16, P16, 7, P16, 64, 4, 64, P16, 1, P16, NULL) == 3
+
+
+def test_bitplane_validation(L):
+    assert L.mq_bitplanes_bytes(14336, 3584) == 14336 * 3584
+    assert L.mq_bitplanes_bytes(4, 256) == 0          # K not a multiple of 512
+    assert L.mq_bitplanes_bytes(1 << 16, 65536) == 0  # more than 2^31 codes
+    assert L.mq_pack_bitplanes(NULL, 4, 512, P16, NULL) == 1
+    assert L.mq_pack_bitplanes(P16, 4, 640, P16, NULL) == 2
+    assert L.mq_pack_bitplanes(P16, 0, 512, P16, NULL) == 2
+    assert L.mq_pack_bitplanes(P16, 4, 512, P1, NULL) == 5
+
+    def gemv(p=P16, r=4, extra=0, a=P16, z=P16, g=512, N=4, K=512, x=P16, M=1, y=P16):
+        return L.mq_gemv_bitplanes(p, r, extra, a, z, g, N, K, x, M, y, NULL)
+
+    assert gemv(p=NULL) == 1
+    assert gemv(r=0) == 3 and gemv(r=9) == 3
+    assert gemv(extra=2) == 3
+    assert gemv(K=1000, g=1000) == 2
+    assert gemv(M=0) == 2 and gemv(M=9) == 2
+    assert gemv(g=64) == 4
+    assert gemv(y=P1) == 5
