@@ -18,6 +18,9 @@ from .matquant import (  # noqa: F401
     float_from_bf16_bits,
     linear,
     linear_extra_precision,
+    MLP_ACTIVATIONS,
+    mlp_activation,
+    mlp_decode,
     mixnmatch_forward,
     mixnmatch_layer,
     overflow_lists,

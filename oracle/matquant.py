@@ -483,6 +483,44 @@ def mixnmatch_forward(layers, x_bf16_bits, traces=None) -> np.ndarray:
     return h
 
 
+# --------------------------------------------------------------------------
+# Decode MLP block: up and gate from one x, the gated product, then down
+# --------------------------------------------------------------------------
+
+MLP_ACTIVATIONS = ("identity", "silu", "gelu_tanh")
+
+
+def mlp_activation(g, act: str) -> np.ndarray:
+    """The gate activation of a gated MLP, float64.
+    READING (the pages name the FFN as the main decode cost, [MQX] §5, but
+    give no block): identity (the elementwise gate of the Mix'n'Match
+    reading), SiLU g * sigmoid(g), or GELU in its tanh form
+    g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))."""
+    g = np.asarray(g, dtype=np.float64)
+    if act == "identity":
+        return g
+    if act == "silu":
+        return g / (1.0 + np.exp(-g))
+    if act == "gelu_tanh":
+        return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def mlp_decode(x_bf16_bits, up, gate, down, r: int, act: str = "identity", trace=None):
+    """y = W_down bf16(act(W_gate x) * W_up x) with every W the stored codes
+    sliced to r ([MQX] Eq. 6 and dequantization as in linear()).
+    up, gate: dicts q, alpha, zero, group of [F, H]; down: of [H, F].
+    The gated product is formed in float64 and rounded to bf16 (nearest even),
+    the precision of the activations the product takes."""
+    u = linear(x_bf16_bits, up["q"], up["alpha"], up["zero"], up["group"], r)
+    g = linear(x_bf16_bits, gate["q"], gate["alpha"], gate["zero"], gate["group"], r)
+    a_bits = bf16_bits_from_float(mlp_activation(g, act) * u)
+    y = linear(a_bits, down["q"], down["alpha"], down["zero"], down["group"], r)
+    if trace is not None:
+        trace.update(u=u, g=g, a_bits=a_bits)
+    return y
+
+
 def effective_bits(layers) -> float:
     """Average stored bits per weight of a Mix'n'Match assignment (the
     "effective bits per parameter" measure of [MQX] "Mix'n'Match")."""

@@ -522,3 +522,68 @@ def test_oracle_and_library_share_no_code():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src
+
+
+# ---------------------------------------------------------------- decode MLP block
+
+def test_mlp_activations_against_library_and_identities():
+    from scipy import special
+
+    g = np.linspace(-9.0, 9.0, 181)
+    # SiLU is g * sigmoid(g) (scipy's logistic); GELU's tanh form is within
+    # 1e-3 of the exact g * Phi(g) (scipy's erf)
+    assert np.allclose(oracle.mlp_activation(g, "silu"), g * special.expit(g), rtol=1e-13, atol=1e-15)
+    exact = 0.5 * g * (1.0 + special.erf(g / np.sqrt(2.0)))
+    assert np.max(np.abs(oracle.mlp_activation(g, "gelu_tanh") - exact)) < 1e-3
+    # both are x * (something in [0, 1]) with f(x) - f(-x) = x
+    for act in ("silu", "gelu_tanh"):
+        f = oracle.mlp_activation(g, act)
+        assert np.allclose(f - oracle.mlp_activation(-g, act), g, rtol=0, atol=1e-12)
+        assert oracle.mlp_activation(np.array([0.0]), act)[0] == 0.0
+    assert np.array_equal(oracle.mlp_activation(g, "identity"), g)
+    with pytest.raises(ValueError):
+        oracle.mlp_activation(g, "relu")
+
+
+@pytest.mark.parametrize("act", ["identity", "silu", "gelu_tanh"])
+def test_mlp_decode_constant_weights_closed_form(act):
+    # constant matrices dequantize to their constant exactly (code 0, alpha 1,
+    # z = -c), so u = c_u * sum(x), g = c_g * sum(x) in every output, and every
+    # output of down is c_d * F * bf16(act(g) * u)
+    h_dim, f_dim = 8, 24
+    rg = np.random.default_rng(9)
+    x = oracle.bf16_bits_from_float(rg.standard_normal((3, h_dim)))
+    consts = {"up": 0.375, "gate": -0.75, "down": 0.0625}
+    mats = {}
+    for name, (n, k) in {"up": (f_dim, h_dim), "gate": (f_dim, h_dim), "down": (h_dim, f_dim)}.items():
+        q, a, z = oracle.quantize_minmax(np.full((n, k), consts[name], dtype=np.float32), k)
+        mats[name] = {"q": q, "alpha": a, "zero": z, "group": k}
+    sx = oracle.float_from_bf16_bits(x).sum(axis=1, keepdims=True)
+    gv = consts["gate"] * sx
+    if act == "silu":
+        gv = gv / (1.0 + np.exp(-gv))
+    elif act == "gelu_tanh":
+        from scipy import special
+        gv = 0.5 * gv * (1.0 + np.tanh(np.sqrt(2 / np.pi) * (gv + 0.044715 * gv ** 3)))
+        assert np.allclose(gv, 0.5 * (consts["gate"] * sx) * (1 + special.erf(consts["gate"] * sx / np.sqrt(2))), atol=1e-3)
+    for r in (8, 4, 2):
+        got = oracle.mlp_decode(x, mats["up"], mats["gate"], mats["down"], r, act)
+        want = consts["down"] * f_dim * _bf16(gv * consts["up"] * sx)
+        assert got.shape == (3, h_dim)
+        assert np.allclose(got, np.broadcast_to(want, got.shape), rtol=1e-14, atol=1e-14)
+
+
+def test_mlp_decode_is_the_mixnmatch_gated_branch():
+    # with the identity activation the block is the u * g -> down branch of a
+    # Mix'n'Match layer fed the same bf16 input
+    rg = np.random.default_rng(10)
+    layer = {"r": 4}
+    for name, (n, k) in {"q": (16, 16), "k": (4, 16), "v": (4, 16), "o": (16, 16),
+                         "up": (32, 16), "gate": (32, 16), "down": (16, 32)}.items():
+        q, a, z = oracle.quantize_minmax((rg.standard_normal((n, k)) * 0.02).astype(np.float32), k)
+        layer[name] = {"q": q, "alpha": a, "zero": z, "group": k}
+    x = oracle.bf16_bits_from_float(rg.standard_normal((2, 16)))
+    tr = []
+    oracle.mixnmatch_forward([layer], x, tr)
+    y = oracle.mlp_decode(tr[0]["a_bits"], layer["up"], layer["gate"], layer["down"], 4)
+    assert np.array_equal(y, tr[0]["d"])
