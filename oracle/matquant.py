@@ -502,7 +502,12 @@ def mlp_activation(g, act: str) -> np.ndarray:
     if act == "silu":
         return g / (1.0 + np.exp(-g))
     if act == "gelu_tanh":
-        return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+        # g/2 * (1 + tanh(z)) written as g / (1 + exp(-2z)), the same function:
+        # 1 + tanh(z) cancels to 0 in float64 once tanh(z) rounds to -1
+        # (g below about -7), where the product is still about 1e-17
+        z = np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)
+        with np.errstate(over="ignore"):
+            return g / (1.0 + np.exp(-2.0 * z))
     raise ValueError(f"unknown activation {act!r}")
 
 

@@ -541,6 +541,17 @@ def test_mlp_activations_against_library_and_identities():
         assert np.allclose(f - oracle.mlp_activation(-g, act), g, rtol=0, atol=1e-12)
         assert oracle.mlp_activation(np.array([0.0]), act)[0] == 0.0
     assert np.array_equal(oracle.mlp_activation(g, "identity"), g)
+    # the tanh form of GELU as written, where it does not cancel (g > -4)
+    mid = g[g > -4.0]
+    tanh_form = 0.5 * mid * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (mid + 0.044715 * mid ** 3)))
+    assert np.allclose(oracle.mlp_activation(mid, "gelu_tanh"), tanh_form, rtol=1e-12, atol=1e-15)
+    # far below, where tanh(z) rounds to -1: 1 + tanh(z) = 2 e^(2z) (1 - e^(2z) + ...),
+    # so the value tends to g e^(2z) (not to the zero the tanh form gives in float64)
+    far = np.array([-8.0, -9.0, -10.0])
+    tail = oracle.mlp_activation(far, "gelu_tanh")
+    z = np.sqrt(2.0 / np.pi) * (far + 0.044715 * far ** 3)
+    assert np.all(1.0 + np.tanh(z) == 0.0)
+    assert np.allclose(tail, far * np.exp(2.0 * z), rtol=1e-9, atol=0)
     with pytest.raises(ValueError):
         oracle.mlp_activation(g, "relu")
 
@@ -566,6 +577,7 @@ def test_mlp_decode_constant_weights_closed_form(act):
         from scipy import special
         gv = 0.5 * gv * (1.0 + np.tanh(np.sqrt(2 / np.pi) * (gv + 0.044715 * gv ** 3)))
         assert np.allclose(gv, 0.5 * (consts["gate"] * sx) * (1 + special.erf(consts["gate"] * sx / np.sqrt(2))), atol=1e-3)
+        assert np.all(np.abs(consts["gate"] * sx) < 5)  # the tanh form has no cancellation here
     for r in (8, 4, 2):
         got = oracle.mlp_decode(x, mats["up"], mats["gate"], mats["down"], r, act)
         want = consts["down"] * f_dim * _bf16(gv * consts["up"] * sx)
