@@ -247,6 +247,8 @@ def run_rows(torch, mq, inputs, dev):
     rows["extra_precision_gemma_r2"] = run_extra(torch, mq, inputs, dev)
     # f3: bit-plane storage, one copy served at several r
     rows["bitplanes_gemma9b_mlp"] = run_bitplanes(torch, mq, inputs, dev)
+    # f4: the decode MLP block (up/gate paired, gated product in the epilogue, then down)
+    rows["mlp_decode_gemma9b"] = run_mlp(torch, mq, inputs, dev)
     return rows
 
 
@@ -317,6 +319,41 @@ def run_bitplanes(torch, mq, inputs, dev):
         out[f"r{r}" + ("_extra" if extra else "")] = {
             "us_3_launches": round(us, 2), "bytes": b, "GB/s": round(b / us / 1e3, 1),
             "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def run_mlp(torch, mq, inputs, dev):
+    """NEXT-4: the Gemma-2-9B decode MLP block (up and gate paired in one
+    launch writing bf16(u * gelu(g)), then down), batch 1, at r = 8, 4, 2."""
+    mats = {}
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=i, outlier_frac=1e-3)
+        codes, alpha, zero = mq.quantize(w, k)
+        del w
+        mats[name] = dict(codes=codes, alpha=alpha, zero=zero, N=n, K=k, group=k)
+    F, H = mats["up"]["N"], mats["up"]["K"]
+    xb = inputs.activations_bf16("gemma9b_mlp", 1, H, matrix=0)
+    x = torch.from_numpy(xb.view("int16")).to(dev)
+    y = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(mq.mlp_workspace_bytes(1, F), dtype=torch.uint8, device=dev)
+    out = {}
+    for r in RS:
+        one = sum(m["N"] * m["K"] * r // 8 for m in mats.values())
+        ncopy = max(2, -(-ROTATE_BYTES // one))
+        copies = [{nm: dict(m, packed=mq.pack(m["codes"], r)) for nm, m in mats.items()}
+                  for _ in range(ncopy)]
+
+        def run(i):
+            c = copies[i % ncopy]
+            mq.mlp_decode(c["up"], c["gate"], c["down"], r, x, act="gelu_tanh", workspace=ws,
+                          out=y)
+
+        us = time_loop(torch, run, 50)
+        b = sum(linear_bytes(m["N"], m["K"], r, m["K"], 1) for m in mats.values())
+        out[f"r{r}"] = {"us": round(us, 2), "bytes": b, "GB/s": round(b / us / 1e3, 1),
+                        "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del copies
     return out
 
 

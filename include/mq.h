@@ -281,6 +281,30 @@ mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, i
 mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, int64_t M,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode MLP block on sliced planes (the FFN, the main decode cost: the
+ * explainer's §5; a step either side of the product):
+ *   u = W_up x,  g = W_gate x              (one launch: the rows of up and
+ *                                           gate share workgroups and x)
+ *   a = bf16(u * act(g))                    (fp32 product, nearest even)
+ *   y = W_down a                            (second launch)
+ * act: 0 identity, 1 SiLU (g * sigmoid(g)), 2 GELU, tanh form.  The pages
+ * give no MLP block; this is the library's definition.
+ *   up, gate: mq_linear [F, H] (same group); down: mq_linear [H, F]; all
+ *   packed at r (r in {2, 3, 4, 6, 8}).
+ *   x bf16 bits [M, H] and y fp32 [M, H] (output), 16-byte aligned;
+ *   1 <= M <= 8.
+ *   workspace: mq_mlp_workspace_bytes(M, F) bytes, 256-byte aligned; after
+ *   the call's work it holds u and g (fp32 [M, F]) at byte offsets 0 and A
+ *   and a (bf16 [M, F]) at 2A, with A = M*F*4 rounded up to 256.
+ * Returns MQ_ERR_GROUP if up and gate differ in group.
+ */
+size_t mq_mlp_workspace_bytes(int64_t M, int64_t F);
+mq_status mq_mlp_decode(const mq_linear* up, const mq_linear* gate, const mq_linear* down, int r,
+                        int act, const uint16_t* x, int64_t M, float* y, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,7 @@ EXPORTS = (
     "mq_gemm", "mq_mixnmatch_workspace_bytes", "mq_mixnmatch_workspace_offsets",
     "mq_mixnmatch_forward", "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
     "mq_bitplanes_bytes", "mq_pack_bitplanes", "mq_gemv_bitplanes",
+    "mq_mlp_workspace_bytes", "mq_mlp_decode",
 )
 
 
@@ -104,6 +105,11 @@ def lib() -> ctypes.CDLL:
     L.mq_pack_bitplanes.argtypes = [vp, i64, i64, vp, vp]
     L.mq_gemv_bitplanes.restype = i32
     L.mq_gemv_bitplanes.argtypes = [vp, i32, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp]
+    L.mq_mlp_workspace_bytes.restype = sz
+    L.mq_mlp_workspace_bytes.argtypes = [i64, i64]
+    L.mq_mlp_decode.restype = i32
+    L.mq_mlp_decode.argtypes = [ctypes.POINTER(Linear), ctypes.POINTER(Linear),
+                                ctypes.POINTER(Linear), i32, i32, vp, i64, vp, vp, sz, vp]
     L.mq_gemv_mixed.restype = i32
     L.mq_gemv_mixed.argtypes = [ctypes.POINTER(GemvProblem), ctypes.POINTER(ctypes.c_int), i32,
                                 i64, vp]
@@ -330,6 +336,42 @@ def make_layers(layers):
                            p["N"], p["K"], p["group"])
         arr[i] = Layer(**kw)
     return arr
+
+
+MLP_ACTS = {"identity": 0, "silu": 1, "gelu_tanh": 2}
+
+
+def make_linear(p):
+    """{"packed", "alpha", "zero", "N", "K", "group"} -> a ctypes Linear."""
+    return Linear(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
+                  p["N"], p["K"], p["group"])
+
+
+def mlp_workspace_bytes(M: int, F: int) -> int:
+    return int(lib().mq_mlp_workspace_bytes(M, F))
+
+
+def mlp_decode(up, gate, down, r: int, x, act="identity", workspace=None, out=None,
+               stream=None):
+    """y = W_down bf16(W_up x * act(W_gate x)) for M <= 8 rows of bf16 x.
+    up, gate, down: dicts as for make_linear.  Returns (y fp32 [M, H],
+    workspace), the workspace holding u, g (fp32) and the bf16 product."""
+    import torch
+
+    x = _bits16(x)
+    m = x.shape[0]
+    F, H = up["N"], up["K"]
+    need = mlp_workspace_bytes(m, F)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((m, H), dtype=torch.float32, device=x.device)
+    lu, lg, ld = make_linear(up), make_linear(gate), make_linear(down)
+    _check(lib().mq_mlp_decode(ctypes.byref(lu), ctypes.byref(lg), ctypes.byref(ld), r,
+                               MLP_ACTS[act], _ptr(x), m, _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "mq_mlp_decode")
+    return out, workspace
 
 
 def mixnmatch_workspace_bytes(layer_arr, M: int) -> int:

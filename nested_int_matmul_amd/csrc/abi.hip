@@ -453,4 +453,51 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, i
   return MQ_OK;
 }
 
+// ---- decode MLP block
+
+size_t mq_mlp_workspace_bytes(int64_t M, int64_t F) {
+  if (M < 1 || M > mq::kSkinnyMaxM || F < 1) return 0;
+  return 2 * up256((size_t)(M * F * 4)) + up256((size_t)(M * F * 2));
+}
+
+mq_status mq_mlp_decode(const mq_linear* up, const mq_linear* gate, const mq_linear* down, int r,
+                        int act, const uint16_t* x, int64_t M, float* y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!up || !gate || !down || !x || !y) return MQ_ERR_NULL;
+  if (!up->packed || !up->alpha || !up->zero || !gate->packed || !gate->alpha || !gate->zero ||
+      !down->packed || !down->alpha || !down->zero)
+    return MQ_ERR_NULL;
+  if (!valid_r(r) || act < mq::kActIdentity || act > mq::kActGeluTanh) return MQ_ERR_PRECISION;
+  if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
+  const int64_t F = up->N, H = up->K;
+  if (!linear_ok(*up, F, H, r) || !linear_ok(*gate, F, H, r) || !linear_ok(*down, H, F, r))
+    return MQ_ERR_SHAPE;
+  if (up->group != gate->group) return MQ_ERR_GROUP;
+  if (!aligned16(x) || !aligned16(y)) return MQ_ERR_ALIGN;
+  const size_t need = mq_mlp_workspace_bytes(M, F);
+  if (!workspace || workspace_bytes < need) return MQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MQ_ERR_ALIGN;
+  mq_status s = check_device();
+  if (s != MQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const size_t fb = up256((size_t)(M * F * 4));
+  float* u = reinterpret_cast<float*>(ws);
+  float* g = reinterpret_cast<float*>(ws + fb);
+  uint16_t* a = reinterpret_cast<uint16_t*>(ws + 2 * fb);
+  // up and gate in one launch (rows paired in each workgroup, x read once),
+  // writing bf16(u * act(g)); then down from that bf16 copy
+  mq::SkinnyProblem p1 = prob(*up, r, x, nullptr, mq::kXBf16, u);
+  p1.packed2 = gate->packed;
+  p1.alpha2 = gate->alpha;
+  p1.zero2 = gate->zero;
+  p1.y2 = g;
+  p1.ybf = a;
+  p1.act = act;
+  s = run_mixed(&p1, 1, M, st);
+  if (s != MQ_OK) return s;
+  mq::SkinnyProblem p2 = prob(*down, r, a, nullptr, mq::kXBf16, y);
+  return run_mixed(&p2, 1, M, st);
+}
+
 }  // extern "C"

@@ -154,6 +154,19 @@ struct LoadT<3, 0> {
   }
 };
 
+// Activation of a gated MLP's gate output: identity, SiLU g * sigmoid(g), or
+// GELU in its tanh form g/2 * (1 + tanh(z)), z = sqrt(2/pi) * (g + 0.044715 g^3),
+// evaluated as g / (1 + exp(-2z)) (the same function): 1 + tanh(z) cancels
+// where tanh(z) is near -1, and in fp32 loses most of its digits there.
+__device__ __forceinline__ float gate_act(float g, int act) {
+  if (act == kActSilu) return g / (1.f + expf(-g));
+  if (act == kActGeluTanh) {
+    const float z = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+    return g / (1.f + expf(-2.f * z));
+  }
+  return g;
+}
+
 // One workgroup's share of problem pi, at slice precision R.
 template <int R, bool GROUPED>
 __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi) {
@@ -448,7 +461,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     }
   }
   if (paired && P.ybf) {
-    // bf16(first * second) for the rows of this workgroup
+    // bf16(first * act(second)) for the rows of this workgroup
     __syncthreads();
     const int half = rows_wg / 2;  // distinct rows
     for (int t = threadIdx.x; t < half * M; t += blockDim.x) {
@@ -456,7 +469,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       const int rr1 = ((j >> 4) * 2) * 16 + (j & 15), rr2 = rr1 + 16;
       const int n = (rb0 + (j >> 4)) * 16 + (j & 15);
       if (n < N) {
-        const float v = fin[rr1 * M + m] * fin[rr2 * M + m];
+        const float v = fin[rr1 * M + m] * gate_act(fin[rr2 * M + m], P.act);
         P.ybf[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
       }
     }

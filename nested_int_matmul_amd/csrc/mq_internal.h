@@ -31,13 +31,16 @@ struct SkinnyProblem {
   int tile0;     // first workgroup index of this problem
   // optional: a second matrix of the same shape, precision and scales layout
   // on the same x (its rows are computed by the same workgroups), and a
-  // bf16 copy of the output: bf16(y) alone, bf16(y * y2) for a pair
+  // bf16 copy of the output: bf16(y) alone, bf16(y * act(y2)) for a pair
   const uint8_t* packed2;
   const float* alpha2;
   const float* zero2;
   float* y2;
   uint16_t* ybf;
+  int act;       // pair only: activation of the second output (kActIdentity, ...)
 };
+
+enum GateAct { kActIdentity = 0, kActSilu = 1, kActGeluTanh = 2 };
 
 
 struct SkinnyArgs {

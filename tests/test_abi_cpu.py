@@ -136,3 +136,26 @@ def test_bitplane_validation(L):
     assert gemv(M=0) == 2 and gemv(M=9) == 2
     assert gemv(g=64) == 4
     assert gemv(y=P1) == 5
+
+
+def test_mlp_validation(L):
+    assert L.mq_mlp_workspace_bytes(1, 14336) == 2 * 57344 + 28672
+    assert L.mq_mlp_workspace_bytes(9, 64) == 0
+    lin = lambda n, k, g=None: mq.Linear(0x10000, 0x10000, 0x10000, n, k, g or k)
+    up, gate, down = lin(128, 64), lin(128, 64), lin(64, 128)
+    ws = 1 << 20
+
+    def call(u=up, g=gate, d=down, r=4, act=0, x=P16, M=1, y=P16, w=P16):
+        return L.mq_mlp_decode(ctypes.byref(u) if u else NULL, ctypes.byref(g), ctypes.byref(d),
+                               r, act, x, M, y, w, ws, NULL)
+
+    assert call(u=None) == 1
+    assert call(x=NULL) == 1
+    assert call(r=5) == 3
+    assert call(act=3) == 3
+    assert call(M=0) == 2 and call(M=9) == 2
+    assert call(d=lin(64, 64)) == 2                # down's K must be up's N
+    assert call(g=lin(128, 64, 128)) in (2, 4)     # group 128 needs K % 128 (shape) / differs from up
+    assert call(u=lin(128, 256, 128), g=lin(128, 256, 256), d=lin(256, 128)) == 4
+    assert call(w=NULL) == 6
+    assert call(y=P1) == 5
