@@ -99,38 +99,71 @@ __global__ void __launch_bounds__(64 * kRowWaves) overflow_fill_kernel(
   }
 }
 
-// y[m, n] += step * sum over row n's list of alpha[n, k / group] * x[m, k];
-// one wave per row, fixed summation order (deterministic).
-__global__ void __launch_bounds__(64 * kRowWaves) overflow_apply_kernel(
+// y[m, n] += step * sum over row n's list of alpha[n, k >> gshift] * x[m, k]
+// (gshift = 7 for groups of 128, 31 for one group per row).  One wave per
+// row (four rows per 256-thread workgroup).  A lane takes every 64th entry of
+// its row, eight at a time: the eight index loads are issued together, then
+// the eight gathers (no branch between them), so one round trip serves 512
+// entries of the row.  The 64 lanes are then summed in a fixed xor order
+// (deterministic).  Activation rows go in blocks of 8; y is read before the
+// list so that its latency overlaps.  (A runtime integer division for the
+// group index cost more than the rest of the kernel: the shift replaces it.)
+constexpr int kApplyLanes = 64;
+constexpr int kApplyRows = 256 / kApplyLanes;
+constexpr int kApplyBatch = 8;
+
+__global__ void __launch_bounds__(256) overflow_apply_kernel(
     const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
     const float* __restrict__ alpha, const uint16_t* __restrict__ x, float* __restrict__ y,
-    int N, int K, int G, int group, int M, float step) {
-  const int lane = threadIdx.x & 63;
-  for (int n = blockIdx.x * kRowWaves + (threadIdx.x >> 6); n < N; n += gridDim.x * kRowWaves) {
-    const int b = row_ptr[n], e = row_ptr[n + 1];
-    if (b == e) continue;  // wave-uniform
-    for (int m0 = 0; m0 < M; m0 += 8) {
-      float acc[8];
+    int N, int K, int G, int gshift, int M, float step) {
+  const int sub = threadIdx.x & (kApplyLanes - 1);
+  const int n = blockIdx.x * kApplyRows + (int)(threadIdx.x / kApplyLanes);
+  int b = 0, e = 0;
+  if (n < N) {
+    b = row_ptr[n];
+    e = row_ptr[n + 1];
+  }
+  const float* arow = alpha + (int64_t)(n < N ? n : 0) * G;
+  for (int m0 = 0; m0 < M; m0 += 8) {
+    // this lane's output, read before the list so that its latency overlaps
+    const bool writer = n < N && sub < 8 && m0 + sub < M;
+    float* yp = y + (int64_t)(m0 + (writer ? sub : 0)) * N + (n < N ? n : 0);
+    const float y0 = writer ? *yp : 0.f;
+    float acc[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int j = b + lane; j < e; j += 64) {
-        const int k = col_idx[j];
-        const float a = alpha[(int64_t)n * G + k / group];
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int j0 = b + sub; j0 < e; j0 += kApplyLanes * kApplyBatch) {
+      int k[kApplyBatch];
+      float w[kApplyBatch];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (m0 + q < M) acc[q] += a * bf16_to_f32(x[(int64_t)(m0 + q) * K + k]);
+      for (int u = 0; u < kApplyBatch; ++u) {
+        const int j = j0 + u * kApplyLanes;
+        k[u] = col_idx[j < e ? j : j0];  // j0 < e: a valid entry of the row
+        w[u] = j < e ? 1.f : 0.f;
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int u = 0; u < kApplyBatch; ++u) w[u] *= arow[k[u] >> gshift];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off);
-      if (lane < 8 && m0 + lane < M) {
-        float v = acc[0];
+      for (int q = 0; q < 8; ++q) {
+        if (m0 + q < M) {
+          const uint16_t* xr = x + (int64_t)(m0 + q) * K;
 #pragma unroll
-        for (int q = 1; q < 8; ++q) v = lane == q ? acc[q] : v;
-        float* yp = y + (int64_t)(m0 + lane) * N + n;
-        *yp = *yp + step * v;
+          for (int u = 0; u < kApplyBatch; ++u) acc[q] += w[u] * bf16_to_f32(xr[k[u]]);
+        }
       }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (m0 + q < M) {
+#pragma unroll
+        for (int off = kApplyLanes / 2; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off);
+      }
+    }
+    if (writer) {
+      float v = acc[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) v = sub == q ? acc[q] : v;
+      *yp = y0 + step * v;
     }
   }
 }
@@ -164,9 +197,10 @@ hipError_t launch_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int 
 hipError_t launch_overflow_apply(const int* row_ptr, const int* col_idx, int r, const float* alpha,
                                  int64_t group, int64_t N, int64_t K, const uint16_t* x,
                                  int64_t M, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(overflow_apply_kernel, dim3(row_blocks(N)), dim3(64 * kRowWaves), 0, s,
-                     row_ptr, col_idx, alpha, x, y, (int)N, (int)K, (int)(K / group), (int)group,
-                     (int)M, (float)(1 << (8 - r)));
+  const unsigned blocks = (unsigned)((N + kApplyRows - 1) / kApplyRows);
+  hipLaunchKernelGGL(overflow_apply_kernel, dim3(blocks), dim3(256), 0, s,
+                     row_ptr, col_idx, alpha, x, y, (int)N, (int)K, (int)(K / group),
+                     group == K ? 31 : 7, (int)M, (float)(1 << (8 - r)));
   return hipGetLastError();
 }
 
