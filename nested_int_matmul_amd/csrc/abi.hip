@@ -88,12 +88,10 @@ mq_status run_mixed(mq::SkinnyProblem* probs, int count, int64_t M, hipStream_t 
 mq_status gemv_products(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
                         hipStream_t stream) {
   if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
-  int n_grouped = 0;
   for (int i = 0; i < count; ++i) {
     const mq_gemv_problem& p = problems[i];
     mq_status s = check_product(p.packed, r[i], p.alpha, p.zero, p.group, p.N, p.K, p.x, p.y);
     if (s != MQ_OK) return s;
-    n_grouped += (p.group != p.K) ? 1 : 0;
   }
   mq_status s = check_device();
   if (s != MQ_OK) return s;
@@ -103,7 +101,6 @@ mq_status gemv_products(const mq_gemv_problem* problems, const int* r, int count
     probs[i] = mq::SkinnyProblem{p.packed, p.alpha, p.zero, p.x, nullptr, p.y, (int)p.N,
                                  (int)p.K, (int)p.group, mq::kXBf16, r[i], 0, 0, 0, 0};
   }
-  (void)n_grouped;
   return run_mixed(probs, count, M, stream);
 }
 
