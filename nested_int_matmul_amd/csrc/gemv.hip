@@ -330,7 +330,9 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
     for (int j = 0; j < C::DEPTH; ++j) buf[j] = LD::load(wr, loff(lo + j), loff_lo(lo + j));
     __syncthreads();
-    {
+    if constexpr (GROUPED) {
+      // per group of 128: sum of x and of offset * x (16 consecutive blocks
+      // of 8 values per group, summed across lanes)
       const int bpr = clen / PB;
       const int total = M * bpr;
       const uint32_t ones = 0x3F803F80u;
@@ -349,7 +351,6 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
           }
           if (R != 2) so = (float)Enc<R>::kOffset * s;
         }
-        // sum over the 16 consecutive blocks of one group of 128
 #pragma unroll
         for (int off = 1; off < 128 / PB; off <<= 1) {
           s += __shfl_xor(s, off);
@@ -360,25 +361,44 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
           sxos[m * g_per_chunk + kb / 128] = so;
         }
       }
-    }
-    __syncthreads();
-    if (!GROUPED) {
-      // one wave per activation row (rows strided over the waves)
-      for (int m = wave; m < M; m += kSkinnyWaves) {
+    } else {
+      // per-channel scales need only the chunk's totals per activation row:
+      // each thread sums its blocks of 8, then one reduction per row (the
+      // per-group sums and their lane shuffles are not formed at all)
+      const int bpr = clen / PB;
+      const uint32_t ones = 0x3F803F80u;
+      float* part_s = sxs;   // [waves] partial sums (sxs is free per-channel)
+      float* part_so = sxos;
+      for (int m = 0; m < M; ++m) {
         float s = 0.f, so = 0.f;
-        for (int gi = lane; gi < clen / 128; gi += 64) {
-          s += sxs[m * g_per_chunk + gi];
-          so += sxos[m * g_per_chunk + gi];
+        for (int bi = threadIdx.x; bi < bpr; bi += blockDim.x) {
+          const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + bi * PB);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            s = dot2_bf16(w4[q], ones, s);
+            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q), so);
+          }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
           s += __shfl_xor(s, off);
-          so += __shfl_xor(so, off);
+          if (R == 2) so += __shfl_xor(so, off);
         }
         if (lane == 0) {
-          sxt[m] += s;
-          sxot[m] += so;
+          part_s[wave] = s;
+          part_so[wave] = so;
         }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          float ts = 0.f, tso = 0.f;
+          for (int w = 0; w < kSkinnyWaves; ++w) {
+            ts += part_s[w];
+            tso += part_so[w];
+          }
+          sxt[m] += ts;
+          sxot[m] += (R == 2) ? tso : (float)Enc<R>::kOffset * ts;
+        }
+        __syncthreads();
       }
     }
 
