@@ -55,9 +55,9 @@ constexpr int kSkinnyWaves = 4;   // waves per workgroup
 
 template <int R>
 __device__ __forceinline__ bf16x8 unpack_op(const uint32_t* d, int i, const UnpackK& k,
-                                            const UnpackK36& k36) {
+                                            const UnpackK36& k36, const R2MConst& k2) {
   if (R == 4) return unpack_r4(d[i], k);
-  if (R == 2) return (i & 1) ? unpack_r2m<1>(d[i >> 1], k) : unpack_r2m<0>(d[i >> 1], k);
+  if (R == 2) return (i & 1) ? unpack_r2m<1>(d[i >> 1], k2) : unpack_r2m<0>(d[i >> 1], k2);
   if (R == 6) return unpack_r6(d[i], d[4 + (i >> 1)], i & 1, k36);  // 4 high, 2 low words
   if (R == 3) return unpack_r3(d[i >> 1], d[2], i, k36);             // 2 high, 1 low word
   return unpack_r8(d[2 * i], d[2 * i + 1]);
@@ -247,6 +247,8 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   const UnpackK uk = UnpackK::make();
   UnpackK36 uk36;
   if constexpr (C::SPLIT) uk36 = UnpackK36::make();
+  R2MConst uk2;
+  if constexpr (R == 2) uk2 = R2MConst::make();
   // all lanes read activations: columns past M duplicate column M - 1 (ignored)
   const int xcol = col < M ? col : M - 1;
 
@@ -347,7 +349,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             s = dot2_bf16(w4[q], ones, s);
-            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q), so);
+            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q, (kb >> 3) & 1), so);
           }
           if (R != 2) so = (float)Enc<R>::kOffset * s;
         }
@@ -361,6 +363,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
           sxos[m * g_per_chunk + kb / 128] = so;
         }
       }
+      __syncthreads();  // the streaming loop reads other threads' group sums
     } else {
       // per-channel scales need only the chunk's totals per activation row:
       // each thread sums its blocks of 8, then one reduction per row (the
@@ -376,7 +379,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             s = dot2_bf16(w4[q], ones, s);
-            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q), so);
+            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q, bi & 1), so);
           }
         }
 #pragma unroll
@@ -418,7 +421,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
             for (int i = 0; i < C::MFMAS; ++i) {
               const u32x4 w = *reinterpret_cast<const u32x4*>(xp + 8 * i);
-              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36),
+              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36, uk2),
                                                              __builtin_bit_cast(bf16x8, w), part,
                                                              0, 0, 0);
             }
@@ -443,7 +446,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
           for (int i = 0; i < C::MFMAS; ++i) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(xp + 8 * i);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36),
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36, uk2),
                                                            __builtin_bit_cast(bf16x8, w), part,
                                                            0, 0, 0);
           }

@@ -73,12 +73,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
 // literal operand, so (w & mask) | magic is one v_and_or_b32 only when mask
 // and magic sit in registers.
 struct UnpackK {
-  uint32_t m4, one4, m2, one2, m2a, one2a, m2b;
+  uint32_t m4, one4, m2, one2;
   __device__ __forceinline__ static UnpackK make() {
-    UnpackK k{0x00780078u, 0x41804180u, 0x00600060u, 0x40804080u,
-              0x00060006u, 0x42804280u, 0x00180018u};
-    asm volatile("" : "+v"(k.m4), "+v"(k.one4), "+v"(k.m2), "+v"(k.one2), "+v"(k.m2a),
-                 "+v"(k.one2a), "+v"(k.m2b));
+    UnpackK k{0x00780078u, 0x41804180u, 0x00600060u, 0x40804080u};
+    asm volatile("" : "+v"(k.m4), "+v"(k.one4), "+v"(k.m2), "+v"(k.one2));
     return k;
   }
 };
@@ -124,19 +122,28 @@ __device__ __forceinline__ bf16x8 unpack_r2(uint32_t w, const UnpackK& k) {
 template <int H>
 __device__ __forceinline__ bf16x8 unpack_r2(uint32_t w) { return unpack_r2<H>(w, UnpackK::make()); }
 
-// --- r = 2 with three magics (12 instead of 16 operations per word).  Same
-//     registers as unpack_r2; fields sitting at bits (1,2), (3,4) or (5,6) of
-//     a half after one shift use the bf16 constants 64, 16 or 4, so the
-//     operand is u = offset + t with a per-register offset: registers 0..3 of
-//     an operand (elements 2q, 2q+1) carry 64, 16, 4, 4.  The caller removes
-//     sum_k offset(k) * x[k] (R2MOffset) in fp32.
-struct R2MOffset {
-  __device__ __forceinline__ static float of_reg(int q) {  // q = register 0..3 of an operand
-    return (q & 3) == 0 ? 64.f : ((q & 3) == 1 ? 16.f : 4.f);
+// --- r = 2 with the fields read where they are stored (10 instead of 16
+//     operations per word).  In a half, field j (element 2j or 2j+1 of the
+//     word) sits at bits [2j, 2j+2).  Fields 0, 1, 2 are read in place,
+//     fields 3, 4, 5 after >> 6 and fields 6, 7 after >> 12, each then at bit
+//     p = 0, 2 or 4 of its half, under the bf16 constant 2^(7-p) (128, 32, 8),
+//     whose mantissa step at bit p is 1: the operand is u = offset + t with a
+//     per-register offset.  Registers 0..3 of the operand of elements 0..7 of
+//     the word (h = 0) carry 128, 32, 8, 128; of elements 8..15 (h = 1) 32, 8,
+//     128, 32.  The caller removes sum_k offset(k) * x[k] (R2MOffset) in fp32.
+struct R2MConst {
+  uint32_t m0, m2, m4, c128, c32, c8;
+  __device__ __forceinline__ static R2MConst make() {
+    R2MConst k{0x00030003u, 0x000C000Cu, 0x00300030u, 0x43004300u, 0x42004200u, 0x41004100u};
+    asm volatile("" : "+v"(k.m0), "+v"(k.m2), "+v"(k.m4), "+v"(k.c128), "+v"(k.c32), "+v"(k.c8));
+    return k;
   }
-  // bf16 pair (offset, offset) of register q, for v_dot2 sums
-  __device__ __forceinline__ static uint32_t pair_bits(int q) {
-    return (q & 3) == 0 ? 0x42804280u : ((q & 3) == 1 ? 0x41804180u : 0x40804080u);
+};
+struct R2MOffset {
+  // bf16 pair (offset, offset) of register q of half h, for v_dot2 sums
+  __device__ __forceinline__ static uint32_t pair_bits(int q, int h) {
+    const int p = h ? (q == 2 ? 0 : (q == 1 ? 4 : 2)) : (q == 0 || q == 3 ? 0 : (q == 1 ? 2 : 4));
+    return p == 0 ? 0x43004300u : (p == 2 ? 0x42004200u : 0x41004100u);
   }
 };
 
@@ -146,20 +153,20 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 template <int H>
-__device__ __forceinline__ bf16x8 unpack_r2m(uint32_t w, const UnpackK& k) {
-  if (H == 0) {
-    const uint32_t w1 = w << 1;
-    uint32_t p0 = and_or(w1, k.m2a, k.one2a);
-    uint32_t p1 = and_or(w1, k.m2b, k.one4);
-    uint32_t p2 = and_or(w1, k.m2, k.one2);
-    uint32_t p3 = and_or(w >> 1, k.m2, k.one2);
+__device__ __forceinline__ bf16x8 unpack_r2m(uint32_t w, const R2MConst& k) {
+  const uint32_t w6 = w >> 6;
+  if (H == 0) {  // elements 0..7: fields 0, 1, 2 in place, field 3 from w >> 6
+    uint32_t p0 = and_or(w, k.m0, k.c128);
+    uint32_t p1 = and_or(w, k.m2, k.c32);
+    uint32_t p2 = and_or(w, k.m4, k.c8);
+    uint32_t p3 = and_or(w6, k.m0, k.c128);
     return as_bf16x8(p0, p1, p2, p3);
-  } else {
-    const uint32_t w2 = w >> 7;
-    uint32_t p0 = and_or(w2, k.m2a, k.one2a);
-    uint32_t p1 = and_or(w2, k.m2b, k.one4);
-    uint32_t p2 = and_or(w2, k.m2, k.one2);
-    uint32_t p3 = and_or(w >> 9, k.m2, k.one2);
+  } else {       // elements 8..15: fields 4, 5 from w >> 6, fields 6, 7 from w >> 12
+    const uint32_t w12 = w >> 12;
+    uint32_t p0 = and_or(w6, k.m2, k.c32);
+    uint32_t p1 = and_or(w6, k.m4, k.c8);
+    uint32_t p2 = and_or(w12, k.m0, k.c128);
+    uint32_t p3 = and_or(w12, k.m2, k.c32);
     return as_bf16x8(p0, p1, p2, p3);
   }
 }

@@ -127,6 +127,29 @@ def test_mlp_decode_matches_separate_products():
     compare(y, y2.double().cpu().numpy(), "fused vs separate y")
 
 
+@pytest.mark.parametrize("r", [2, 4, 8])
+def test_mlp_decode_grouped_repeated_identical(r):
+    """The paired up/gate launch at group 128, 20 times: every intermediate
+    and the output bit-identical to the first call (fixed order), the first
+    call's up output against the oracle."""
+    H, F, M = 1536, 512, 2
+    note(f"mlp repeated r={r}")
+    host, devm = _mats(H, F, 128, r, workload="mistral_small")
+    xb = inputs.activations_bf16("mistral_small", M, H, matrix=12, heavy_channels=8)
+    x = x_device(xb)
+    y0, ws0 = mq.mlp_decode(devm["up"], devm["gate"], devm["down"], r, x, act="silu")
+    torch.cuda.synchronize()
+    u0 = ws0.clone()
+    p = host["up"]
+    u, _, _ = _split_workspace(ws0, M, F)
+    compare(u, oracle.linear(xb, p["q"], p["alpha"], p["zero"], p["group"], r), f"mlp repeated up r{r}")
+    for i in range(20):
+        y, ws = mq.mlp_decode(devm["up"], devm["gate"], devm["down"], r, x, act="silu")
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0), f"call {i}: output differs"
+        assert torch.equal(ws, u0), f"call {i}: intermediates differ"
+
+
 def test_mlp_decode_error_enqueues_nothing():
     H, F, r = 256, 512, 4
     host, devm = _mats(H, F, "K", r)

@@ -204,6 +204,32 @@ def test_gemv_deterministic():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("r", [2, 4, 8, 6])
+def test_gemv_grouped_repeated_launches_identical(r):
+    """Group-128 scales read per-group activation sums that other threads of
+    the workgroup write to LDS.  40 launches, single and grouped, must be
+    bit-identical to the first (the kernel's order is fixed), and the first
+    must match the oracle.  Regression test for a missing barrier between
+    those writes and the reads."""
+    note(f"gemv grouped repeated r={r}")
+    n, k = 520, 1536
+    m = quantized("mistral_small", n, k, 128, matrix=9)
+    xb = inputs.activations_bf16("mistral_small", 3, k, matrix=9, heavy_channels=8)
+    x = x_device(xb)
+    plane = mq.pack(m["q_d"], r)
+    y0 = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x)
+    torch.cuda.synchronize()
+    compare(y0, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 128, r), f"grouped r{r}")
+    lin = dict(packed=plane, alpha=m["alpha_d"], zero=m["zero_d"], N=n, K=k, group=128, x=x)
+    for i in range(40):
+        y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x)
+        y2, y3 = torch.empty_like(y), torch.empty_like(y)
+        mq.gemv_grouped([dict(lin, y=y2), dict(lin, y=y3)], r, 3)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0), f"launch {i} differs"
+        assert torch.equal(y2, y0) and torch.equal(y3, y0), f"grouped launch {i} differs"
+
+
 def test_error_enqueues_nothing():
     note("error path")
     m = quantized("tiny_linear", 64, 512, 512)
