@@ -18,13 +18,16 @@
 //    activation columns (only the first M are non-zero), fp32 accumulation.
 //  - The activations are staged once per workgroup in LDS as stored (the
 //    plane layout makes unpacked operands come out in natural k order), in
-//    chunks of `kc` codes; the same pass forms the per-128 sums of x and of
-//    offset * x used by the zero-point and encoding-offset terms.
+//    chunks of `kc` codes; the same pass forms the sums of x and of
+//    offset * x used by the zero-point and encoding-offset terms: per group
+//    of 128 for group-128 scales, only the chunk's totals per activation row
+//    for per-channel scales.
 //  - alpha, 2^(8-r) and the zero point are applied in fp32: per group of 128
 //    when group == 128, once at the end for per-channel scales (whose alpha
 //    and z are fetched at kernel start).
-//  - Waves that share a row block split K; their partial results are summed
-//    in LDS in a fixed order (deterministic), then written as fp32.
+//  - Waves that share a row block split K (while each keeps at least 16 load
+//    steps); their partial results are summed in LDS in a fixed order
+//    (deterministic), then written as fp32.
 //  - One launch can carry up to 16 independent problems (grouped GEMV), each
 //    at its own r; a problem may pair two matrices of one shape that share x
 //    (alternate row blocks of a workgroup), which can also write bf16 of the
