@@ -13,8 +13,8 @@
 //  - each K iteration covers 64 codes: the activation tile (256 x 64 bf16) and
 //    the packed weight tile (256 rows x 64 codes) are brought into LDS with
 //    buffer-to-LDS loads, double-buffered, one barrier per iteration; the
-//    activation tile is XOR-swizzled in 16-byte chunks so that the operand
-//    reads of 8 consecutive rows hit distinct banks;
+//    activation and weight tiles are XOR-swizzled in 16-byte chunks so that
+//    the operand reads of 16 consecutive rows hit distinct banks;
 //  - one accumulator set carries all groups: at the end of group g it holds
 //    C_g = P_g + (running total) / a_g in units of 1/a_g (a_g = alpha * 2^(8-r));
 //    the group's zero-point term is subtracted in those units and the set is
@@ -41,6 +41,18 @@ struct Cfg {
   static constexpr int WT_BYTES = BN * WROW;
   static constexpr int LDS = 2 * XT_BYTES + 2 * WT_BYTES + BM * 4;
 };
+
+// LDS swizzles (16-byte chunks).  Operand reads serve 16 lanes per cycle
+// (256 bytes); both swizzles keep those lanes on distinct banks, and also the
+// 8-lane groups of a 128-byte cycle.
+//  - activations, row r (128 bytes): logical chunk c sits at c ^ xsw(r);
+//  - packed weights, row r (WROW bytes = 2 or 4 chunks at r = 4, 8): chunk c
+//    sits at c ^ wsw(r) (r = 2 rows are one chunk: no swizzle).
+__device__ __forceinline__ int xsw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <int R>
+__device__ __forceinline__ int wsw(int r) {
+  return R == 4 ? ((r >> 2) ^ (r >> 3)) & 1 : R == 8 ? ((r >> 1) ^ (r >> 2)) & 3 : 0;
+}
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -84,7 +96,7 @@ __global__ void __launch_bounds__(THREADS)
     for (int q = 0; q < BM * 128 / 1024 / WAVES; ++q) {
       const int rb = (wave * (BM * 128 / 1024 / WAVES) + q) * 8;  // first row of this piece
       const int row = rb + (lane >> 3);
-      const int c = (lane & 7) ^ (row & 7);                       // logical 16-byte chunk
+      const int c = (lane & 7) ^ xsw(row);                        // logical 16-byte chunk
       const int m = m0 + row;
       const uint32_t off = m < M ? (uint32_t)(((int64_t)m * K + k0 + c * 8) * 2) : 0x80000000u;
       lds_dma16(xr, xs + rb * 128, off);
@@ -93,7 +105,8 @@ __global__ void __launch_bounds__(THREADS)
     constexpr int WPIECES = C::WT_BYTES / 1024;
     for (int q = wave; q < WPIECES; q += WAVES) {
       const int byte = q * 1024 + lane * 16;
-      const int row = byte / C::WROW, col = byte % C::WROW;
+      const int row = byte / C::WROW;
+      const int col = (((byte % C::WROW) >> 4) ^ wsw<R>(row)) << 4;  // logical chunk held here
       const int n = n0 + row;
       const uint32_t off =
           n < N ? (uint32_t)n * (uint32_t)rowbytes + (uint32_t)(k0 * R / 8 + col) : 0x80000000u;
@@ -122,8 +135,9 @@ __global__ void __launch_bounds__(THREADS)
   auto scale = [&](int j, int g) -> float { return alpha[(int64_t)nld[j] * G + g]; };
   auto zraw = [&](int j, int g) -> float { return zero[(int64_t)nld[j] * G + g]; };
 
-  // row sums of x: thread (row = tid / 2, half = tid % 2) sums 32 codes per iteration
-  const int srow = tid >> 1, shalf = tid & 1;
+  // row sums of x: thread (row = 32 * wave + lane % 32, half = lane / 32)
+  // sums 32 codes per iteration
+  const int srow = wave * 32 + (lane & 31), shalf = lane >> 5;
   float srun = 0.f;
   const uint32_t ones = 0x3F803F80u;
 
@@ -171,12 +185,11 @@ __global__ void __launch_bounds__(THREADS)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const int c = shalf * 4 + c4;
-          const u32x4 w =
-              *reinterpret_cast<const u32x4*>(xs + srow * 128 + ((c ^ (srow & 7)) * 16));
+          const u32x4 w = *reinterpret_cast<const u32x4*>(xs + srow * 128 + ((c ^ xsw(srow)) * 16));
 #pragma unroll
           for (int e = 0; e < 4; ++e) sp = dot2_bf16(w[e], ones, sp);
         }
-        sp += __shfl_xor(sp, 1);
+        sp += __shfl_xor(sp, 32);
         srun += sp;
         if (GROUPED && it2 == IPG - 1) {
           if (shalf == 0) sxg[srow] = srun;
@@ -192,14 +205,16 @@ __global__ void __launch_bounds__(THREADS)
       uint32_t wv[NB][R];  // this lane's packed bytes of the iteration (4R bytes) per n-block
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const unsigned char* p = ws + (wn * 64 + j * 32 + l32) * C::WROW + s * (4 * R);
+        const int wrow = wn * 64 + j * 32 + l32;
+        const unsigned char* p = ws + wrow * C::WROW;
         if (R == 2) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+          const u32x2 v = *reinterpret_cast<const u32x2*>(p + s * 8);
           wv[j][0] = v[0]; wv[j][1] = v[1];
         } else {
 #pragma unroll
           for (int h = 0; h < R / 4; ++h) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * h);
+            const int c = s * (R / 4) + h;  // logical chunk
+            const u32x4 v = *reinterpret_cast<const u32x4*>(p + ((c ^ wsw<R>(wrow)) << 4));
             wv[j][4 * h + 0] = v[0]; wv[j][4 * h + 1] = v[1];
             wv[j][4 * h + 2] = v[2]; wv[j][4 * h + 3] = v[3];
           }
@@ -212,8 +227,7 @@ __global__ void __launch_bounds__(THREADS)
         for (int i = 0; i < MB; ++i) {
           const int row = wm * 128 + i * 32 + l32;
           const int c = 4 * s + kk;
-          const u32x4 v =
-              *reinterpret_cast<const u32x4*>(xs + row * 128 + ((c ^ (row & 7)) * 16));
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 128 + ((c ^ xsw(row)) * 16));
           a[i] = __builtin_bit_cast(bf16x8, v);
         }
 #pragma unroll
