@@ -23,22 +23,24 @@
 //  - The index t = h + c is formed bit-sliced on whole words (32 codes per
 //    operation): a ripple carry through the h planes, with c dropped where h
 //    is all ones unless the unclamped slice is asked for.
-//  - Word G of a lane covers 32 codes of group G (128 codes); the four lanes
+//  - Word G of a lane covers 32 codes of group G (128 codes); the four lane
 //    slots together cover the group, so one v_mfma_f32_16x16x32_bf16 never
-//    mixes groups.  Bit i and bit 16 + i of a t-plane word j are moved to
-//    mantissa bit e in {4, 5, 6} and OR-ed under the exponent of
-//    2^(7 - e + j): an exact bf16 equal to 2^(7-e+j) + 2^j * bit.  All planes
-//    of a group accumulate into one fp32 accumulator that starts at minus the
-//    group's total offset (sum over planes and codes of 2^(7-e+j) * x), so it
-//    holds the group's sum of x * t; the small positions e keep the offset,
-//    and so the fp32 rounding, small.  At the group's end it is folded into
-//    the row total (with the group's alpha and z when group = 128).
+//    mixes groups.  The t-planes become exact bf16 operands by a bit
+//    transpose: delta swaps turn planes 0-3 (and 4-7 when present) into
+//    4-bit indices, nibble q of word a holding the code at word position
+//    4q + a (codes 8q + 2a and 8q + 2a + 1 of the 32 for nibbles q and
+//    q + 4).  Low nibbles go on mantissa bits 3..6 under bf16 16 (u = 16 + n),
+//    high nibbles under bf16 256 (u = 256 + 16 n).  Operand a pairs with
+//    activation dwords 4q + a, so four products (eight above four planes)
+//    cover the 32 codes whatever r is.
+//    A group's products accumulate into one fp32 accumulator that starts at
+//    minus the group's offset (16 or 272 times the group's sum of x), so it
+//    holds the group's sum of x * t; at the group's end it is folded into the
+//    row total (with the group's alpha and z when group = 128).
 //  - Activations are staged in LDS in natural order (buffer-to-LDS loads);
-//    the same pass forms, per group of 128, the sum of x and the offset sum.
+//    the same pass forms the sum of x per group of 128.
 //  - Waves that share a row block split the superblocks; their results are
 //    summed in LDS in a fixed order (deterministic).
-#include <utility>
-
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -55,40 +57,42 @@ struct Bp {
   static constexpr int FIRST = R < 8 ? 7 - R : 0;                // lowest plane read
   static constexpr int PT = R < 8 ? (EXTRA ? R + 1 : R) : 8;     // planes of t
   static constexpr int DEPTH = PL <= 2 ? 4 : (PL <= 3 ? 3 : 2);  // superblocks in flight
-  static constexpr float WTOT = (float)((1 << PT) - 1);          // sum of plane weights 2^j
   static constexpr float STEP = (float)(1 << (8 - R));           // 2^(8-r)
 };
-
-// Word bit i (and 16 + i) is shifted right by bit_shift(i) (left if negative)
-// onto mantissa bit bit_pos(i) in {4, 5, 6} of the low (high) bf16 half.
-__host__ __device__ constexpr int bit_shift(int i) {
-  return i == 0 ? -4 : i < 4 ? -3 : i < 7 ? 0 : i < 10 ? 3 : i < 13 ? 6 : 9;
-}
-__host__ __device__ constexpr int bit_pos(int i) { return i - bit_shift(i); }
-
-template <int I>
-__device__ __forceinline__ uint32_t shifted(uint32_t w) {
-  constexpr int s = bit_shift(I);
-  if constexpr (s >= 0) return w >> s;
-  else return w << (-s);
-}
 
 // (w & mask) | magic, written in C so that the compiler sees every write and
 // keeps the wait states the matrix cores need between an operand's last
 // write and its read (and between that read and the operand's next write).
-// The mask sits in a vector register and the magic is a constant, so the pair
-// forms one v_and_or_b32 with the magic in a scalar register.
+// With mask and magic in vector registers the pair is one v_and_or_b32.
 __device__ __forceinline__ uint32_t and_or_c(uint32_t w, uint32_t m, uint32_t o) {
   return (w & m) | o;
 }
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
+// Delta swap: the bit blocks of width s at odd block positions of a trade
+// places with the blocks at even positions of b.
+__device__ __forceinline__ void delta_swap(uint32_t& a, uint32_t& b, int sh, uint32_t m) {
+  const uint32_t d = ((a >> sh) ^ b) & m;
+  b ^= d;
+  a ^= d << sh;
 }
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
+
+// Four bit-sliced words (bit p of word j = bit j of the index of the code at
+// word position p) -> four words of 4-bit indices: nibble q of word a holds
+// the index bits of the code at position 4q + a.
+__device__ __forceinline__ void transpose4(uint32_t& w0, uint32_t& w1, uint32_t& w2,
+                                           uint32_t& w3) {
+  delta_swap(w0, w1, 1, 0x55555555u);
+  delta_swap(w2, w3, 1, 0x55555555u);
+  delta_swap(w0, w2, 2, 0x33333333u);
+  delta_swap(w1, w3, 2, 0x33333333u);
+}
+
+// Nibbles q and q + 4 of w on mantissa bits 3..6 of the two halves under the
+// bf16 constant `one` (16: unit 1, u = 16 + n; 256: unit 16, u = 256 + 16 n),
+// for q = 0..3: both exact.
+__device__ __forceinline__ bf16x8 nibble_operand(uint32_t w, uint32_t m4, uint32_t one) {
+  return as_bf16x8(and_or_c(w << 3, m4, one), and_or_c(w >> 1, m4, one),
+                   and_or_c(w >> 5, m4, one), and_or_c(w >> 9, m4, one));
 }
 
 struct Args {
@@ -114,8 +118,7 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
   const int gpc = kc / 128;  // groups per chunk
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                       // [M][xstride]
   float* sxs = reinterpret_cast<float*>(smem + (size_t)M * xstride * 2);  // [M][gpc] sum of x
-  float* sxos = sxs + M * gpc;           // [M][gpc] sum of 2^(7 - e) x
-  float* sxt = sxos + M * gpc;           // [M] total of x
+  float* sxt = sxs + M * gpc;            // [M] total of x
   float* red = sxt + kSkinnyMaxM;        // [kWaves * 16][M]
 
   const uint32_t rowb = (uint32_t)K / 8;
@@ -145,12 +148,9 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
   }
   if (threadIdx.x < kSkinnyMaxM) sxt[threadIdx.x] = 0.f;
 
-  // masks of mantissa bits 4, 5, 6 in both halves, held in vector registers
-  uint32_t mk4 = 0x00100010u, mk5 = 0x00200020u, mk6 = 0x00400040u;
-  asm volatile("" : "+v"(mk4), "+v"(mk5), "+v"(mk6));
-  auto mask_of = [&](int e) __attribute__((always_inline)) {
-    return e == 4 ? mk4 : (e == 5 ? mk5 : mk6);
-  };
+  // nibble operands: mask of mantissa bits 3..6 and the bf16 constants 16, 256
+  uint32_t m4n = 0x00780078u, one16 = 0x41804180u, one256 = 0x43804380u;
+  asm volatile("" : "+v"(m4n), "+v"(one16), "+v"(one256));
 
   const int xcol = col < M ? col : M - 1;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x, (uint32_t)((int64_t)M * K * 2));
@@ -192,37 +192,25 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
         buf[d][pl] = buf_load16(pr, o == 0x80000000u ? o : o + (uint32_t)pl * plane_bytes);
       }
     __syncthreads();
-    // ---- per group of 128: sum of x and sum of 2^(7 - e(k)) x, where
-    //      e(k) = bit_pos(((k mod 32) >> 1)) is the mantissa bit of code k
+    // ---- per group of 128: sum of x
     {
       const int bpr = clen / 8;
       const int total = M * bpr;
       const uint32_t ones = 0x3F803F80u;
       for (int b0 = 0; b0 < total; b0 += blockDim.x) {
         const int b = b0 + threadIdx.x;
-        float s = 0.f, so = 0.f;
+        float s = 0.f;
         int m = 0, kb = 0;
         if (b < total) {
           m = b / bpr;
           kb = (b - m * bpr) * 8;
           const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + kb);
-          const int i0 = (kb & 31) >> 1;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float pair = dot2_bf16(w4[q], ones, 0.f);
-            s += pair;
-            so += (float)(1 << (7 - bit_pos(i0 + q))) * pair;
-          }
+          for (int q = 0; q < 4; ++q) s += dot2_bf16(w4[q], ones, 0.f);
         }
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          s += __shfl_xor(s, off);
-          so += __shfl_xor(so, off);
-        }
-        if (b < total && (kb % 128) == 0) {
-          sxs[m * gpc + kb / 128] = s;
-          sxos[m * gpc + kb / 128] = so;
-        }
+        for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
+        if (b < total && (kb % 128) == 0) sxs[m * gpc + kb / 128] = s;
       }
     }
     __syncthreads();
@@ -268,31 +256,40 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
               if constexpr (EXTRA) t[R] = cy;
             }
             const int gl = st * 4 + Gi;  // group in the chunk
-            const float so = sxos[xcol * gpc + gl];
+            const uint16_t* xp = xrow + st * kSuper + Gi * 128;
+            // the t-planes transposed into 4-bit indices (planes 0-3, and
+            // 4-7 when there are more than four): word a then holds, in
+            // nibbles q and q + 4, the codes of word positions 4q + a and
+            // 4q + 16 + a, i.e. codes 8q + 2a and 8q + 2a + 1 of the 32.
+            // Operand a pairs them with activation dwords 4q + a.
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              lo[j] = j < C::PT ? t[j] : 0u;
+              hi[j] = j + 4 < C::PT ? t[j + 4] : 0u;
+            }
+            transpose4(lo[0], lo[1], lo[2], lo[3]);
+            if constexpr (C::PT > 4) transpose4(hi[0], hi[1], hi[2], hi[3]);
+            // u = 16 + (t & 15) [+ 256 + 16 (t >> 4)]: start at minus the offsets
+            const float gsx = sxs[xcol * gpc + gl];
+            const float off = C::PT > 4 ? 272.f : 16.f;
             f32x4 part;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part[i] = -C::WTOT * so;
-            const uint16_t* xp = xrow + st * kSuper + Gi * 128;
-            static_for<4>([&](auto mu) __attribute__((always_inline)) {
-              const u32x4 xv = *reinterpret_cast<const u32x4*>(xp + 8 * mu.value);
-              static_for<C::PT>([&](auto jc) __attribute__((always_inline)) {
-                constexpr int j = decltype(jc)::value;
-                constexpr int i0 = 4 * decltype(mu)::value;
-                uint32_t a[4];
-                static_for<4>([&](auto qc) __attribute__((always_inline)) {
-                  constexpr int i = i0 + decltype(qc)::value;
-                  constexpr int e = bit_pos(i);
-                  constexpr uint32_t mag = (uint32_t)((134 - e + j) << 7) * 0x00010001u;
-                  a[decltype(qc)::value] = and_or_c(shifted<i>(t[j]), mask_of(e), mag);
-                });
-                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[0], a[1], a[2], a[3]),
-                                                               __builtin_bit_cast(bf16x8, xv),
-                                                               part, 0, 0, 0);
-              });
-            });
+            for (int i = 0; i < 4; ++i) part[i] = -off * gsx;
+            u32x4 xv[4];
+#pragma unroll
+            for (int mu = 0; mu < 4; ++mu) xv[mu] = *reinterpret_cast<const u32x4*>(xp + 8 * mu);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const bf16x8 xa = as_bf16x8(xv[0][a], xv[1][a], xv[2][a], xv[3][a]);
+              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nibble_operand(lo[a], m4n, one16),
+                                                             xa, part, 0, 0, 0);
+              if constexpr (C::PT > 4)
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    nibble_operand(hi[a], m4n, one256), xa, part, 0, 0, 0);
+            }
             if constexpr (GROUPED) {
               const int g = ck0 / 128 + gl;
-              const float gsx = sxs[xcol * gpc + gl];
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int n = row0 + 4 * slot + i;
@@ -444,7 +441,7 @@ hipError_t launch_gemv_bitplanes(const uint8_t* planes, int r, bool extra, const
   const int rbpw = bp::kWaves / ks;
   const unsigned tiles = (unsigned)((rblocks + rbpw - 1) / rbpw);
   const int gpc = kc / 128;
-  const size_t lds = (size_t)M * (kc + bp::kXPad) * 2 + (size_t)(2 * M * gpc + kSkinnyMaxM) * 4 +
+  const size_t lds = (size_t)M * (kc + bp::kXPad) * 2 + (size_t)(M * gpc + kSkinnyMaxM) * 4 +
                      (size_t)bp::kWaves * 16 * M * 4;
   const bool grouped = group != K;
   const bool ex = extra && r < 8;
