@@ -162,7 +162,7 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
  * mq_gemm: the same product for any number of activation rows M >= 1 (small
  * batches and prefill), on bf16 matrix cores with fp32 accumulation.  Same
  * definitions and layouts as mq_gemv; M <= 8 takes the mq_gemv kernel.
- * r = 3 and r = 6 are served for M <= 8 only (MQ_ERR_PRECISION above).
+ * r = 3 and r = 6 are served for M <= 64 (MQ_ERR_PRECISION above).
  *   workspace  device scratch of at least mq_gemm_workspace_bytes(M, N, K, group)
  *              bytes (may be NULL when that is 0), 256-byte aligned
  * Sizes: M >= 1, N >= 1, K >= 64, K % 64 == 0, K <= 65536.

@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t) {
-  return (M > kSkinnyMaxM && M <= 64) ? panel_workspace_bytes(M, N, K) : 0;
+  return (M > kSkinnyMaxM && M <= kPanelMaxM) ? panel_workspace_bytes(M, N, K) : 0;
 }
 
 template <int R, int MB, int NB, int WM, int WN>
@@ -267,7 +267,7 @@ static hipError_t launch_r(const uint8_t* packed, const float* alpha, const floa
 hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                        int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        void* workspace, hipStream_t s) {
-  if (M <= 64)
+  if (M <= kPanelMaxM)
     return launch_gemm_panel(packed, r, alpha, zero, group, N, K, x, M, y, workspace, s);
   if (M >= 256) return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, s);
   switch (r) {

@@ -13,6 +13,8 @@
 //    straight into registers (no LDS for weights: every row has one reader),
 //    DEPTH steps ahead of use, and unpacks them into exact bf16 integers
 //    (mq_device.h).  One unpacked operand feeds MB matrix-core products.
+//    r = 3 and 6 (a high-bit and a low-bit plane) take 32 codes per lane per
+//    step from both planes and assemble u = 128 + t in the same registers.
 //  - alpha and z of the panel's groups are staged in LDS with the
 //    activations; group-128 scales are applied at each group end in fp32
 //    (y += alpha 2^(8-r) P_g - alpha (z + shift) sum_g x), per-channel scales
@@ -35,10 +37,15 @@ constexpr int DEPTH = 8;          // weight loads in flight per lane
 
 template <int R>
 struct Pc {
-  static constexpr int CPL = 16 * 8 / R;    // codes per lane per step (16 bytes)
+  // r = 3 and 6: a high-bit and a low-bit plane (rows of the high plane, then
+  // rows of the low plane), 32 codes per lane per step from each
+  static constexpr bool SPLIT = (R == 3 || R == 6);
+  static constexpr int RL = R == 6 ? 2 : 1, RH = R - RL;  // split: plane widths
+  static constexpr int CPL = SPLIT ? 32 : 16 * 8 / R;    // codes per lane per step
   static constexpr int STEP = 2 * CPL;      // codes per row per step (two lane slots)
   static constexpr int MFMAS = CPL / 8;     // 16-deep products per step per m-block
   static constexpr int SPG = 128 / STEP;    // steps per group of 128
+  using LD = LoadT<R, SPLIT ? 0 : 16>;      // one lane's loads of a step
 };
 
 struct Args {
@@ -57,9 +64,12 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
 }
 
 template <int R>
-__device__ __forceinline__ bf16x8 unpack_b(const uint32_t* d, int i, const UnpackK& k) {
+__device__ __forceinline__ bf16x8 unpack_b(const uint32_t* d, int i, const UnpackK& k,
+                                           const UnpackK36& k36) {
   if (R == 4) return unpack_r4(d[i], k);
   if (R == 2) return (i & 1) ? unpack_r2<1>(d[i >> 1], k) : unpack_r2<0>(d[i >> 1], k);
+  if (R == 6) return unpack_r6(d[i], d[4 + (i >> 1)], i & 1, k36);  // 4 high, 2 low words
+  if (R == 3) return unpack_r3(d[i >> 1], d[2], i, k36);             // 2 high, 1 low word
   return unpack_r8(d[2 * i], d[2 * i + 1]);
 }
 
@@ -127,14 +137,25 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   }
 
   // ---- first DEPTH weight loads (behind the staging loads)
-  const uint32_t row_off = n < N ? (uint32_t)n * (uint32_t)rowbytes : plane;
-  const uint32_t base_off = row_off + (uint32_t)((k0 + s * C::CPL) * R / 8);
+  // split planes: the lane's high-plane bytes, and its low-plane bytes after
+  // all N rows of the high plane
+  constexpr int WH = C::SPLIT ? C::RH : R;  // bits per code in the (high) plane
+  const uint32_t hrow = (uint32_t)(K * WH / 8), lrow = (uint32_t)(K * C::RL / 8);
+  const uint32_t row_off = n < N ? (uint32_t)n * hrow : plane;
+  const uint32_t base_off = row_off + (uint32_t)((k0 + s * C::CPL) * WH / 8);
+  const uint32_t base_lo = n < N ? (uint32_t)N * hrow + (uint32_t)n * lrow +
+                                       (uint32_t)((k0 + s * C::CPL) * C::RL / 8)
+                                 : plane;
   auto loff = [&](int st) -> uint32_t {
-    return st < steps ? base_off + (uint32_t)(st * (C::STEP * R / 8)) : 0x80000000u;
+    return st < steps ? base_off + (uint32_t)(st * (C::STEP * WH / 8)) : 0x80000000u;
   };
-  u32x4 buf[DEPTH];
+  auto loff_lo = [&](int st) -> uint32_t {
+    return st < steps ? base_lo + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
+  };
+  using LD = typename C::LD;
+  typename LD::T buf[DEPTH];
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) buf[j] = buf_load16(wr, loff(j));
+  for (int j = 0; j < DEPTH; ++j) buf[j] = LD::load(wr, loff(j), loff_lo(j));
 
   if (GROUPED) {
 #pragma unroll
@@ -167,6 +188,8 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
 
   // ---- stream the slice
   const UnpackK uk = UnpackK::make();
+  UnpackK36 uk36;
+  if constexpr (C::SPLIT) uk36 = UnpackK36::make();
   f32x16 acc[MB], part[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -200,11 +223,12 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
     for (int j = 0; j < DEPTH; ++j) {
       const int st = base + j;
       if (st < steps) {
-        const uint32_t d[4] = {buf[j][0], buf[j][1], buf[j][2], buf[j][3]};
+        uint32_t d[LD::NW];
+        LD::words(buf[j], d);
         const uint16_t* xp = xa + st * C::STEP;
 #pragma unroll
         for (int i = 0; i < C::MFMAS; ++i) {
-          const bf16x8 b = unpack_b<R>(d, i, uk);
+          const bf16x8 b = unpack_b<R>(d, i, uk, uk36);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             const u32x4 v =
@@ -228,7 +252,7 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
         }
       }
       // refill this slot after its last use
-      buf[j] = buf_load16(wr, loff(st + DEPTH));
+      buf[j] = LD::load(wr, loff(st + DEPTH), loff_lo(st + DEPTH));
     }
   }
 
@@ -349,10 +373,18 @@ hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, c
     case 9: e = launch_panel_t<2, 1, true>(a, p, s); break;
     case 10: e = launch_panel_t<2, 2, false>(a, p, s); break;
     case 11: e = launch_panel_t<2, 2, true>(a, p, s); break;
+    case 12: e = launch_panel_t<3, 1, false>(a, p, s); break;
+    case 13: e = launch_panel_t<3, 1, true>(a, p, s); break;
+    case 14: e = launch_panel_t<3, 2, false>(a, p, s); break;
+    case 15: e = launch_panel_t<3, 2, true>(a, p, s); break;
     case 16: e = launch_panel_t<4, 1, false>(a, p, s); break;
     case 17: e = launch_panel_t<4, 1, true>(a, p, s); break;
     case 18: e = launch_panel_t<4, 2, false>(a, p, s); break;
     case 19: e = launch_panel_t<4, 2, true>(a, p, s); break;
+    case 24: e = launch_panel_t<6, 1, false>(a, p, s); break;
+    case 25: e = launch_panel_t<6, 1, true>(a, p, s); break;
+    case 26: e = launch_panel_t<6, 2, false>(a, p, s); break;
+    case 27: e = launch_panel_t<6, 2, true>(a, p, s); break;
     case 32: e = launch_panel_t<8, 1, false>(a, p, s); break;
     case 33: e = launch_panel_t<8, 1, true>(a, p, s); break;
     case 34: e = launch_panel_t<8, 2, false>(a, p, s); break;

@@ -92,71 +92,6 @@ __device__ __forceinline__ u32x4 load_x8(const SkinnyProblem& p, int m, int k) {
   return w;
 }
 
-// Per-step weight loads of a lane: one bounds-checked load (r = 2, 4, 8) or
-// one from each plane of a split (r = 3, 6); `words` flattens them.
-template <int R, int V>
-struct LoadT;
-template <int R>
-struct LoadT<R, 16> {
-  typedef u32x4 T;
-  static constexpr int NW = 4;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t) {
-    return buf_load16(r, off);
-  }
-  __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
-    d[0] = t[0]; d[1] = t[1]; d[2] = t[2]; d[3] = t[3];
-  }
-};
-template <int R>
-struct LoadT<R, 8> {
-  typedef u32x2 T;
-  static constexpr int NW = 2;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t) {
-    return buf_load8(r, off);
-  }
-  __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
-    d[0] = t[0]; d[1] = t[1];
-  }
-};
-struct Split6 {  // 16 high bytes (32 four-bit fields) + 8 low bytes (32 two-bit fields)
-  u32x4 h;
-  u32x2 l;
-};
-struct Split3 {  // 8 high bytes (32 two-bit fields) + 4 low bytes (32 one-bit fields)
-  u32x2 h;
-  uint32_t l;
-};
-template <>
-struct LoadT<6, 0> {
-  typedef Split6 T;
-  static constexpr int NW = 6;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t oh, uint32_t ol) {
-    T t;
-    t.h = buf_load16(r, oh);
-    t.l = buf_load8(r, ol);
-    return t;
-  }
-  __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
-    d[0] = t.h[0]; d[1] = t.h[1]; d[2] = t.h[2]; d[3] = t.h[3];
-    d[4] = t.l[0]; d[5] = t.l[1];
-  }
-};
-template <>
-struct LoadT<3, 0> {
-  typedef Split3 T;
-  static constexpr int NW = 3;
-  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t oh, uint32_t ol) {
-    T t;
-    t.h = buf_load8(r, oh);
-    t.l = buf_load4(r, ol);
-    return t;
-  }
-  __device__ __forceinline__ static void words(const T& t, uint32_t* d) {
-    d[0] = t.h[0]; d[1] = t.h[1];
-    d[2] = t.l;
-  }
-};
-
 // Activation of a gated MLP's gate output: identity, SiLU g * sigmoid(g), or
 // GELU in its tanh form g/2 * (1 + tanh(z)), z = sqrt(2/pi) * (g + 0.044715 g^3),
 // evaluated as g / (1 + exp(-2z)) (the same function): 1 + tanh(z) cancels

@@ -15,6 +15,7 @@ enum XMode : int {
 
 constexpr int kMaxProblems = 16;
 constexpr int kSkinnyMaxM = 8;
+constexpr int kPanelMaxM = 64;  // mq_gemm: rows served by the small-batch kernel
 
 struct SkinnyProblem {
   const uint8_t* packed;

@@ -185,12 +185,47 @@ def test_gemv_mixed_granularities(M):
         compare(y, ref, what)
 
 
-def test_gemm_split_precision_needs_decode_shape():
+def test_gemm_split_precision_limit():
+    """r = 3 and 6 are served up to 64 activation rows; above, an error and
+    nothing written."""
     m = quantized("tiny_linear", 64, 512, 512)
     plane = mq.pack(m["q_d"], 6)
-    xb = x_device(inputs.activations_bf16("tiny_linear", 9, 512))
+    xb = x_device(inputs.activations_bf16("tiny_linear", 65, 512))
+    y = torch.full((65, 64), 5.0, device=dev())
     with pytest.raises(mq.MQError):
-        mq.gemm(plane, 6, m["alpha_d"], m["zero_d"], 512, 64, 512, xb)
+        mq.gemm(plane, 6, m["alpha_d"], m["zero_d"], 512, 64, 512, xb, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 5.0)
+
+
+@pytest.mark.parametrize("r", [6, 3])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [9, 16, 33, 64])
+def test_gemm_split_precision_small_batch(r, group, M):
+    """9 <= M <= 64 at r = 3 and 6 (high and low planes) on the small-batch
+    kernel: ragged N, two K slices and a ragged last slice at K = 1536."""
+    n, k = 300, 1536
+    g = k if group == "K" else 128
+    note(f"gemm split precision r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=6)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=6, heavy_channels=8)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+
+
+@pytest.mark.parametrize("r", [6, 3])
+def test_gemm_split_precision_mistral_full_size(r):
+    """Mistral 14336 x 4096 and 4096 x 14336 at M = 16, group 128, sampled rows."""
+    for (n, k) in inputs.MISTRAL_SMALL_SHAPES:
+        note(f"gemm split precision mistral r={r} {n}x{k}")
+        m = quantized("mistral_small", n, k, 128, matrix=n // 4096)
+        xb = inputs.activations_bf16("mistral_small", 16, k, heavy_channels=8)
+        y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(r).choice(n, 150, replace=False)]))
+        compare(y[:, rows], oracle.linear(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], 128, r),
+                f"gemm mistral r{r} {n}x{k}")
 
 
 def test_gemv_deterministic():
