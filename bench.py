@@ -206,7 +206,7 @@ def run_rows(torch, mq, inputs, dev):
         w = inputs.device_gaussian_weights("mistral_small", N2, K2, dev, matrix=N2 // 4096)
         c2, a2, z2 = mq.quantize(w, 128)
         del w
-        for r in (4, 2):
+        for r in (4, 2, 6, 3):
             pl = mq.pack(c2, r)
             b1 = linear_bytes(N2, K2, r, 128, 0)
             nc = max(2, -(-ROTATE_BYTES // b1))
@@ -233,7 +233,7 @@ def run_rows(torch, mq, inputs, dev):
     x5 = torch.from_numpy(xb.view("int16")).to(dev)
     y5 = torch.empty((M, N), dtype=torch.float32, device=dev)
     pre = {}
-    for r in (4, 2, 8):
+    for r in (4, 2, 8, 6, 3):
         pl = mq.pack(c5, r)
         us = time_loop(torch, lambda i: mq.gemm(pl, r, a5, z5, 128, N, K, x5, out=y5), 10)
         tf = 2 * M * N * K / us / 1e6

@@ -47,7 +47,7 @@ typedef enum mq_status {
   MQ_OK = 0,
   MQ_ERR_NULL = 1,      /* a required pointer is NULL                          */
   MQ_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)       */
-  MQ_ERR_PRECISION = 3, /* r is not 2, 3, 4, 6 or 8 (or not served at that M) */
+  MQ_ERR_PRECISION = 3, /* r is not 2, 3, 4, 6 or 8 */
   MQ_ERR_GROUP = 4,     /* group is neither K nor 128                          */
   MQ_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                    */
   MQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than required          */
@@ -162,7 +162,8 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
  * mq_gemm: the same product for any number of activation rows M >= 1 (small
  * batches and prefill), on bf16 matrix cores with fp32 accumulation.  Same
  * definitions and layouts as mq_gemv; M <= 8 takes the mq_gemv kernel.
- * r = 3 and r = 6 are served for M <= 64 (MQ_ERR_PRECISION above).
+ * Every r in {2, 3, 4, 6, 8} is served at every M (r = 3 and 6 from their
+ * high- and low-bit planes).
  *   workspace  device scratch of at least mq_gemm_workspace_bytes(M, N, K, group)
  *              bytes (may be NULL when that is 0), 256-byte aligned
  * Sizes: M >= 1, N >= 1, K >= 64, K % 64 == 0, K <= 65536.

@@ -201,8 +201,6 @@ mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float*
   mq_status s = check_product(packed, r, alpha, zero, group, N, K, x, y);
   if (s != MQ_OK) return s;
   if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
-  // the split precisions have the decode and small-batch kernels only
-  if (M > mq::kPanelMaxM && mq::split_precision(r)) return MQ_ERR_PRECISION;
   const size_t need = mq::gemm_workspace_bytes(M, N, K, group);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MQ_ERR_WORKSPACE;
   s = check_device();

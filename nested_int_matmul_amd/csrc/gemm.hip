@@ -269,7 +269,9 @@ hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const f
                        void* workspace, hipStream_t s) {
   if (M <= kPanelMaxM)
     return launch_gemm_panel(packed, r, alpha, zero, group, N, K, x, M, y, workspace, s);
-  if (M >= 256) return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, s);
+  // split planes (r = 3, 6) above the small batch: the prefill kernel, whose
+  // partial tiles cover any M
+  if (M >= 256 || split_precision(r)) return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, s);
   switch (r) {
     case 2: return launch_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
     case 4: return launch_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);

@@ -22,6 +22,9 @@
 //    (two VALU operations per accumulator per group, and the accumulator
 //    stays centred, which keeps fp32 cancellation small);
 //  - the per-group row sums of x come from the staged tiles (v_dot2);
+//  - r = 3 and 6 stage a high-plane and a low-plane sub-tile per iteration
+//    and assemble u = 128 + t from both (8-byte low rows at r = 3 go through
+//    4-byte buffer-to-LDS loads);
 //  - tiles are mapped to XCDs so that the workgroups of one XCD share
 //    activation rows (its L2 keeps them).
 #include "mq_device.h"
@@ -37,8 +40,14 @@ constexpr int MB = 4, NB = 2;               // 32x32 blocks per wave (m, n)
 constexpr int XT_BYTES = BM * BK * 2;       // staged activation tile
 template <int R>
 struct Cfg {
-  static constexpr int WROW = BK * R / 8;   // packed bytes per weight row per iteration
-  static constexpr int WT_BYTES = BN * WROW;
+  // r = 3 and 6: a high-bit plane (rows of K * RH / 8 bytes) followed by a
+  // low-bit plane (rows of K * RL / 8 bytes); staged as two sub-tiles
+  static constexpr bool SPLIT = (R == 3 || R == 6);
+  static constexpr int RL = SPLIT ? (R == 6 ? 2 : 1) : 0, RH = R - RL;
+  static constexpr int WROW = BK * RH / 8;  // (high-)plane bytes per weight row per iteration
+  static constexpr int WLOW = BK * RL / 8;  // low-plane bytes per weight row per iteration
+  static constexpr int LO_OFF = BN * WROW;  // low sub-tile within a stage
+  static constexpr int WT_BYTES = BN * (WROW + WLOW);
   static constexpr int LDS = 2 * XT_BYTES + 2 * WT_BYTES + BM * 4;
 };
 
@@ -46,17 +55,21 @@ struct Cfg {
 // (256 bytes); both swizzles keep those lanes on distinct banks, and also the
 // 8-lane groups of a 128-byte cycle.
 //  - activations, row r (128 bytes): logical chunk c sits at c ^ xsw(r);
-//  - packed weights, row r (WROW bytes = 2 or 4 chunks at r = 4, 8): chunk c
-//    sits at c ^ wsw(r) (r = 2 rows are one chunk: no swizzle).
+//  - packed weights, row r (WROW bytes = CPR chunks: 2 at r = 4 and 6, 4 at
+//    r = 8): chunk c sits at c ^ wsw(r) (one-chunk rows: no swizzle).
 __device__ __forceinline__ int xsw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-template <int R>
+template <int CPR>
 __device__ __forceinline__ int wsw(int r) {
-  return R == 4 ? ((r >> 2) ^ (r >> 3)) & 1 : R == 8 ? ((r >> 1) ^ (r >> 2)) & 3 : 0;
+  return CPR == 2 ? ((r >> 2) ^ (r >> 3)) & 1 : CPR == 4 ? ((r >> 1) ^ (r >> 2)) & 3 : 0;
 }
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
 template <int R, bool GROUPED>
@@ -87,6 +100,9 @@ __global__ void __launch_bounds__(THREADS)
   const int iters = K / BK;
   constexpr int IPG = 128 / BK;  // iterations per group of 128 (grouped)
   const UnpackK uk = UnpackK::make();
+  UnpackK36 uk36;
+  if constexpr (C::SPLIT) uk36 = UnpackK36::make();
+  const int hrow = K * C::RH / 8, lrow = K * C::RL / 8;  // plane row bytes (high, low)
 
   // ---- per-iteration staging (buffer-to-LDS, 1 KiB per wave instruction)
   auto stage = [&](int it, int buf) {
@@ -102,15 +118,30 @@ __global__ void __launch_bounds__(THREADS)
       lds_dma16(xr, xs + rb * 128, off);
     }
     unsigned char* ws = ws0 + buf * C::WT_BYTES;
-    constexpr int WPIECES = C::WT_BYTES / 1024;
+    constexpr int WPIECES = BN * C::WROW / 1024;
     for (int q = wave; q < WPIECES; q += WAVES) {
       const int byte = q * 1024 + lane * 16;
       const int row = byte / C::WROW;
-      const int col = (((byte % C::WROW) >> 4) ^ wsw<R>(row)) << 4;  // logical chunk held here
+      const int col = (((byte % C::WROW) >> 4) ^ wsw<C::WROW / 16>(row)) << 4;  // logical chunk here
       const int n = n0 + row;
       const uint32_t off =
-          n < N ? (uint32_t)n * (uint32_t)rowbytes + (uint32_t)(k0 * R / 8 + col) : 0x80000000u;
+          n < N ? (uint32_t)n * (uint32_t)hrow + (uint32_t)(k0 * C::RH / 8 + col) : 0x80000000u;
       lds_dma16(wr, ws + q * 1024, off);
+    }
+    if constexpr (C::SPLIT) {
+      // low-plane sub-tile [BN][WLOW]: 16-byte rows (r = 6) one per lane;
+      // 8-byte rows (r = 3) as 4-byte pieces, 256 bytes per wave instruction
+      constexpr int PIECE = C::WLOW >= 16 ? 1024 : 256;
+      for (int q = wave; q < BN * C::WLOW / PIECE; q += WAVES) {
+        const int byte = q * PIECE + lane * (PIECE / 64);
+        const int row = byte / C::WLOW, col = byte % C::WLOW;
+        const int n = n0 + row;
+        const uint32_t off = n < N ? (uint32_t)N * hrow + (uint32_t)n * lrow +
+                                         (uint32_t)(k0 * C::RL / 8 + col)
+                                   : 0x80000000u;
+        if constexpr (PIECE == 1024) lds_dma16(wr, ws + C::LO_OFF + q * PIECE, off);
+        else lds_dma4(wr, ws + C::LO_OFF + q * PIECE, off);
+      }
     }
   };
 
@@ -202,21 +233,33 @@ __global__ void __launch_bounds__(THREADS)
       //      term and moves to this group's units (cz = 0, rho = 1 before)
       const unsigned char* xs = xs0 + buf * XT_BYTES;
       const unsigned char* ws = ws0 + buf * C::WT_BYTES;
-      uint32_t wv[NB][R];  // this lane's packed bytes of the iteration (4R bytes) per n-block
+      // this lane's packed words of the iteration (its 32 codes) per n-block:
+      // 4R bytes, or for split planes 4 RH high bytes then 4 RL low bytes
+      uint32_t wv[NB][R];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int wrow = wn * 64 + j * 32 + l32;
         const unsigned char* p = ws + wrow * C::WROW;
-        if (R == 2) {
+        if (C::RH == 2) {
           const u32x2 v = *reinterpret_cast<const u32x2*>(p + s * 8);
           wv[j][0] = v[0]; wv[j][1] = v[1];
         } else {
 #pragma unroll
-          for (int h = 0; h < R / 4; ++h) {
-            const int c = s * (R / 4) + h;  // logical chunk
-            const u32x4 v = *reinterpret_cast<const u32x4*>(p + ((c ^ wsw<R>(wrow)) << 4));
+          for (int h = 0; h < C::RH / 4; ++h) {
+            const int c = s * (C::RH / 4) + h;  // logical chunk
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(p + ((c ^ wsw<C::WROW / 16>(wrow)) << 4));
             wv[j][4 * h + 0] = v[0]; wv[j][4 * h + 1] = v[1];
             wv[j][4 * h + 2] = v[2]; wv[j][4 * h + 3] = v[3];
+          }
+        }
+        if constexpr (C::SPLIT) {
+          const unsigned char* pl = ws + C::LO_OFF + wrow * C::WLOW;
+          if (C::RL == 2) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(pl + s * 8);
+            wv[j][4] = v[0]; wv[j][5] = v[1];
+          } else {
+            wv[j][2] = *reinterpret_cast<const uint32_t*>(pl + s * 4);
           }
         }
       }
@@ -235,6 +278,8 @@ __global__ void __launch_bounds__(THREADS)
           if (R == 4) b[j] = unpack_r4(wv[j][kk], uk);
           else if (R == 2) b[j] = (kk & 1) ? unpack_r2<1>(wv[j][kk >> 1], uk)
                                            : unpack_r2<0>(wv[j][kk >> 1], uk);
+          else if (R == 6) b[j] = unpack_r6(wv[j][kk], wv[j][4 + (kk >> 1)], kk & 1, uk36);
+          else if (R == 3) b[j] = unpack_r3(wv[j][kk >> 1], wv[j][2], kk, uk36);
           else b[j] = unpack_r8(wv[j][2 * kk], wv[j][2 * kk + 1]);
         }
 #pragma unroll
@@ -331,6 +376,8 @@ hipError_t launch_gemm_big(const uint8_t* packed, int r, const float* alpha, con
   switch (r) {
     case 2: return launch_big_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
     case 4: return launch_big_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);
+    case 3: return launch_big_r<3>(packed, alpha, zero, group, N, K, x, M, y, s);
+    case 6: return launch_big_r<6>(packed, alpha, zero, group, N, K, x, M, y, s);
     default: return launch_big_r<8>(packed, alpha, zero, group, N, K, x, M, y, s);
   }
 }

@@ -185,17 +185,20 @@ def test_gemv_mixed_granularities(M):
         compare(y, ref, what)
 
 
-def test_gemm_split_precision_limit():
-    """r = 3 and 6 are served up to 64 activation rows; above, an error and
-    nothing written."""
-    m = quantized("tiny_linear", 64, 512, 512)
-    plane = mq.pack(m["q_d"], 6)
-    xb = x_device(inputs.activations_bf16("tiny_linear", 65, 512))
-    y = torch.full((65, 64), 5.0, device=dev())
-    with pytest.raises(mq.MQError):
-        mq.gemm(plane, 6, m["alpha_d"], m["zero_d"], 512, 64, 512, xb, out=y)
+@pytest.mark.parametrize("r", [6, 3])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [65, 130, 256, 300])
+def test_gemm_split_precision_large_batch(r, group, M):
+    """M > 64 at r = 3 and 6 on the prefill kernel: partial 256-row tiles,
+    ragged N, 24 K iterations."""
+    n, k = 300, 1536
+    g = k if group == "K" else 128
+    note(f"gemm split precision large r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=7)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=7, heavy_channels=8)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
     torch.cuda.synchronize()
-    assert torch.all(y == 5.0)
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [6, 3])
@@ -369,7 +372,7 @@ def test_gemm_mistral_small_full_size(r, M, shape):
     compare(y[:, rows], ref, f"mistral small r{r} M{M} {shape}")
 
 
-@pytest.mark.parametrize("r", [4, 2, 8])
+@pytest.mark.parametrize("r", [4, 2, 8, 6, 3])
 def test_gemm_prefill_full_size(r):
     M, k, n = inputs.PREFILL_SHAPE
     note(f"gemm prefill r={r}")
