@@ -113,7 +113,7 @@ const char* mq_status_string(int status) {
     case MQ_OK: return "MQ_OK";
     case MQ_ERR_NULL: return "MQ_ERR_NULL: a required pointer is NULL";
     case MQ_ERR_SHAPE: return "MQ_ERR_SHAPE: a size is out of range";
-    case MQ_ERR_PRECISION: return "MQ_ERR_PRECISION: r must be 2, 4 or 8";
+    case MQ_ERR_PRECISION: return "MQ_ERR_PRECISION: r must be 2, 3, 4, 6 or 8";
     case MQ_ERR_GROUP: return "MQ_ERR_GROUP: group must be K or 128 (with K % 128 == 0)";
     case MQ_ERR_ALIGN: return "MQ_ERR_ALIGN: a pointer is not suitably aligned";
     case MQ_ERR_WORKSPACE: return "MQ_ERR_WORKSPACE: workspace missing or too small";
