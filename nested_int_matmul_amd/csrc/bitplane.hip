@@ -375,13 +375,12 @@ __global__ void __launch_bounds__(256) pack_bitplanes_kernel(const uint8_t* __re
 
 template <int R, bool GROUPED, bool EXTRA>
 static hipError_t launch_r(const Args& a, unsigned tiles, size_t lds, hipStream_t s) {
-  static bool attr_set = false;  // benign race: idempotent attribute call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)bp_gemv_kernel<R, GROUPED, EXTRA>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // the LDS limit is raised once per process (a function-local static is
+  // initialized exactly once, also when several host threads launch)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)bp_gemv_kernel<R, GROUPED, EXTRA>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((bp_gemv_kernel<R, GROUPED, EXTRA>), dim3(tiles), dim3(64 * kWaves), lds, s,
                      a);
   return hipGetLastError();

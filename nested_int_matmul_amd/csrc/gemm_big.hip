@@ -352,14 +352,15 @@ static hipError_t launch_big_r(const uint8_t* packed, const float* alpha, const 
   using namespace big;
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + BN - 1) / BN);
   const size_t lds = Cfg<R>::LDS;
-  static bool attr[2] = {false, false};  // benign race: idempotent attribute calls
   const bool grouped = group != K;
-  const void* fn = grouped ? (const void*)gemm_big_kernel<R, true> : (const void*)gemm_big_kernel<R, false>;
-  if (!attr[grouped]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr[grouped] = true;
-  }
+  // the LDS limit is raised once per process and kernel (function-local
+  // statics are initialized exactly once, also when several host threads launch)
+  static const hipError_t attr_g = hipFuncSetAttribute(
+      (const void*)gemm_big_kernel<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static const hipError_t attr_c = hipFuncSetAttribute(
+      (const void*)gemm_big_kernel<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr_g != hipSuccess) return attr_g;
+  if (attr_c != hipSuccess) return attr_c;
   dim3 grid((unsigned)(mt * nt)), block(THREADS);
   if (grouped)
     hipLaunchKernelGGL((gemm_big_kernel<R, true>), grid, block, lds, s, packed, alpha, zero, x, y,

@@ -338,13 +338,12 @@ static hipError_t launch_panel_t(const panel::Args& a, const PanelPlan& p, hipSt
   constexpr int NW = 8;
   const size_t lds = (size_t)32 * MB * (p.kslice + panel::kXPadE) * 2 +
                      (size_t)(panel::kKSliceMax / 128) * 32 * MB * 4 + (size_t)2 * NW * 32 * 8 * 4;
-  static bool attr = false;  // benign race: idempotent attribute call
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)panel::panel_kernel<R, MB, NW, GROUPED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // the LDS limit is raised once per process (a function-local static is
+  // initialized exactly once, also when several host threads launch)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)panel::panel_kernel<R, MB, NW, GROUPED>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((panel::panel_kernel<R, MB, NW, GROUPED>), dim3(p.panels, p.slices),
                      dim3(64 * NW), lds, s, a);
   return hipGetLastError();

@@ -469,13 +469,12 @@ static int step_codes(int r, bool grouped) {
 
 template <bool GROUPED, bool SPLIT>
 static hipError_t launch_t(const SkinnyArgs& a, size_t lds, hipStream_t s) {
-  static bool attr_set = false;  // benign race: idempotent attribute call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)skinny_kernel<GROUPED, SPLIT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // the LDS limit is raised once per process (a function-local static is
+  // initialized exactly once, also when several host threads launch)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)skinny_kernel<GROUPED, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
+  if (attr != hipSuccess) return attr;
   int tiles = a.p[a.count - 1].tile0 + a.p[a.count - 1].tiles;
   hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(tiles), dim3(64 * kSkinnyWaves), lds, s,
                      a);
