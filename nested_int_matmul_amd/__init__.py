@@ -141,7 +141,15 @@ def _stream(stream=None):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor the library reads or writes: it must live
+    on the GPU and be contiguous (the library takes plain row-major buffers)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("mq: tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("mq: tensors must be contiguous (row-major)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _bits16(x):
@@ -204,9 +212,8 @@ def gemv(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, s
 def _problem_array(problems):
     arr = (GemvProblem * len(problems))()
     for i, p in enumerate(problems):
-        arr[i] = GemvProblem(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
-                             _bits16(p["x"]).data_ptr(), p["y"].data_ptr(), p["N"], p["K"],
-                             p["group"])
+        arr[i] = GemvProblem(_ptr(p["packed"]), _ptr(p["alpha"]), _ptr(p["zero"]),
+                             _ptr(_bits16(p["x"])), _ptr(p["y"]), p["N"], p["K"], p["group"])
     return arr
 
 
@@ -253,6 +260,8 @@ def overflow_lists(codes, r: int, stream=None):
     row_ptr = torch.empty(n + 1, dtype=torch.int32, device=codes.device)
     _check(lib().mq_overflow_rows(_ptr(codes), n, k, r, _ptr(row_ptr), _stream(stream)),
            "mq_overflow_rows")
+    # the count was written on `stream`: wait for it there before reading it
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
     nnz = int(row_ptr[n].item())
     col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=codes.device)
     _check(lib().mq_overflow_cols(_ptr(codes), n, k, r, _ptr(row_ptr), _ptr(col_idx),
@@ -332,7 +341,7 @@ def make_layers(layers):
         kw = {"r": L["r"]}
         for n in LAYER_LINEARS:
             p = L[n]
-            kw[n] = Linear(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
+            kw[n] = Linear(_ptr(p["packed"]), _ptr(p["alpha"]), _ptr(p["zero"]),
                            p["N"], p["K"], p["group"])
         arr[i] = Layer(**kw)
     return arr
@@ -343,7 +352,7 @@ MLP_ACTS = {"identity": 0, "silu": 1, "gelu_tanh": 2}
 
 def make_linear(p):
     """{"packed", "alpha", "zero", "N", "K", "group"} -> a ctypes Linear."""
-    return Linear(p["packed"].data_ptr(), p["alpha"].data_ptr(), p["zero"].data_ptr(),
+    return Linear(_ptr(p["packed"]), _ptr(p["alpha"]), _ptr(p["zero"]),
                   p["N"], p["K"], p["group"])
 
 

@@ -159,3 +159,14 @@ def test_mlp_validation(L):
     assert call(u=lin(128, 256, 128), g=lin(128, 256, 256), d=lin(256, 128)) == 4
     assert call(w=NULL) == 6
     assert call(y=P1) == 5
+
+
+def test_binding_rejects_host_tensors(L):
+    """The binding passes only GPU tensors to the library: a host tensor is
+    refused before any call (no silent host pointer)."""
+    torch = pytest.importorskip("torch")
+    codes = torch.zeros((4, 64), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mq.pack(codes, 4, out=torch.zeros((4, 32), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        mq._ptr(torch.zeros(8))
