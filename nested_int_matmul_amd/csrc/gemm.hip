@@ -15,7 +15,10 @@
 // workgroup of 4 waves computes a BM x BN tile; each K iteration covers 128
 // codes (one scale group): the activation tile (bf16, natural order) and the
 // packed weight tile are staged in LDS, the next tile's global loads are
-// issued before the current tile's MFMAs.
+// issued before the current tile's MFMAs.  Every group is folded into fp32
+// totals in absolute units, so a run of K iterations is an additive partial:
+// when the tiles alone leave CUs idle (few rows of n, long K), K is split over
+// blockIdx.z and the slices are summed in slice order by a second kernel.
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -55,7 +58,7 @@ template <int R, int MB, int NB, int WM, int WN, bool GROUPED>
 __global__ void __launch_bounds__(64 * WM * WN)
     gemm_kernel(const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
                 const float* __restrict__ zero, const uint16_t* __restrict__ x,
-                float* __restrict__ y, int M, int N, int K, int group) {
+                float* __restrict__ y, int M, int N, int K, int group, int its) {
   using C = Gm<R, MB, NB, WM, WN>;
   __shared__ __align__(16) uint16_t xs[C::BM * C::XS];
   __shared__ __align__(16) uint8_t ws[C::BN * C::WS];
@@ -70,7 +73,12 @@ __global__ void __launch_bounds__(64 * WM * WN)
   const uint32_t plane = (uint32_t)((int64_t)N * rowbytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, plane);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  // this workgroup's K iterations [it0, it1) (slice blockIdx.z of its each);
+  // a split writes slice z of the partial tiles [S][M][N]
   const int iters = (K + kBK - 1) / kBK;
+  const int it0 = (int)blockIdx.z * its;
+  const int it1 = min(iters, it0 + its);
+  y += (int64_t)blockIdx.z * M * N;
 
   // ---- per-thread staging assignment
   // x: thread covers XV consecutive 16-byte vectors of one row
@@ -87,7 +95,11 @@ __global__ void __launch_bounds__(64 * WM * WN)
     return (uint32_t)n * (uint32_t)rowbytes + (uint32_t)(it * C::WROW + cb);
   };
 
+  const int l32 = lane & 31, s = lane >> 5;
+  const int am0 = wm * MB * 32, bn0 = wn * NB * 32;
+
   u32x4 xreg[C::XV], wreg[C::WV];
+  float ga[NB], gz[NB];  // grouped: scale and zero point of the loaded group
   auto gload = [&](int it) {
 #pragma unroll
     for (int v = 0; v < C::XV; ++v) {
@@ -97,6 +109,14 @@ __global__ void __launch_bounds__(64 * WM * WN)
     }
 #pragma unroll
     for (int v = 0; v < C::WV; ++v) wreg[v] = buf_load16(wr, wvec_off(v, it));
+    if (GROUPED) {  // group == 128 == kBK: iteration it is group it
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = min(n0 + bn0 + 32 * j + (lane & 31), N - 1);
+        ga[j] = alpha[(int64_t)n * G + it];
+        gz[j] = zero[(int64_t)n * G + it];
+      }
+    }
   };
   float xsum_run = 0.f;  // per-channel: running sum of this thread's x values
   auto lstore = [&]() {
@@ -135,16 +155,20 @@ __global__ void __launch_bounds__(64 * WM * WN)
         tot[i][j][e] = 0.f;
       }
 
-  const int l32 = lane & 31, s = lane >> 5;
-  const int am0 = wm * MB * 32, bn0 = wn * NB * 32;
 
-  gload(0);
+  gload(it0);
 #pragma unroll 1
-  for (int it = 0; it < iters; ++it) {
+  for (int it = it0; it < it1; ++it) {
     __syncthreads();
     lstore();
+    float ca[NB], cz[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      ca[j] = ga[j];
+      cz[j] = gz[j];
+    }
     __syncthreads();
-    if (it + 1 < iters) gload(it + 1);
+    if (it + 1 < it1) gload(it + 1);
 
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -176,17 +200,11 @@ __global__ void __launch_bounds__(64 * WM * WN)
     }
 
     if (GROUPED) {
-      const int g = it;  // group == 128 == kBK
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int n = n0 + bn0 + 32 * j + l32;
-        float av = 0.f, bv = 0.f;
-        if (n < N) {
-          const float al = alpha[(int64_t)n * G + g];
-          const float ze = zero[(int64_t)n * G + g];
-          av = al * Enc<R>::kStep;
-          bv = al * (ze + Enc<R>::kOffsetShift);
-        }
+        // columns past N fold clamped scales; they are never stored
+        const float av = ca[j] * Enc<R>::kStep;
+        const float bv = ca[j] * (cz[j] + Enc<R>::kOffsetShift);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -236,32 +254,60 @@ __global__ void __launch_bounds__(64 * WM * WN)
   }
 }
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t) {
-  return (M > kSkinnyMaxM && M <= kPanelMaxM) ? panel_workspace_bytes(M, N, K) : 0;
+// 64 < M < 256 (r = 2, 4, 8): 128 x 128 tiles of 4 waves.  K is split while
+// the tiles fill fewer than the target number of workgroups (measured best:
+// 512 with per-channel scales, 256 with group-128 scales, whose per-group
+// folds cost more per iteration) and every slice keeps at least
+// kTiledMinIters iterations.
+constexpr int kTiledBM = 128, kTiledBN = 128;
+constexpr int kTiledTargetChannel = 512, kTiledTargetGroup = 256, kTiledMinIters = 4;
+
+struct TiledPlan {
+  int gx, gy, slices, its;
+};
+
+static TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, int64_t group) {
+  const int target = group == K ? kTiledTargetChannel : kTiledTargetGroup;
+  TiledPlan p;
+  p.gx = (int)((N + kTiledBN - 1) / kTiledBN);
+  p.gy = (int)((M + kTiledBM - 1) / kTiledBM);
+  const int iters = (int)((K + kBK - 1) / kBK);
+  int s = 1;
+  while ((int64_t)p.gx * p.gy * s * 2 <= target && iters / (s * 2) >= kTiledMinIters) s *= 2;
+  p.its = (iters + s - 1) / s;
+  p.slices = (iters + p.its - 1) / p.its;
+  return p;
 }
 
-template <int R, int MB, int NB, int WM, int WN>
-static hipError_t launch_cfg(const uint8_t* packed, const float* alpha, const float* zero,
-                             int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
-                             float* y, hipStream_t s) {
-  using C = Gm<R, MB, NB, WM, WN>;
-  dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
-  if (group == K)
-    hipLaunchKernelGGL((gemm_kernel<R, MB, NB, WM, WN, false>), grid, dim3(C::THREADS), 0, s,
-                       packed, alpha, zero, x, y, (int)M, (int)N, (int)K, (int)group);
-  else
-    hipLaunchKernelGGL((gemm_kernel<R, MB, NB, WM, WN, true>), grid, dim3(C::THREADS), 0, s,
-                       packed, alpha, zero, x, y, (int)M, (int)N, (int)K, (int)group);
-  return hipGetLastError();
+static bool tiled_route(int64_t M) { return M > kPanelMaxM && M < 256; }
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (M > kSkinnyMaxM && M <= kPanelMaxM) return panel_workspace_bytes(M, N, K);
+  if (tiled_route(M)) {
+    const TiledPlan p = plan_tiled(M, N, K, group);
+    return p.slices > 1 ? (size_t)p.slices * M * N * 4 : 0;
+  }
+  return 0;
 }
 
 template <int R>
 static hipError_t launch_r(const uint8_t* packed, const float* alpha, const float* zero,
                            int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
-                           float* y, hipStream_t s) {
-  if (M <= 32) return launch_cfg<R, 1, 1, 1, 4>(packed, alpha, zero, group, N, K, x, M, y, s);
-  if (M <= 64) return launch_cfg<R, 1, 2, 2, 2>(packed, alpha, zero, group, N, K, x, M, y, s);
-  return launch_cfg<R, 2, 2, 2, 2>(packed, alpha, zero, group, N, K, x, M, y, s);
+                           float* y, void* workspace, hipStream_t s) {
+  using C = Gm<R, 2, 2, 2, 2>;
+  static_assert(C::BM == kTiledBM && C::BN == kTiledBN, "tile of the plan");
+  const TiledPlan p = plan_tiled(M, N, K, group);
+  float* out = p.slices > 1 ? static_cast<float*>(workspace) : y;
+  dim3 grid((unsigned)p.gx, (unsigned)p.gy, (unsigned)p.slices);
+  if (group == K)
+    hipLaunchKernelGGL((gemm_kernel<R, 2, 2, 2, 2, false>), grid, dim3(C::THREADS), 0, s, packed,
+                       alpha, zero, x, out, (int)M, (int)N, (int)K, (int)group, p.its);
+  else
+    hipLaunchKernelGGL((gemm_kernel<R, 2, 2, 2, 2, true>), grid, dim3(C::THREADS), 0, s, packed,
+                       alpha, zero, x, out, (int)M, (int)N, (int)K, (int)group, p.its);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.slices == 1) return e;
+  return launch_reduce_slices(out, y, M * N, p.slices, s);
 }
 
 hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
@@ -273,9 +319,9 @@ hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const f
   // partial tiles cover any M
   if (M >= 256 || split_precision(r)) return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, s);
   switch (r) {
-    case 2: return launch_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
-    case 4: return launch_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);
-    default: return launch_r<8>(packed, alpha, zero, group, N, K, x, M, y, s);
+    case 2: return launch_r<2>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
+    case 4: return launch_r<4>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
+    default: return launch_r<8>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
   }
 }
 

@@ -390,10 +390,12 @@ hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, c
     default: e = launch_panel_t<8, 2, true>(a, p, s); break;
   }
   if (e != hipSuccess || p.slices == 1) return e;
-  const int64_t count = M * N;
+  return launch_reduce_slices(static_cast<const float*>(workspace), y, M * N, p.slices, s);
+}
+
+hipError_t launch_reduce_slices(const float* part, float* y, int64_t count, int S, hipStream_t s) {
   const int blocks = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 2048);
-  hipLaunchKernelGGL(panel::reduce_slices, dim3(blocks), dim3(256), 0, s,
-                     static_cast<const float*>(workspace), y, count, p.slices);
+  hipLaunchKernelGGL(panel::reduce_slices, dim3(blocks), dim3(256), 0, s, part, y, count, S);
   return hipGetLastError();
 }
 

@@ -43,7 +43,25 @@ def test_status_strings_and_sizes(L):
     assert L.mq_packed_bytes(14336, 3584, 2) == 14336 * 3584 // 4
     assert L.mq_packed_bytes(10, 64, 3) == 10 * 64 * 3 // 8
     assert L.mq_packed_bytes(10, 64, 5) == 0
-    assert L.mq_gemm_workspace_bytes(2048, 14336, 4096, 128) >= 0
+    assert L.mq_gemm_workspace_bytes(2048, 14336, 4096, 128) == 0
+
+
+def test_mid_batch_split_plan(L):
+    """64 < M < 256: K (iterations of 128) is split in powers of two while the
+    128 x 128 tiles stay under 512 (per-channel) or 256 (group-128) workgroups
+    and each slice keeps 4 iterations; the workspace holds one fp32 [M, N]
+    partial per slice."""
+    ws = L.mq_gemm_workspace_bytes
+    # 4096 x 14336, M = 96: 32 tiles, 112 iterations -> 16 slices of 7 / 8 of 14
+    assert ws(96, 4096, 14336, 14336) == 16 * 96 * 4096 * 4
+    assert ws(96, 4096, 14336, 128) == 8 * 96 * 4096 * 4
+    # 33 iterations over 6 tiles: 8-way split of 5 iterations -> 7 slices
+    assert ws(130, 300, 4224, 4224) == 7 * 130 * 300 * 4
+    # 14336 x 4096 at M = 200: 224 tiles, one doubling under 512, none under 256
+    assert ws(200, 14336, 4096, 4096) == 2 * 200 * 14336 * 4
+    assert ws(200, 14336, 4096, 128) == 0
+    assert ws(130, 200, 640, 640) == 0      # 5 iterations: no slice of 4 fits twice
+    assert ws(256, 300, 4224, 4224) == 0    # prefill kernel, no workspace
 
 
 NULL = None

@@ -356,8 +356,25 @@ def test_gemm_small(r, group, M):
     compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
 
 
+@pytest.mark.parametrize("r", [8, 4, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [65, 130, 255])
+def test_gemm_mid_batch_split_k(r, group, M):
+    """64 < M < 256 with few output tiles and a long K: K is cut into slices
+    (33 iterations of 128, the last slice short), summed in slice order."""
+    n, k = 300, 4224
+    g = k if group == "K" else 128
+    assert mq.gemm_workspace_bytes(M, n, k, g) > 0
+    note(f"gemm mid batch split-K r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=8)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=8, heavy_channels=8)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+
+
 @pytest.mark.parametrize("r", [4, 2])
-@pytest.mark.parametrize("M", [16, 64])
+@pytest.mark.parametrize("M", [16, 64, 96, 200])
 @pytest.mark.parametrize("shape", inputs.MISTRAL_SMALL_SHAPES)
 def test_gemm_mistral_small_full_size(r, M, shape):
     n, k = shape
