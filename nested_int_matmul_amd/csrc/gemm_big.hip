@@ -22,6 +22,10 @@
 //    (two VALU operations per accumulator per group, and the accumulator
 //    stays centred, which keeps fp32 cancellation small);
 //  - the per-group row sums of x come from the staged tiles (v_dot2);
+//  - the scales and zero points reach LDS in windows of 4 groups (16 bytes
+//    of a column per lane), double-buffered: read per group from global
+//    memory, each column's value is a cache line of its own (columns are G
+//    floats apart);
 //  - r = 3 and 6 stage a high-plane and a low-plane sub-tile per iteration
 //    and assemble u = 128 + t from both (8-byte low rows at r = 3 go through
 //    4-byte buffer-to-LDS loads);
@@ -49,6 +53,8 @@ struct Cfg {
   static constexpr int LO_OFF = BN * WROW;  // low sub-tile within a stage
   static constexpr int WT_BYTES = BN * (WROW + WLOW);
   static constexpr int LDS = 2 * XT_BYTES + 2 * WT_BYTES + BM * 4;
+  // group-128 scales: + [2 windows][alpha, zero][BN columns][4 groups] fp32
+  static constexpr int LDS_GROUPED = LDS + 2 * 2 * BN * 4 * 4;
 };
 
 // LDS swizzles (16-byte chunks).  Operand reads serve 16 lanes per cycle
@@ -103,6 +109,22 @@ __global__ void __launch_bounds__(THREADS)
   UnpackK36 uk36;
   if constexpr (C::SPLIT) uk36 = UnpackK36::make();
   const int hrow = K * C::RH / 8, lrow = K * C::RL / 8;  // plane row bytes (high, low)
+
+  // ---- group scales (grouped): window w = groups [4w, 4w + 4) into LDS
+  //      buffer w & 1; waves 0-3 bring alpha, waves 4-7 the zero points, 64
+  //      columns each.  Columns past N take the last row (never stored);
+  //      groups past G read beyond the row (or 0 past the array) and are
+  //      never used.
+  float* sw = reinterpret_cast<float*>(smem + 2 * XT_BYTES + 2 * C::WT_BYTES + BM * 4);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(alpha, (uint32_t)((int64_t)N * G * 4));
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(zero, (uint32_t)((int64_t)N * G * 4));
+  auto stage_scales = [&](int w) {
+    const int n = min(n0 + (wave & 3) * 64 + lane, N - 1);
+    const uint32_t off = (uint32_t)(((int64_t)n * G + 4 * w) * 4);
+    float* dst = sw + (w & 1) * (2 * BN * 4) + (wave >> 2) * (BN * 4) + (wave & 3) * 256;
+    if (wave < 4) lds_dma16(ar, dst, off);
+    else lds_dma16(zr, dst, off);
+  };
 
   // ---- per-iteration staging (buffer-to-LDS, 1 KiB per wave instruction)
   auto stage = [&](int it, int buf) {
@@ -184,6 +206,7 @@ __global__ void __launch_bounds__(THREADS)
 
   // the first group's update reads these (cz = 0): keep them finite
   if (GROUPED && shalf == 0) sxg[srow] = 0.f;
+  if (GROUPED) stage_scales(0);
   stage(0, 0);
   // one trip of the outer loop = one group of 128 codes = IPG iterations
 #pragma unroll 1
@@ -195,19 +218,27 @@ __global__ void __launch_bounds__(THREADS)
       const int buf = it & 1;
       __syncthreads();  // staging of `it` complete (vmcnt waited by the compiler), buf^1 free
       // raw scales of the group ending with this trip and of the next one,
-      // issued before the staging loads so that using them never waits for those
+      // read from LDS before this iteration's staging is issued
       float a0n[NB], a1n[NB], z0n[NB];
       const bool prep = GROUPED && it2 == IPG - 1 && it + 1 < iters;
       if (prep) {
         const int g = it / IPG;
+        const float* w0 = sw + ((g >> 2) & 1) * (2 * BN * 4) + (g & 3);
+        const float* w1 = sw + (((g + 1) >> 2) & 1) * (2 * BN * 4) + ((g + 1) & 3);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          a0n[j] = scale(j, g);
-          a1n[j] = scale(j, g + 1);
-          z0n[j] = zraw(j, g);
+          const int col = wn * 64 + j * 32 + l32;
+          a0n[j] = w0[col * 4];
+          z0n[j] = w0[BN * 4 + col * 4];
+          a1n[j] = w1[col * 4];
         }
       }
       if (it + 1 < iters) stage(it + 1, buf ^ 1);
+      // the next scale window, at the start of a window: its buffer was last
+      // read before this iteration's barrier, and it is first needed at the
+      // window's last group end
+      if (GROUPED && it2 == 0 && ((it0 / IPG) & 3) == 0 && it0 / IPG + 4 < G)
+        stage_scales(it0 / IPG / 4 + 1);
 
       // ---- row sums of this tile's activations
       {
@@ -351,14 +382,16 @@ static hipError_t launch_big_r(const uint8_t* packed, const float* alpha, const 
                                float* y, hipStream_t s) {
   using namespace big;
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + BN - 1) / BN);
-  const size_t lds = Cfg<R>::LDS;
   const bool grouped = group != K;
+  const size_t lds = grouped ? Cfg<R>::LDS_GROUPED : Cfg<R>::LDS;
   // the LDS limit is raised once per process and kernel (function-local
   // statics are initialized exactly once, also when several host threads launch)
   static const hipError_t attr_g = hipFuncSetAttribute(
-      (const void*)gemm_big_kernel<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      (const void*)gemm_big_kernel<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg<R>::LDS_GROUPED);
   static const hipError_t attr_c = hipFuncSetAttribute(
-      (const void*)gemm_big_kernel<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      (const void*)gemm_big_kernel<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg<R>::LDS);
   if (attr_g != hipSuccess) return attr_g;
   if (attr_c != hipSuccess) return attr_c;
   dim3 grid((unsigned)(mt * nt)), block(THREADS);
