@@ -167,7 +167,8 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
  *   workspace  device scratch of at least mq_gemm_workspace_bytes(M, N, K, group)
  *              bytes (may be NULL when that is 0), 256-byte aligned: the fp32
  *              partial products of K slices, used where the output tiles alone
- *              leave the chip idle (small batches; 64 < M < 256 at long K)
+ *              leave the chip idle (small batches; larger M with long K or
+ *              few output columns, e.g. a 4096-wide down projection)
  * Sizes: M >= 1, N >= 1, K >= 64, K % 64 == 0, K <= 65536.
  */
 size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);

@@ -1,5 +1,6 @@
-// Batched product (M > 8 activation rows: small batches and prefill) against
-// r-bit planes, on bf16 matrix cores.
+// Batched product against r-bit planes on bf16 matrix cores: the router of
+// mq_gemm (M <= 8 decode kernel, 9..64 panel kernel, 65..127 at r = 2, 4, 8
+// the tiled kernel below, everything else the prefill kernel).
 //
 //   y[m, n] = sum_g alpha[n, g] * (2^(8-r) * sum_{k in g} x[m, k] t[n, k]
 //                                   - z[n, g] * sum_{k in g} x[m, k])
@@ -19,6 +20,8 @@
 // totals in absolute units, so a run of K iterations is an additive partial:
 // when the tiles alone leave CUs idle (few rows of n, long K), K is split over
 // blockIdx.z and the slices are summed in slice order by a second kernel.
+#include <algorithm>
+
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -254,7 +257,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
   }
 }
 
-// 64 < M < 256 (r = 2, 4, 8): 128 x 128 tiles of 4 waves.  K is split while
+// 64 < M < 128 (r = 2, 4, 8): 128 x 128 tiles of 4 waves.  K is split while
 // the tiles fill fewer than the target number of workgroups (measured best:
 // 512 with per-channel scales, 256 with group-128 scales, whose per-group
 // folds cost more per iteration) and every slice keeps at least
@@ -279,15 +282,21 @@ static TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, int64_t group) {
   return p;
 }
 
-static bool tiled_route(int64_t M) { return M > kPanelMaxM && M < 256; }
+// From M = 128 the prefill kernel (256 x 256 tiles, buffer-to-LDS staging,
+// its own K split) measured faster at the Mistral shapes; below, the
+// 128-row tiles waste fewer rows.
+constexpr int kTiledMaxM = 127;
+static bool tiled_route(int64_t M) { return M > kPanelMaxM && M <= kTiledMaxM; }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (M > kSkinnyMaxM && M <= kPanelMaxM) return panel_workspace_bytes(M, N, K);
-  if (tiled_route(M)) {
-    const TiledPlan p = plan_tiled(M, N, K, group);
-    return p.slices > 1 ? (size_t)p.slices * M * N * 4 : 0;
-  }
-  return 0;
+  if (M <= kSkinnyMaxM) return 0;
+  if (M <= kPanelMaxM) return panel_workspace_bytes(M, N, K);
+  const size_t big = gemm_big_workspace_bytes(M, N, K);
+  if (!tiled_route(M)) return big;
+  // r is not an argument: 64 < M < 128 takes the tiled kernel at r = 2, 4, 8
+  // and the prefill kernel at r = 3, 6; the workspace covers both
+  const TiledPlan p = plan_tiled(M, N, K, group);
+  return std::max(big, p.slices > 1 ? (size_t)p.slices * M * N * 4 : (size_t)0);
 }
 
 template <int R>
@@ -315,9 +324,10 @@ hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const f
                        void* workspace, hipStream_t s) {
   if (M <= kPanelMaxM)
     return launch_gemm_panel(packed, r, alpha, zero, group, N, K, x, M, y, workspace, s);
-  // split planes (r = 3, 6) above the small batch: the prefill kernel, whose
-  // partial tiles cover any M
-  if (M >= 256 || split_precision(r)) return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, s);
+  // M >= 128, and the split planes (r = 3, 6) above the small batch: the
+  // prefill kernel, whose partial tiles cover any M
+  if (!tiled_route(M) || split_precision(r))
+    return launch_gemm_big(packed, r, alpha, zero, group, N, K, x, M, y, workspace, s);
   switch (r) {
     case 2: return launch_r<2>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
     case 4: return launch_r<4>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);

@@ -30,7 +30,11 @@
 //    and assemble u = 128 + t from both (8-byte low rows at r = 3 go through
 //    4-byte buffer-to-LDS loads);
 //  - tiles are mapped to XCDs so that the workgroups of one XCD share
-//    activation rows (its L2 keeps them).
+//    activation rows (its L2 keeps them);
+//  - when the tiles alone leave CUs idle (few rows of y or of n, e.g. a
+//    4096-wide down projection), K is split over blockIdx.y into slices of
+//    whole groups; each slice ends in absolute units with its own last
+//    group's scale, and the slices are summed in slice order afterwards.
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -82,7 +86,8 @@ template <int R, bool GROUPED>
 __global__ void __launch_bounds__(THREADS)
     gemm_big_kernel(const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
                     const float* __restrict__ zero, const uint16_t* __restrict__ x,
-                    float* __restrict__ y, int M, int N, int K, int group, int mt, int nt) {
+                    float* __restrict__ y, int M, int N, int K, int group, int mt, int nt,
+                    int its) {
   using C = Cfg<R>;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* xs0 = smem;                                  // [2][BM][128 B] swizzled
@@ -105,6 +110,11 @@ __global__ void __launch_bounds__(THREADS)
   const int G = K / group;
   const int iters = K / BK;
   constexpr int IPG = 128 / BK;  // iterations per group of 128 (grouped)
+  // this workgroup's K slice: iterations [ib, ie) (its is a multiple of
+  // IPG); slice blockIdx.y of a split writes partial [blockIdx.y][M][N]
+  const int ib = (int)blockIdx.y * its;
+  const int ie = min(iters, ib + its);
+  y += (int64_t)blockIdx.y * M * N;
   const UnpackK uk = UnpackK::make();
   UnpackK36 uk36;
   if constexpr (C::SPLIT) uk36 = UnpackK36::make();
@@ -206,21 +216,27 @@ __global__ void __launch_bounds__(THREADS)
 
   // the first group's update reads these (cz = 0): keep them finite
   if (GROUPED && shalf == 0) sxg[srow] = 0.f;
-  if (GROUPED) stage_scales(0);
-  stage(0, 0);
+  if (GROUPED) {
+    // the slice's first window; and the next one when the slice starts
+    // inside a window (the loop issues a window only at a window's start)
+    const int gb = ib / IPG;
+    stage_scales(gb >> 2);
+    if ((gb & 3) != 0 && 4 * ((gb >> 2) + 1) < G) stage_scales((gb >> 2) + 1);
+  }
+  stage(ib, ib & 1);
   // one trip of the outer loop = one group of 128 codes = IPG iterations
 #pragma unroll 1
-  for (int it0 = 0; it0 < iters; it0 += IPG) {
+  for (int it0 = ib; it0 < ie; it0 += IPG) {
 #pragma unroll
     for (int it2 = 0; it2 < IPG; ++it2) {
       const int it = it0 + it2;
-      if (!GROUPED && it >= iters) break;  // per-channel K may end mid-pair
+      if (!GROUPED && it >= ie) break;  // per-channel K may end mid-pair
       const int buf = it & 1;
       __syncthreads();  // staging of `it` complete (vmcnt waited by the compiler), buf^1 free
       // raw scales of the group ending with this trip and of the next one,
       // read from LDS before this iteration's staging is issued
       float a0n[NB], a1n[NB], z0n[NB];
-      const bool prep = GROUPED && it2 == IPG - 1 && it + 1 < iters;
+      const bool prep = GROUPED && it2 == IPG - 1 && it + 1 < ie;
       if (prep) {
         const int g = it / IPG;
         const float* w0 = sw + ((g >> 2) & 1) * (2 * BN * 4) + (g & 3);
@@ -233,7 +249,7 @@ __global__ void __launch_bounds__(THREADS)
           a1n[j] = w1[col * 4];
         }
       }
-      if (it + 1 < iters) stage(it + 1, buf ^ 1);
+      if (it + 1 < ie) stage(it + 1, buf ^ 1);
       // the next scale window, at the start of a window: its buffer was last
       // read before this iteration's barrier, and it is first needed at the
       // window's last group end
@@ -347,7 +363,7 @@ __global__ void __launch_bounds__(THREADS)
   // ---- epilogue: last group's (or the only group's) zero-point term and scale
   if (!GROUPED && shalf == 0) sxg[srow] = srun;
   __syncthreads();
-  const int glast = G - 1;
+  const int glast = GROUPED ? ie / IPG - 1 : 0;  // the slice's last group
   float av[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -376,12 +392,39 @@ __global__ void __launch_bounds__(THREADS)
 
 }  // namespace big
 
+// K split: while the tiles fill fewer than kBigTarget CUs (one workgroup
+// each) and every slice keeps at least kBigMinIters iterations (whole groups)
+constexpr int kBigTarget = 256, kBigMinIters = 8;
+
+struct BigPlan {
+  int mt, nt, slices, its;
+};
+
+static BigPlan plan_big(int64_t M, int64_t N, int64_t K) {
+  using namespace big;
+  BigPlan p;
+  p.mt = (int)((M + BM - 1) / BM);
+  p.nt = (int)((N + BN - 1) / BN);
+  const int iters = (int)(K / BK);
+  int s = 1;
+  while ((int64_t)p.mt * p.nt * s * 2 <= kBigTarget && iters / (s * 2) >= kBigMinIters) s *= 2;
+  const int ipg = 128 / BK;
+  p.its = ((iters + s - 1) / s + ipg - 1) / ipg * ipg;
+  p.slices = (iters + p.its - 1) / p.its;
+  return p;
+}
+
+size_t gemm_big_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const BigPlan p = plan_big(M, N, K);
+  return p.slices > 1 ? (size_t)p.slices * M * N * 4 : 0;
+}
+
 template <int R>
 static hipError_t launch_big_r(const uint8_t* packed, const float* alpha, const float* zero,
                                int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
-                               float* y, hipStream_t s) {
+                               float* y, void* workspace, hipStream_t s) {
   using namespace big;
-  const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + BN - 1) / BN);
+  const BigPlan p = plan_big(M, N, K);
   const bool grouped = group != K;
   const size_t lds = grouped ? Cfg<R>::LDS_GROUPED : Cfg<R>::LDS;
   // the LDS limit is raised once per process and kernel (function-local
@@ -394,25 +437,28 @@ static hipError_t launch_big_r(const uint8_t* packed, const float* alpha, const 
       Cfg<R>::LDS);
   if (attr_g != hipSuccess) return attr_g;
   if (attr_c != hipSuccess) return attr_c;
-  dim3 grid((unsigned)(mt * nt)), block(THREADS);
+  float* out = p.slices > 1 ? static_cast<float*>(workspace) : y;
+  dim3 grid((unsigned)(p.mt * p.nt), (unsigned)p.slices), block(THREADS);
   if (grouped)
-    hipLaunchKernelGGL((gemm_big_kernel<R, true>), grid, block, lds, s, packed, alpha, zero, x, y,
-                       (int)M, (int)N, (int)K, (int)group, mt, nt);
+    hipLaunchKernelGGL((gemm_big_kernel<R, true>), grid, block, lds, s, packed, alpha, zero, x,
+                       out, (int)M, (int)N, (int)K, (int)group, p.mt, p.nt, p.its);
   else
-    hipLaunchKernelGGL((gemm_big_kernel<R, false>), grid, block, lds, s, packed, alpha, zero, x, y,
-                       (int)M, (int)N, (int)K, (int)group, mt, nt);
-  return hipGetLastError();
+    hipLaunchKernelGGL((gemm_big_kernel<R, false>), grid, block, lds, s, packed, alpha, zero, x,
+                       out, (int)M, (int)N, (int)K, (int)group, p.mt, p.nt, p.its);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.slices == 1) return e;
+  return launch_reduce_slices(out, y, M * N, p.slices, s);
 }
 
 hipError_t launch_gemm_big(const uint8_t* packed, int r, const float* alpha, const float* zero,
                            int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
-                           float* y, hipStream_t s) {
+                           float* y, void* workspace, hipStream_t s) {
   switch (r) {
-    case 2: return launch_big_r<2>(packed, alpha, zero, group, N, K, x, M, y, s);
-    case 4: return launch_big_r<4>(packed, alpha, zero, group, N, K, x, M, y, s);
-    case 3: return launch_big_r<3>(packed, alpha, zero, group, N, K, x, M, y, s);
-    case 6: return launch_big_r<6>(packed, alpha, zero, group, N, K, x, M, y, s);
-    default: return launch_big_r<8>(packed, alpha, zero, group, N, K, x, M, y, s);
+    case 2: return launch_big_r<2>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
+    case 4: return launch_big_r<4>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
+    case 3: return launch_big_r<3>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
+    case 6: return launch_big_r<6>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
+    default: return launch_big_r<8>(packed, alpha, zero, group, N, K, x, M, y, workspace, s);
   }
 }
 

@@ -72,7 +72,9 @@ hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, c
 hipError_t launch_reduce_slices(const float* part, float* y, int64_t count, int S, hipStream_t s);
 hipError_t launch_gemm_big(const uint8_t* packed, int r, const float* alpha, const float* zero,
                            int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
-                           float* y, hipStream_t s);
+                           float* y, void* workspace, hipStream_t s);
+// partial slices of the prefill kernel's K split (0 when it does not split)
+size_t gemm_big_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                        int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        void* workspace, hipStream_t stream);

@@ -358,10 +358,11 @@ def test_gemm_small(r, group, M):
 
 @pytest.mark.parametrize("r", [8, 4, 2])
 @pytest.mark.parametrize("group", ["K", 128])
-@pytest.mark.parametrize("M", [65, 130, 255])
+@pytest.mark.parametrize("M", [65, 100, 127, 128, 255])
 def test_gemm_mid_batch_split_k(r, group, M):
-    """64 < M < 256 with few output tiles and a long K: K is cut into slices
-    (33 iterations of 128, the last slice short), summed in slice order."""
+    """M > 64 with few output tiles and a long K: K is cut into slices, summed
+    in slice order.  65..127: the tiled kernel (33 iterations of 128, 7 slices,
+    the last short); from 128: the prefill kernel (66 of 64, 7 slices)."""
     n, k = 300, 4224
     g = k if group == "K" else 128
     assert mq.gemm_workspace_bytes(M, n, k, g) > 0
@@ -401,6 +402,25 @@ def test_gemm_prefill_full_size(r):
     cols = _sample_rows(n, 128)
     ref = oracle.linear(xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], 128, r)
     compare(y[:, cols], ref, f"prefill r{r}")
+
+
+@pytest.mark.parametrize("r", [4, 2, 8, 6, 3])
+@pytest.mark.parametrize("M,group", [(2048, 128), (512, 128), (512, "K")])
+def test_gemm_prefill_down_projection_split_k(r, M, group):
+    """The 4096-wide down projection (K = 14336) has 128 (M = 2048) or 32
+    (M = 512) tiles of 256 x 256, so K is split over workgroups (2 or 8
+    slices) and the slices are summed in order; sampled columns."""
+    n, k = 4096, 14336
+    g = k if group == "K" else 128
+    assert mq.gemm_workspace_bytes(M, n, k, g) > 0
+    note(f"gemm prefill down projection r={r} M={M} g={g}")
+    m = quantized("prefill", n, k, g, matrix=1)
+    xb = inputs.activations_bf16("prefill", M, k, matrix=1)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    cols = _sample_rows(n, 128, seed=r)
+    ref = oracle.linear(xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], g, r)
+    compare(y[:, cols], ref, f"prefill down r{r} M{M} g{g}")
 
 
 # ---------------------------------------------------------------- Mix'n'Match
