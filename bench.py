@@ -241,6 +241,25 @@ def run_rows(torch, mq, inputs, dev):
                         "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
     rows["gemm_prefill_M2048"] = pre
     del c5, a5, z5, x5, y5
+    # a4, the 4096-wide down projection of the same layer (K = 14336): 128
+    # output tiles at M = 2048, so the kernel splits K over workgroups
+    w = inputs.device_gaussian_weights("prefill", K, N, dev, matrix=1)
+    c6, a6, z6 = mq.quantize(w, 128)
+    del w
+    xb = inputs.activations_bf16("prefill", M, N, matrix=1)
+    x6 = torch.from_numpy(xb.view("int16")).to(dev)
+    y6 = torch.empty((M, K), dtype=torch.float32, device=dev)
+    ws6 = torch.empty(mq.gemm_workspace_bytes(M, K, N, 128), dtype=torch.uint8, device=dev)
+    down = {}
+    for r in (4, 2, 8):
+        pl = mq.pack(c6, r)
+        us = time_loop(torch, lambda i: mq.gemm(pl, r, a6, z6, 128, K, N, x6, out=y6,
+                                                workspace=ws6), 10)
+        tf = 2 * M * N * K / us / 1e6
+        down[f"r{r}"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+                         "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    rows["gemm_prefill_down_M2048"] = down
+    del c6, a6, z6, x6, y6, ws6
     # a5: Mix'n'Match stack, 32 Mistral-7B layers, batch 1
     rows["mixnmatch_mistral7b_32l"] = run_stack(torch, mq, inputs, dev)
     # f2: Extra-Precision r = 2 on the Gemma MLP: the sparse addition after the plane product
