@@ -374,6 +374,21 @@ def test_gemm_mid_batch_split_k(r, group, M):
     compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
 
 
+@pytest.mark.parametrize("r", [8, 6, 4])
+def test_gemm_prefill_split_k_odd_iterations(r):
+    """Per-channel K = 4160: 65 iterations of 64 on the prefill kernel, split
+    into 7 slices of 10 (whole groups) whose last one has 5 and ends
+    mid-pair; M = 256 rows (one tile row), N = 300 (two tiles, ragged)."""
+    M, n, k = 256, 300, 4160
+    assert mq.gemm_workspace_bytes(M, n, k, k) == 7 * M * n * 4
+    note(f"gemm prefill split-K odd r={r}")
+    m = quantized("mistral_small", n, k, k, matrix=9)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=9, heavy_channels=8)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], k, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], k, r), f"gemm odd r{r}")
+
+
 @pytest.mark.parametrize("r", [4, 2])
 @pytest.mark.parametrize("M", [16, 64, 96, 200])
 @pytest.mark.parametrize("shape", inputs.MISTRAL_SMALL_SHAPES)
