@@ -305,8 +305,6 @@ def test_overflow_lists_bit_exact(r):
 def test_extra_precision_product(r, group, M):
     """plane product at r + the sparse addition = the unclamped (errata Eq. 8)
     product of the oracle."""
-    if M > 8 and r in (3, 6):
-        pytest.skip("r = 3 and 6 are served at M <= 8 only")
     n, k = 260, 1024
     g = k if group == "K" else 128
     note(f"extra precision r={r} g={g} M={M}")
