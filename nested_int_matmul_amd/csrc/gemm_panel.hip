@@ -286,12 +286,13 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   }
 }
 
-// y = sum over S slices of the partial tiles, in slice order.
+// y = sum over S slices of the partial tiles, in slice order.  16-byte
+// vectors only when every slice starts 16-byte aligned (count % 4 == 0).
 __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ part,
                                                      float* __restrict__ y, int64_t count,
                                                      int S) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t n4 = count >> 2;
+  const int64_t n4 = (count & 3) ? 0 : count >> 2;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     f32x4 v = reinterpret_cast<const f32x4*>(part)[i];
     for (int sl = 1; sl < S; ++sl) v += reinterpret_cast<const f32x4*>(part + sl * count)[i];

@@ -48,7 +48,7 @@ def test_status_strings_and_sizes(L):
 
 def test_split_k_plans(L):
     """K splits and their workspace (one fp32 [M, N] partial per slice).
-    Tiled kernel (64 < M < 256, r = 2, 4, 8): 128 x 128 tiles, K in iterations
+    Tiled kernel (64 < M < 128, r = 2, 4, 8): 128 x 128 tiles, K in iterations
     of 128, split in powers of two while the tiles stay under 512
     (per-channel) or 256 (group-128) workgroups and each slice keeps 4
     iterations.  Prefill kernel (M >= 128, and r = 3, 6 above M = 64):

@@ -372,6 +372,23 @@ def test_gemm_mid_batch_split_k(r, group, M):
     compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
 
 
+@pytest.mark.parametrize("r", [4, 8, 3])
+@pytest.mark.parametrize("M", [9, 33, 65, 131])
+def test_gemm_split_k_unaligned_slices(r, M):
+    """K splits whose partial slices are M * N = odd floats long (N = 301),
+    so slice starts are not 16-byte aligned: the panel kernel (M = 9, 33),
+    the tiled kernel (65; the prefill kernel at r = 3) and the prefill kernel
+    (131), group 128, K = 4224."""
+    n, k = 301, 4224
+    assert mq.gemm_workspace_bytes(M, n, k, 128) > 0
+    note(f"gemm split-K unaligned slices r={r} M={M}")
+    m = quantized("mistral_small", n, k, 128, matrix=10)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=10, heavy_channels=8)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 128, r), f"gemm r{r} M{M}")
+
+
 @pytest.mark.parametrize("r", [8, 6, 4])
 def test_gemm_prefill_split_k_odd_iterations(r):
     """Per-channel K = 4160: 65 iterations of 64 on the prefill kernel, split
