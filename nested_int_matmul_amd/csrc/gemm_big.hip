@@ -1,5 +1,5 @@
-// Large-batch product (prefill-sized M) against r-bit planes on bf16 matrix
-// cores:
+// Batched product (M >= 65 activation rows, up to prefill sizes) against
+// r-bit planes on bf16 matrix cores:
 //   y[m, n] = sum_g alpha[n, g] * (2^(8-r) * sum_{k in g} x[m, k] u[n, k]
 //                                   - (z[n, g] + shift) * sum_{k in g} x[m, k])
 // with u the exact bf16 operand of the index t (mq_device.h), which equals
@@ -7,10 +7,11 @@
 // ("Matryoshka Quantization" explainer, §3.4: Eq. 6 and Eq. 1).
 //
 // Tiling (gfx950, v_mfma_f32_32x32x16_bf16, A = activations, B = weights):
-//  - a workgroup of 8 waves computes a 256 x 256 tile of y; each wave owns a
-//    128 (m) x 64 (n) sub-tile = 4 x 2 blocks of 32 x 32 (128 fp32
-//    accumulators per lane);
-//  - each K iteration covers 64 codes: the activation tile (256 x 64 bf16) and
+//  - a workgroup of 8 waves computes a BM x 256 tile of y (BM = 256, or 128
+//    up to M = 128, where a 256-row tile would be half padding); each wave
+//    owns a BM/2 (m) x 64 (n) sub-tile = BM/64 x 2 blocks of 32 x 32 (128 or
+//    64 fp32 accumulators per lane);
+//  - each K iteration covers 64 codes: the activation tile (BM x 64 bf16) and
 //    the packed weight tile (256 rows x 64 codes) are brought into LDS with
 //    buffer-to-LDS loads, double-buffered, one barrier per iteration; the
 //    activation and weight tiles are XOR-swizzled in 16-byte chunks so that
@@ -42,12 +43,14 @@ namespace mq {
 
 namespace big {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BN = 256, BK = 64;
 constexpr int WAVES = 8, THREADS = 64 * WAVES;
-constexpr int MB = 4, NB = 2;               // 32x32 blocks per wave (m, n)
-constexpr int XT_BYTES = BM * BK * 2;       // staged activation tile
-template <int R>
+constexpr int NB = 2;  // 32x32 blocks per wave along n
+// BM = 256 or 128 rows per tile (the 128-row tiles for small M)
+template <int R, int BM>
 struct Cfg {
+  static constexpr int MB = BM / 64;          // 32x32 blocks per wave along m (2 m-waves)
+  static constexpr int XT_BYTES = BM * BK * 2;  // staged activation tile
   // r = 3 and 6: a high-bit plane (rows of K * RH / 8 bytes) followed by a
   // low-bit plane (rows of K * RL / 8 bytes); staged as two sub-tiles
   static constexpr bool SPLIT = (R == 3 || R == 6);
@@ -82,13 +85,14 @@ __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, ui
       r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
-template <int R, bool GROUPED>
+template <int R, bool GROUPED, int BM>
 __global__ void __launch_bounds__(THREADS)
     gemm_big_kernel(const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
                     const float* __restrict__ zero, const uint16_t* __restrict__ x,
                     float* __restrict__ y, int M, int N, int K, int group, int mt, int nt,
                     int its) {
-  using C = Cfg<R>;
+  using C = Cfg<R, BM>;
+  constexpr int MB = C::MB, XT_BYTES = C::XT_BYTES;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* xs0 = smem;                                  // [2][BM][128 B] swizzled
   unsigned char* ws0 = smem + 2 * XT_BYTES;                   // [2][BN][WROW]
@@ -198,9 +202,10 @@ __global__ void __launch_bounds__(THREADS)
   auto scale = [&](int j, int g) -> float { return alpha[(int64_t)nld[j] * G + g]; };
   auto zraw = [&](int j, int g) -> float { return zero[(int64_t)nld[j] * G + g]; };
 
-  // row sums of x: thread (row = 32 * wave + lane % 32, half = lane / 32)
-  // sums 32 codes per iteration
-  const int srow = wave * 32 + (lane & 31), shalf = lane >> 5;
+  // row sums of x: RPW rows per wave; thread (row = RPW * wave + lane % RPW,
+  // part = lane / RPW) sums CPT 16-byte chunks (8 codes each) per iteration
+  constexpr int RPW = BM / WAVES, CPT = 8 / (64 / RPW);
+  const int srow = wave * RPW + lane % RPW, spart = lane / RPW;
   float srun = 0.f;
   const uint32_t ones = 0x3F803F80u;
 
@@ -215,7 +220,7 @@ __global__ void __launch_bounds__(THREADS)
   }
 
   // the first group's update reads these (cz = 0): keep them finite
-  if (GROUPED && shalf == 0) sxg[srow] = 0.f;
+  if (GROUPED && spart == 0) sxg[srow] = 0.f;
   if (GROUPED) {
     // the slice's first window; and the next one when the slice starts
     // inside a window (the loop issues a window only at a window's start)
@@ -261,16 +266,17 @@ __global__ void __launch_bounds__(THREADS)
         const unsigned char* xs = xs0 + buf * XT_BYTES;
         float sp = 0.f;
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const int c = shalf * 4 + c4;
+        for (int c4 = 0; c4 < CPT; ++c4) {
+          const int c = spart * CPT + c4;
           const u32x4 w = *reinterpret_cast<const u32x4*>(xs + srow * 128 + ((c ^ xsw(srow)) * 16));
 #pragma unroll
           for (int e = 0; e < 4; ++e) sp = dot2_bf16(w[e], ones, sp);
         }
-        sp += __shfl_xor(sp, 32);
+#pragma unroll
+        for (int off = RPW; off < 64; off <<= 1) sp += __shfl_xor(sp, off);
         srun += sp;
         if (GROUPED && it2 == IPG - 1) {
-          if (shalf == 0) sxg[srow] = srun;
+          if (spart == 0) sxg[srow] = srun;
           srun = 0.f;
         }
       }
@@ -315,7 +321,7 @@ __global__ void __launch_bounds__(THREADS)
         bf16x8 a[MB], b[NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-          const int row = wm * 128 + i * 32 + l32;
+          const int row = wm * (MB * 32) + i * 32 + l32;
           const int c = 4 * s + kk;
           const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 128 + ((c ^ xsw(row)) * 16));
           a[i] = __builtin_bit_cast(bf16x8, v);
@@ -335,7 +341,7 @@ __global__ void __launch_bounds__(THREADS)
           if (GROUPED && it2 == 0 && kk == 0) {
 #pragma unroll
             for (int eq = 0; eq < 4; ++eq)
-              sv[eq] = *reinterpret_cast<const f32x4*>(sxg + wm * 128 + i * 32 + eq * 8 + s * 4);
+              sv[eq] = *reinterpret_cast<const f32x4*>(sxg + wm * (MB * 32) + i * 32 + eq * 8 + s * 4);
           }
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
@@ -361,7 +367,7 @@ __global__ void __launch_bounds__(THREADS)
   }
 
   // ---- epilogue: last group's (or the only group's) zero-point term and scale
-  if (!GROUPED && shalf == 0) sxg[srow] = srun;
+  if (!GROUPED && spart == 0) sxg[srow] = srun;
   __syncthreads();
   const int glast = GROUPED ? ie / IPG - 1 : 0;  // the slice's last group
   float av[NB];
@@ -374,7 +380,7 @@ __global__ void __launch_bounds__(THREADS)
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int eq = 0; eq < 4; ++eq) {
-      const int row = wm * 128 + i * 32 + eq * 8 + s * 4;
+      const int row = wm * (MB * 32) + i * 32 + eq * 8 + s * 4;
       const f32x4 sv = *reinterpret_cast<const f32x4*>(sxg + row);
 #pragma unroll
       for (int e3 = 0; e3 < 4; ++e3) {
@@ -392,18 +398,26 @@ __global__ void __launch_bounds__(THREADS)
 
 }  // namespace big
 
+// Tile height: 128 rows up to kBig128MaxM rows of x (fewer padded rows and
+// twice the tiles), 256 above.  Measured at the Mistral shapes: 128-row
+// tiles take 65 <= M <= 128 25-35% faster than a 128 x 128 register-staged
+// kernel did, and gain nothing over 256-row tiles from M = 160.
+constexpr int kBig128MaxM = 128;
+static int big_rows(int64_t M) { return M <= kBig128MaxM ? 128 : 256; }
+
 // K split: while the tiles fill fewer than kBigTarget CUs (one workgroup
 // each) and every slice keeps at least kBigMinIters iterations (whole groups)
 constexpr int kBigTarget = 256, kBigMinIters = 8;
 
 struct BigPlan {
-  int mt, nt, slices, its;
+  int bm, mt, nt, slices, its;
 };
 
 static BigPlan plan_big(int64_t M, int64_t N, int64_t K) {
   using namespace big;
   BigPlan p;
-  p.mt = (int)((M + BM - 1) / BM);
+  p.bm = big_rows(M);
+  p.mt = (int)((M + p.bm - 1) / p.bm);
   p.nt = (int)((N + BN - 1) / BN);
   const int iters = (int)(K / BK);
   int s = 1;
@@ -419,33 +433,43 @@ size_t gemm_big_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return p.slices > 1 ? (size_t)p.slices * M * N * 4 : 0;
 }
 
+template <int R, int BM>
+static hipError_t launch_big_t(const BigPlan& p, const uint8_t* packed, const float* alpha,
+                               const float* zero, int64_t group, int64_t N, int64_t K,
+                               const uint16_t* x, int64_t M, float* out, hipStream_t s) {
+  using namespace big;
+  using C = Cfg<R, BM>;
+  const bool grouped = group != K;
+  // the LDS limit is raised once per process and kernel (function-local
+  // statics are initialized exactly once, also when several host threads launch)
+  static const hipError_t attr_g = hipFuncSetAttribute(
+      (const void*)gemm_big_kernel<R, true, BM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      C::LDS_GROUPED);
+  static const hipError_t attr_c = hipFuncSetAttribute(
+      (const void*)gemm_big_kernel<R, false, BM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      C::LDS);
+  if (attr_g != hipSuccess) return attr_g;
+  if (attr_c != hipSuccess) return attr_c;
+  dim3 grid((unsigned)(p.mt * p.nt), (unsigned)p.slices), block(THREADS);
+  if (grouped)
+    hipLaunchKernelGGL((gemm_big_kernel<R, true, BM>), grid, block, C::LDS_GROUPED, s, packed,
+                       alpha, zero, x, out, (int)M, (int)N, (int)K, (int)group, p.mt, p.nt,
+                       p.its);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<R, false, BM>), grid, block, C::LDS, s, packed, alpha,
+                       zero, x, out, (int)M, (int)N, (int)K, (int)group, p.mt, p.nt, p.its);
+  return hipGetLastError();
+}
+
 template <int R>
 static hipError_t launch_big_r(const uint8_t* packed, const float* alpha, const float* zero,
                                int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                                float* y, void* workspace, hipStream_t s) {
-  using namespace big;
   const BigPlan p = plan_big(M, N, K);
-  const bool grouped = group != K;
-  const size_t lds = grouped ? Cfg<R>::LDS_GROUPED : Cfg<R>::LDS;
-  // the LDS limit is raised once per process and kernel (function-local
-  // statics are initialized exactly once, also when several host threads launch)
-  static const hipError_t attr_g = hipFuncSetAttribute(
-      (const void*)gemm_big_kernel<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      Cfg<R>::LDS_GROUPED);
-  static const hipError_t attr_c = hipFuncSetAttribute(
-      (const void*)gemm_big_kernel<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      Cfg<R>::LDS);
-  if (attr_g != hipSuccess) return attr_g;
-  if (attr_c != hipSuccess) return attr_c;
   float* out = p.slices > 1 ? static_cast<float*>(workspace) : y;
-  dim3 grid((unsigned)(p.mt * p.nt), (unsigned)p.slices), block(THREADS);
-  if (grouped)
-    hipLaunchKernelGGL((gemm_big_kernel<R, true>), grid, block, lds, s, packed, alpha, zero, x,
-                       out, (int)M, (int)N, (int)K, (int)group, p.mt, p.nt, p.its);
-  else
-    hipLaunchKernelGGL((gemm_big_kernel<R, false>), grid, block, lds, s, packed, alpha, zero, x,
-                       out, (int)M, (int)N, (int)K, (int)group, p.mt, p.nt, p.its);
-  hipError_t e = hipGetLastError();
+  hipError_t e = p.bm == 128
+                     ? launch_big_t<R, 128>(p, packed, alpha, zero, group, N, K, x, M, out, s)
+                     : launch_big_t<R, 256>(p, packed, alpha, zero, group, N, K, x, M, out, s);
   if (e != hipSuccess || p.slices == 1) return e;
   return launch_reduce_slices(out, y, M * N, p.slices, s);
 }

@@ -47,28 +47,23 @@ def test_status_strings_and_sizes(L):
 
 
 def test_split_k_plans(L):
-    """K splits and their workspace (one fp32 [M, N] partial per slice).
-    Tiled kernel (64 < M < 128, r = 2, 4, 8): 128 x 128 tiles, K in iterations
-    of 128, split in powers of two while the tiles stay under 512
-    (per-channel) or 256 (group-128) workgroups and each slice keeps 4
-    iterations.  Prefill kernel (M >= 128, and r = 3, 6 above M = 64):
-    256 x 256 tiles, iterations of 64, split while under 256 workgroups with
-    8 iterations per slice, slices of whole groups (an even count).  Between
-    M = 64 and 128 the size covers both kernels (r is not an argument)."""
+    """K splits and their workspace (one fp32 [M, N] partial per slice) for
+    M >= 65: tiles of 128 (M <= 128) or 256 rows by 256 columns, K in
+    iterations of 64, split in powers of two while the tiles stay under 256
+    workgroups and every slice keeps 8 iterations; slices hold whole groups
+    (an even count of iterations)."""
     ws = L.mq_gemm_workspace_bytes
-    # 4096 x 14336, M = 96: tiled 32 tiles, 112 iterations -> 16 slices of 7
-    # (per-channel) or 8 of 14 (g128); prefill 16 tiles, 224 iterations -> 16
+    # 4096 x 14336, M = 96: 16 tiles, 224 iterations -> 16 slices of 14
     assert ws(96, 4096, 14336, 14336) == 16 * 96 * 4096 * 4
     assert ws(96, 4096, 14336, 128) == 16 * 96 * 4096 * 4
-    # tiled: 33 iterations over 6 tiles, 8-way split of 5 -> 7 slices;
-    # prefill: 66 iterations over 2 tiles, 8-way split of 10 -> 7 slices
+    # 66 iterations over 2 tiles: 8-way split of 9, rounded to 10 -> 7 slices
     assert ws(100, 300, 4224, 4224) == 7 * 100 * 300 * 4
     assert ws(130, 300, 4224, 4224) == 7 * 130 * 300 * 4
     assert ws(256, 300, 4224, 4224) == 7 * 256 * 300 * 4
     # 14336 x 4096 at M = 200: prefill 56 tiles, 64 iterations -> 4 slices of 16
     assert ws(200, 14336, 4096, 4096) == 4 * 200 * 14336 * 4
     assert ws(200, 14336, 4096, 128) == 4 * 200 * 14336 * 4
-    # 10 iterations of 64: no slice of 8 fits twice; tiled: 5 of 128
+    # 10 iterations of 64: no slice of 8 fits twice
     assert ws(130, 200, 640, 640) == 0
     assert ws(100, 200, 640, 640) == 0
     # prefill at M = 2048: 448 tiles fill the chip; the 4096-wide down

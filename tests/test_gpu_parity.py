@@ -358,9 +358,9 @@ def test_gemm_small(r, group, M):
 @pytest.mark.parametrize("group", ["K", 128])
 @pytest.mark.parametrize("M", [65, 100, 127, 128, 255])
 def test_gemm_mid_batch_split_k(r, group, M):
-    """M > 64 with few output tiles and a long K: K is cut into slices, summed
-    in slice order.  65..127: the tiled kernel (33 iterations of 128, 7 slices,
-    the last short); from 128: the prefill kernel (66 of 64, 7 slices)."""
+    """M > 64 with few output tiles and a long K: K (66 iterations of 64) is
+    cut into 7 slices of 10, the last one short, summed in slice order;
+    128-row tiles up to M = 128, 256-row tiles above."""
     n, k = 300, 4224
     g = k if group == "K" else 128
     assert mq.gemm_workspace_bytes(M, n, k, g) > 0
@@ -376,9 +376,9 @@ def test_gemm_mid_batch_split_k(r, group, M):
 @pytest.mark.parametrize("M", [9, 33, 65, 131])
 def test_gemm_split_k_unaligned_slices(r, M):
     """K splits whose partial slices are M * N = odd floats long (N = 301),
-    so slice starts are not 16-byte aligned: the panel kernel (M = 9, 33),
-    the tiled kernel (65; the prefill kernel at r = 3) and the prefill kernel
-    (131), group 128, K = 4224."""
+    so slice starts are not 16-byte aligned: the panel kernel (M = 9, 33)
+    and the M >= 65 kernel with 128-row (65) and 256-row (131) tiles, group
+    128, K = 4224."""
     n, k = 301, 4224
     assert mq.gemm_workspace_bytes(M, n, k, 128) > 0
     note(f"gemm split-K unaligned slices r={r} M={M}")
