@@ -209,9 +209,8 @@ __global__ void __launch_bounds__(THREADS)
   float srun = 0.f;
   const uint32_t ones = 0x3F803F80u;
 
-  // scale factors of the next group transition, loaded one iteration ahead
-  // (before that iteration's staging loads, so using them never waits for
-  // the staging)
+  // factors of the next group transition (zero-point term and rescale),
+  // formed at each group's last iteration from the LDS scale window
   float cz[NB], rho[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
