@@ -215,8 +215,10 @@ def run_rows(torch, mq, inputs, dev):
                 xb = inputs.activations_bf16("mistral_small", M2, K2, heavy_channels=8)
                 x2 = torch.from_numpy(xb.view("int16")).to(dev)
                 y2 = torch.empty((M2, N2), dtype=torch.float32, device=dev)
+                ws2 = torch.empty(max(1, mq.gemm_workspace_bytes(M2, N2, K2, 128)),
+                                  dtype=torch.uint8, device=dev)
                 us = time_loop(torch, lambda i: mq.gemm(pls[i % nc], r, a2, z2, 128, N2, K2, x2,
-                                                        out=y2), 40)
+                                                        out=y2, workspace=ws2), 40)
                 b = linear_bytes(N2, K2, r, 128, M2)
                 small[f"M{M2}_N{N2}_K{K2}_r{r}"] = {
                     "us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
@@ -233,9 +235,12 @@ def run_rows(torch, mq, inputs, dev):
     x5 = torch.from_numpy(xb.view("int16")).to(dev)
     y5 = torch.empty((M, N), dtype=torch.float32, device=dev)
     pre = {}
+    ws5 = torch.empty(max(1, mq.gemm_workspace_bytes(M, N, K, 128)), dtype=torch.uint8,
+                      device=dev)
     for r in (4, 2, 8, 6, 3):
         pl = mq.pack(c5, r)
-        us = time_loop(torch, lambda i: mq.gemm(pl, r, a5, z5, 128, N, K, x5, out=y5), 10)
+        us = time_loop(torch, lambda i: mq.gemm(pl, r, a5, z5, 128, N, K, x5, out=y5,
+                                                workspace=ws5), 10)
         tf = 2 * M * N * K / us / 1e6
         pre[f"r{r}"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
                         "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
