@@ -89,32 +89,69 @@ __device__ __forceinline__ uint32_t slice_byte(uint32_t q) {
   return t > hi ? hi : t;
 }
 
+// slice_byte of the four bytes of w at once (r = 2, 4): with h = q >> 1,
+// (h + 2^(6-r)) >> (7-r) is the same rounded quotient (q + 2^(7-r)) >> (8-r)
+// and stays below 256 in every byte, so no carry crosses bytes; the one
+// value above 2^r - 1 (2^r itself) is clamped by subtracting its top bit.
 template <int R>
-__global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ codes, u32x4* __restrict__ out,
-                                                   int64_t n_out16) {
-  constexpr int IN16 = 8 / R;  // 16-byte input vectors per 16-byte output vector
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_out16;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    u32x4 in[IN16];
+__device__ __forceinline__ uint32_t slice4(uint32_t w) {
+  constexpr uint32_t ONES = 0x01010101u;
+  const uint32_t h = (w >> 1) & 0x7F7F7F7Fu;
+  const uint32_t v = ((h + ONES * (1u << (6 - R))) >> (7 - R)) & (ONES * ((2u << R) - 1u));
+  return v - ((v >> R) & ONES);
+}
+
+// One 16-byte vector of codes (16 consecutive codes of a row) per thread and
+// step at r = 2 and 8, so every wave load is one contiguous 1 KiB; two
+// adjacent vectors at r = 4, so that each thread stores 16 bytes (measured
+// faster than 8-byte stores).  Bytewise for r = 2, 4: a dword d of four indices (one per
+// byte) becomes d | d >> (16 - R), whose byte 0 holds the indices of codes 0
+// and 2 (code 0 in the low bits) and byte 1 those of codes 1 and 3; byte
+// permutes then gather the even codes into the low half of each output word
+// and the odd codes into the high half (v_perm_b32: selector values 0-3 pick
+// bytes of the second source, 4-7 bytes of the first).  At r = 8 the same
+// layout swaps bytes 1 and 2 of every dword (codes 0, 2 low; 1, 3 high).
+template <int R>
+__global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ codes,
+                                                   uint8_t* __restrict__ out, int64_t n_in16) {
+  if constexpr (R == 4) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_in16 / 2;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const u32x4 in0 = __builtin_nontemporal_load(codes + 2 * i);
+      const u32x4 in1 = __builtin_nontemporal_load(codes + 2 * i + 1);
+      u32x4 o;
 #pragma unroll
-    for (int j = 0; j < IN16; ++j) in[j] = __builtin_nontemporal_load(codes + i * IN16 + j);
-    uint32_t o[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t acc = 0;
-      constexpr int PER_WORD = 32 / R;  // indices per output word
-#pragma unroll
-      for (int e = 0; e < PER_WORD; ++e) {
-        const int flat = w * PER_WORD + e;  // input byte index within this thread's span
-        const uint32_t word = in[flat / 16][(flat / 4) & 3];
-        const uint32_t q = (word >> (8 * (flat & 3))) & 0xffu;
-        const int field = (e & 1) ? 16 + (e >> 1) * R : (e >> 1) * R;
-        acc |= slice_byte<R>(q) << field;
+      for (int w = 0; w < 4; ++w) {  // codes 8w .. 8w + 7: dwords 2w, 2w + 1 of the pair
+        const u32x4& v = w < 2 ? in0 : in1;
+        const uint32_t t0 = slice4<4>(v[(2 * w) & 3]), t1 = slice4<4>(v[(2 * w + 1) & 3]);
+        o[w] = __builtin_amdgcn_perm(t1 | (t1 >> 12), t0 | (t0 >> 12), 0x05010400u);
       }
-      o[w] = acc;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + i);
     }
-    u32x4 ov = {o[0], o[1], o[2], o[3]};
-    __builtin_nontemporal_store(ov, out + i);
+  } else {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_in16;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const u32x4 in = __builtin_nontemporal_load(codes + i);
+      if constexpr (R == 8) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_perm(in[k], in[k], 0x03010200u);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + i);
+      } else {
+        static_assert(R == 2, "byte-aligned precisions only");
+        uint32_t tp[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t t = slice4<2>(in[k]);
+          tp[k] = t | (t >> 14);
+        }
+        // 2-bit pairs of two dwords side by side, then their nibbles merged
+        const uint32_t u01 = __builtin_amdgcn_perm(tp[1], tp[0], 0x05010400u);
+        const uint32_t u23 = __builtin_amdgcn_perm(tp[3], tp[2], 0x05010400u);
+        const uint32_t o = __builtin_amdgcn_perm(u23 | (u23 >> 4), u01 | (u01 >> 4), 0x06020400u);
+        __builtin_nontemporal_store(o, reinterpret_cast<uint32_t*>(out) + i);
+      }
+    }
   }
 }
 
@@ -189,13 +226,12 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_
                          packed, n_thr, lo_base);
     return hipGetLastError();
   }
-  const int64_t out_bytes = N * K * r / 8;
-  const int64_t n16 = out_bytes / 16;
+  const int64_t n16 = N * K / 16;  // input vectors of 16 codes (K % 64 == 0: even)
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   if (blocks < 1) blocks = 1;
   const u32x4* in = reinterpret_cast<const u32x4*>(codes);
-  u32x4* out = reinterpret_cast<u32x4*>(packed);
+  uint8_t* out = packed;
   switch (r) {
     case 2:
       hipLaunchKernelGGL(pack_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
