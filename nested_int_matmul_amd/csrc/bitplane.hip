@@ -336,8 +336,32 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
   }
 }
 
+// delta swap: exchange the bits of x under m with the bits sh above them
+__device__ __forceinline__ uint32_t dswap(uint32_t x, int sh, uint32_t m) {
+  const uint32_t t = (x ^ (x >> sh)) & m;
+  return x ^ t ^ (t << sh);
+}
+// 8 x 8 bit transpose of 8 bytes (lo: rows 0-3, hi: rows 4-7, row k = byte
+// k): afterwards byte j holds bit j of every row, row k at bit k.  Swaps of
+// 1-bit, 2-bit and 4-bit blocks; the last one crosses the two dwords.
+__device__ __forceinline__ void transpose8x8(uint32_t& lo, uint32_t& hi) {
+  lo = dswap(lo, 7, 0x00AA00AAu);
+  hi = dswap(hi, 7, 0x00AA00AAu);
+  lo = dswap(lo, 14, 0x0000CCCCu);
+  hi = dswap(hi, 14, 0x0000CCCCu);
+  const uint32_t t = (lo ^ (hi << 4)) & 0xF0F0F0F0u;
+  lo ^= t;
+  hi ^= t >> 4;
+}
+
 // codes [N][K] -> planes [8][N][K/8]; one thread per output word of a row
-// (32 codes: 128G + 32s + 0..31 of a superblock), one word per plane.
+// (32 codes: 128G + 32s + 0..31 of a superblock), one word per plane.  Bit
+// 16h + i of plane p's word is bit p of code 2i + h: byte permutes
+// (v_perm_b32: selector values 0-3 pick bytes of the second source, 4-7 of
+// the first) split the even codes from the odd ones, an 8 x 8 bit transpose
+// of each group of 8 gives one byte per plane, and a 4 x 4 byte transpose
+// places the four bytes of each plane (even codes 0-14, 16-30, odd codes
+// 1-15, 17-31).
 __global__ void __launch_bounds__(256) pack_bitplanes_kernel(const uint8_t* __restrict__ codes,
                                                              int N, int K,
                                                              uint8_t* __restrict__ planes) {
@@ -354,20 +378,29 @@ __global__ void __launch_bounds__(256) pack_bitplanes_kernel(const uint8_t* __re
     const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
     const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
     const uint32_t dw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    // E[j]: even codes 8j .. 8j + 6 of dwords 2j, 2j + 1; O[j]: the odd ones
+    uint32_t E[4], O[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      E[j] = __builtin_amdgcn_perm(dw[2 * j + 1], dw[2 * j], 0x06040200u);
+      O[j] = __builtin_amdgcn_perm(dw[2 * j + 1], dw[2 * j], 0x07050301u);
+    }
+    transpose8x8(E[0], E[1]);  // even codes 0-14: byte p = plane p
+    transpose8x8(E[2], E[3]);  // even codes 16-30
+    transpose8x8(O[0], O[1]);  // odd codes 1-15
+    transpose8x8(O[2], O[3]);  // odd codes 17-31
     uint32_t w[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) w[p] = 0u;
-    // dword a holds codes 4a .. 4a+3 (byte b): code 4a + b has i = 2a + (b >> 1),
-    // h = b & 1, so its bit goes to 16h + i: b = 0 -> 2a, 1 -> 16 + 2a, 2 -> 2a + 1,
-    // 3 -> 17 + 2a
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const uint32_t x = (dw[a] >> p) & 0x01010101u;
-        const uint32_t y = (x & 1u) | ((x & 0x100u) << 8) | ((x >> 15) & 2u) | ((x >> 7) & 0x20000u);
-        w[p] |= y << (2 * a);
-      }
+    for (int half = 0; half < 2; ++half) {  // planes 4 half .. 4 half + 3
+      const uint32_t a = __builtin_amdgcn_perm(E[2 + half], E[half], 0x05010400u);
+      const uint32_t b = __builtin_amdgcn_perm(E[2 + half], E[half], 0x07030602u);
+      const uint32_t c = __builtin_amdgcn_perm(O[2 + half], O[half], 0x05010400u);
+      const uint32_t d = __builtin_amdgcn_perm(O[2 + half], O[half], 0x07030602u);
+      w[4 * half + 0] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+      w[4 * half + 1] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+      w[4 * half + 2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+      w[4 * half + 3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+    }
 #pragma unroll
     for (int p = 0; p < 8; ++p) out[p * plane_words + t] = w[p];
   }
