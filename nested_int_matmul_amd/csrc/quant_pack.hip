@@ -78,18 +78,11 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, 
 // half in bits [j*r, j*r + r) of that half (so that one AND-OR per register
 // yields operand pairs of consecutive k, see mq_device.h).  Rows need no
 // special handling: K is a multiple of 64, so the flat packing of the [N, K]
-// array is the row-by-row packing.  Each thread writes 16 output bytes (one
-// 128-bit store) from 128/r input bytes; the loop is grid-strided.
+// array is the row-by-row packing.  The loops are grid-strided.
 // ---------------------------------------------------------------------------
-template <int R>
-__device__ __forceinline__ uint32_t slice_byte(uint32_t q) {
-  if (R == 8) return q;
-  uint32_t t = (q + (1u << (7 - R))) >> (8 - R);
-  uint32_t hi = (1u << R) - 1u;
-  return t > hi ? hi : t;
-}
 
-// slice_byte of the four bytes of w at once (r = 2, 4): with h = q >> 1,
+// The index t = min((q + 2^(7-r)) >> (8-r), 2^r - 1) (Eq. 6, rounding half
+// up) of the four bytes of w at once (r = 2, 3, 4, 6): with h = q >> 1,
 // (h + 2^(6-r)) >> (7-r) is the same rounded quotient (q + 2^(7-r)) >> (8-r)
 // and stays below 256 in every byte, so no carry crosses bytes; the one
 // value above 2^r - 1 (2^r itself) is clamped by subtracting its top bit.
@@ -155,55 +148,77 @@ __global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ cod
   }
 }
 
+// One packed word from dwords of b-bit indices, one index per byte (b = 4:
+// 2 dwords, 2: 4 dwords, 1: 8 dwords), in the word layout above: d | d >>
+// (16 - b) puts the indices of codes 0 and 2 in byte 0 and of codes 1 and 3
+// in byte 1; byte permutes and shifts then merge them, even codes into the
+// low half, odd codes into the high half.
+__device__ __forceinline__ uint32_t word_of4(const uint32_t* t) {
+  return __builtin_amdgcn_perm(t[1] | (t[1] >> 12), t[0] | (t[0] >> 12), 0x05010400u);
+}
+__device__ __forceinline__ uint32_t word_of2(const uint32_t* t) {
+  uint32_t tp[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tp[k] = t[k] | (t[k] >> 14);
+  const uint32_t u01 = __builtin_amdgcn_perm(tp[1], tp[0], 0x05010400u);
+  const uint32_t u23 = __builtin_amdgcn_perm(tp[3], tp[2], 0x05010400u);
+  return __builtin_amdgcn_perm(u23 | (u23 >> 4), u01 | (u01 >> 4), 0x06020400u);
+}
+__device__ __forceinline__ uint32_t word_of1(const uint32_t* t) {
+  uint32_t v[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {  // 4 indices (2 even, 2 odd) per byte pair -> nibbles
+    const uint32_t u = __builtin_amdgcn_perm(t[2 * a + 1] | (t[2 * a + 1] >> 15),
+                                             t[2 * a] | (t[2 * a] >> 15), 0x05010400u);
+    v[a] = u | (u >> 6);
+  }
+  const uint32_t w01 = __builtin_amdgcn_perm(v[1], v[0], 0x06020400u);
+  const uint32_t w23 = __builtin_amdgcn_perm(v[3], v[2], 0x06020400u);
+  return __builtin_amdgcn_perm(w23 | (w23 >> 4), w01 | (w01 >> 4), 0x06020400u);
+}
+
 // r = 3 and r = 6: the index t is split into its high bits t >> r_lo (a plane
 // of width r - r_lo) and its low bits (width r_lo = 1 or 2), each packed in
 // the word layout above; the high plane of all rows comes first, then the low
-// plane.  Each thread takes 128 / r_hi consecutive codes: 16 bytes of the high
-// plane and 16 * r_lo / r_hi bytes of the low plane.
+// plane.  Each thread takes 32 consecutive codes (two 16-byte loads): 4 r_hi
+// bytes of the high plane and 4 r_lo bytes of the low plane.
 template <int R>
 __global__ void __launch_bounds__(256) pack_split_kernel(const u32x4* __restrict__ codes,
                                                          uint8_t* __restrict__ out,
                                                          int64_t n_thr, int64_t lo_base) {
   constexpr int RL = R == 6 ? 2 : 1, RH = R - RL;
-  constexpr int CODES = 128 / RH;  // codes per thread
+  constexpr int CODES = 32;  // codes per thread
   constexpr int IN16 = CODES / 16;
-  constexpr int LW = CODES * RL / 32;  // low-plane words per thread (2 for both)
+  constexpr int HW = RH, LW = RL;  // high- and low-plane words per thread
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_thr;
        i += (int64_t)gridDim.x * blockDim.x) {
     u32x4 in[IN16];
 #pragma unroll
     for (int j = 0; j < IN16; ++j) in[j] = __builtin_nontemporal_load(codes + i * IN16 + j);
-    auto index_of = [&](int flat) -> uint32_t {
-      const uint32_t word = in[flat / 16][(flat / 4) & 3];
-      return slice_byte<R>((word >> (8 * (flat & 3))) & 0xffu);
-    };
-    uint32_t h[4], l[LW];
+    // indices of 4 codes per dword (bytewise), split into high and low fields
+    constexpr int DW = CODES / 4;
+    uint32_t hi[DW], lo[DW];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t acc = 0;
-      constexpr int PER_WORD = 32 / RH;
-#pragma unroll
-      for (int e = 0; e < PER_WORD; ++e) {
-        const int field = (e & 1) ? 16 + (e >> 1) * RH : (e >> 1) * RH;
-        acc |= (index_of(w * PER_WORD + e) >> RL) << field;
-      }
-      h[w] = acc;
+    for (int k = 0; k < DW; ++k) {
+      const uint32_t t = slice4<R>(in[k >> 2][k & 3]);
+      hi[k] = (t >> RL) & (0x01010101u * ((1u << RH) - 1u));
+      lo[k] = t & (0x01010101u * ((1u << RL) - 1u));
     }
+    uint32_t h[HW], l[LW];
 #pragma unroll
-    for (int w = 0; w < LW; ++w) {
-      uint32_t acc = 0;
-      constexpr int PER_WORD = 32 / RL;
+    for (int w = 0; w < HW; ++w) h[w] = RH == 4 ? word_of4(hi + 2 * w) : word_of2(hi + 4 * w);
 #pragma unroll
-      for (int e = 0; e < PER_WORD; ++e) {
-        const int field = (e & 1) ? 16 + (e >> 1) * RL : (e >> 1) * RL;
-        acc |= (index_of(w * PER_WORD + e) & ((1u << RL) - 1u)) << field;
-      }
-      l[w] = acc;
+    for (int w = 0; w < LW; ++w) l[w] = RL == 2 ? word_of2(lo + 4 * w) : word_of1(lo + 8 * w);
+    if constexpr (R == 6) {
+      const u32x4 hv = {h[0], h[1], h[2], h[3]};
+      const u32x2 lv = {l[0], l[1]};
+      *reinterpret_cast<u32x4*>(out + i * 16) = hv;
+      *reinterpret_cast<u32x2*>(out + lo_base + i * 8) = lv;
+    } else {
+      const u32x2 hv = {h[0], h[1]};
+      *reinterpret_cast<u32x2*>(out + i * 8) = hv;
+      *reinterpret_cast<uint32_t*>(out + lo_base + i * 4) = l[0];
     }
-    u32x4 hv = {h[0], h[1], h[2], h[3]};
-    u32x2 lv = {l[0], l[1]};
-    *reinterpret_cast<u32x4*>(out + i * 16) = hv;
-    *reinterpret_cast<u32x2*>(out + lo_base + i * (LW * 4)) = lv;
   }
 }
 
@@ -211,8 +226,7 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_
                        hipStream_t stream) {
   if (r == 3 || r == 6) {
     const int rh = r == 6 ? 4 : 2;
-    const int64_t codes_per_thr = 128 / rh;
-    const int64_t n_thr = N * K / codes_per_thr;
+    const int64_t n_thr = N * K / 32;  // 32 codes per thread
     int64_t blocks = (n_thr + 255) / 256;
     if (blocks > 256 * 64) blocks = 256 * 64;
     if (blocks < 1) blocks = 1;
