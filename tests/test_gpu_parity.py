@@ -404,6 +404,24 @@ def test_gemm_prefill_split_k_odd_iterations(r):
     compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], k, r), f"gemm odd r{r}")
 
 
+@pytest.mark.parametrize("r", [4, 6])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [9, 40])
+def test_gemm_small_batch_ragged_last_panel(r, group, M):
+    """N = 14000, K = 4096 on the small-batch kernel: 55 panels of 256 rows
+    (the last one 176 rows) x 4 K slices; sampled rows include the last 230."""
+    n, k = 14000, 4096
+    g = k if group == "K" else 128
+    note(f"gemm small batch ragged last panel r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=11)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=11, heavy_channels=8)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([_sample_rows(n, 200, seed=M), np.arange(n - 230, n)]))
+    ref = oracle.linear(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], g, r)
+    compare(y[:, rows], ref, f"ragged panel r{r} g{g} M{M}")
+
+
 @pytest.mark.parametrize("r", [4, 2])
 @pytest.mark.parametrize("M", [16, 64, 96, 200])
 @pytest.mark.parametrize("shape", inputs.MISTRAL_SMALL_SHAPES)
