@@ -403,12 +403,11 @@ def run_stack(torch, mq, inputs, dev, n_layers=32):
     H = inputs.MISTRAL_LAYER["q"][0]
     ws = torch.empty(mq.mixnmatch_workspace_bytes(arr, 1), dtype=torch.uint8, device=dev)
     xb = inputs.activations_bf16("mistral_stack", 1, H)
-    x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16).float()
-    h = x.clone()
+    x = torch.from_numpy(xb.view("int16")).to(dev)
+    h = torch.empty((1, H), dtype=torch.float32, device=dev)
 
     def fwd(i):
-        h.copy_(x)
-        mq.mixnmatch_forward(arr, h, ws)
+        mq.mixnmatch_forward(arr, x, ws, out=h)
 
     us = time_loop(torch, fwd, 10, warmup=2)
     b = codes_bytes + meta_bytes
@@ -417,6 +416,85 @@ def run_stack(torch, mq, inputs, dev, n_layers=32):
            "r_pattern": "".join(str(r) for r in rs), "avg_bits": sum(rs) / len(rs)}
     del layers, arr, ws
     torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- measured peaks
+
+class Peaks:
+    """The probes of libmq_peaks.so (include/mq_peaks.h): the achievable HBM
+    read rate for a given byte count (rotating over >= 1 GiB of buffers, the
+    best of a few grid sizes), the dense bf16 matrix-core rate, and the
+    per-launch cadence of an empty kernel, timed with HIP events on the
+    launch stream."""
+
+    def __init__(self, torch, dev):
+        import ctypes
+
+        from nested_int_matmul_amd import build as _b
+
+        self.torch, self.dev = torch, dev
+        L = ctypes.CDLL(_b.PEAKS_LIB)
+        vp = ctypes.c_void_p
+        L.mqp_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+        L.mqp_mfma_loop.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+        L.mqp_mfma_loop_flops.restype = ctypes.c_double
+        L.mqp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.mqp_empty.argtypes = [vp]
+        self.L, self.vp = L, vp
+        self.stream = torch.cuda.current_stream()
+        self.sp = vp(self.stream.cuda_stream)
+
+    def _time(self, fn, n):
+        torch = self.torch
+        for i in range(3):
+            fn(i)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for i in range(n):
+            fn(i)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n  # us per launch
+
+    def hbm_read(self, nbytes):
+        """Best GB/s reading nbytes per launch, rotating buffers."""
+        torch = self.torch
+        nbytes = (nbytes + 4095) // 4096 * 4096
+        ncopy = max(2, -(-ROTATE_BYTES // nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=self.dev) for _ in range(ncopy)]
+        sink = torch.empty(16384, dtype=torch.int32, device=self.dev)
+        best = 0.0
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            def fn(i):
+                assert self.L.mqp_stream_read(self.vp(bufs[i % ncopy].data_ptr()), nbytes, blocks,
+                                              self.vp(sink.data_ptr()), self.sp) == 0
+            us = self._time(fn, 30)
+            best = max(best, nbytes / us / 1e3)
+        del bufs
+        return best
+
+    def mfma_tflops(self):
+        torch = self.torch
+        blocks, iters = 1024, 2000
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=self.dev)
+
+        def fn(i):
+            assert self.L.mqp_mfma_loop(self.vp(out.data_ptr()), blocks, iters, self.sp) == 0
+
+        us = self._time(fn, 10)
+        return self.L.mqp_mfma_loop_flops(blocks, iters) / us / 1e6
+
+    def empty_launch_us(self):
+        return self._time(lambda i: self.L.mqp_empty(self.sp), 200)
+
+
+def measured_peaks(torch, dev, sizes):
+    P = Peaks(torch, dev)
+    out = {"hbm_read_GBs": {str(k): round(P.hbm_read(b), 1) for k, b in sizes.items()},
+           "bf16_mfma_TFLOPs": round(P.mfma_tflops(), 1),
+           "empty_launch_us": round(P.empty_launch_us(), 3)}
     return out
 
 
@@ -502,11 +580,29 @@ def main():
     launch_us = res["total_ms"] * 1e3 / args.steps
     achieved = res["step_bytes"] / (launch_us * 1e-6) / 1e9
     traffic = traffic_for(sha256(GEMV_SOURCE), "mixed")
+    # measured ceilings: HBM read rate over the same byte counts (the step,
+    # and one MLP at each r), the bf16 matrix-core rate, the launch cadence
+    mlp_bytes = {r: sum(linear_bytes(m["N"], m["K"], r, m["K"], 1) for m in res["mats"])
+                 for r in RS}
+    log("measured peaks: HBM read, bf16 MFMA, empty launch")
+    peaks = measured_peaks(torch, dev, {"step": res["step_bytes"],
+                                        **{f"mlp_r{r}": b for r, b in mlp_bytes.items()}})
+    read_step = peaks["hbm_read_GBs"]["step"]
+    per_r = {}
+    for r, us in res["per_r_us"].items():
+        a = mlp_bytes[r] / us / 1e3
+        per_r[f"r{r}"] = {"launch_us": round(us, 3), "bytes": mlp_bytes[r],
+                          "achieved": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
+                          "frac_of_measured_read":
+                              round(a / peaks["hbm_read_GBs"][f"mlp_r{r}"], 4)}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "skinny_kernel<per-channel> (9 products, r = 8/4/2, one launch)",
+                "kernel": "mq::skinny_kernel<false, false> (9 products, r = 8/4/2, one launch)",
                 "launch_us": round(launch_us, 3), "bytes_per_launch": res["step_bytes"],
-                "single_r_launch_us": {f"r{r}": round(v, 3) for r, v in res["per_r_us"].items()}}
+                "measured_read_peak": read_step,
+                "frac_of_measured_read": round(achieved / read_step, 4),
+                "per_r_single_mlp_launch": per_r,
+                "measured_peaks": peaks}
     del res
 
     if args.copy_calib:

@@ -29,9 +29,8 @@
  *    nothing is enqueued and no output is touched.  A failed launch returns
  *    MQ_ERR_HIP and records the hipError_t (see mq_last_hip_error).  Faults
  *    during execution surface at the caller's next synchronization.
- *  - Entry points other than the explicitly allocating ones allocate no
- *    device memory; the library keeps no state except cached device
- *    properties.  Calls are thread-safe.
+ *  - No entry point allocates device memory.  The library keeps no state
+ *    except cached device properties.  Calls are thread-safe.
  */
 #ifndef MQ_H
 #define MQ_H
@@ -76,7 +75,9 @@ size_t mq_packed_bytes(int64_t N, int64_t K, int r);
  *   alpha = fp32((max v - min v) / 255),  z = fp32(-min v / alpha),
  *   q = clamp(floor(v / alpha + z + 1/2), 0, 255),
  * evaluated in IEEE float64 from the stored fp32 alpha and z.  A constant
- * vector gets alpha = 1, z = -min (all codes 0).
+ * vector gets alpha = 1, z = -min (all codes 0); so does a vector whose range
+ * is so small that its fp32 alpha would be 0 or subnormal (below 2^-126), so
+ * every alpha written is a normal fp32 number.
  *   w      fp32 [N, K], finite values
  *   codes  uint8 [N, K] (output)
  *   alpha  fp32 [N, K/group] (output), zero fp32 [N, K/group] (output)
@@ -113,7 +114,13 @@ mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* pa
  *   y[m, n] = sum_k x[m, k] * (S(q[n, k], r) - z[n, g]) * alpha[n, g],
  *   g = k / group,
  * with the slice read from `packed` (the output of mq_pack for the same r),
- * bf16 x, fp32 accumulation and an fp32 result.
+ * bf16 x, fp32 accumulation and an fp32 result.  The weight is the sliced
+ * code dequantized with the int8 code's own alpha and z: the "Matryoshka
+ * Quantization" explainer, §3.4 "The Bit-Slicing Operator" (Eq. 6; a sliced
+ * value is used in computation like an int8 value) and "Quantization
+ * Primitives" (Eq. 1, dequantization alpha * (q - z)).  At batch 1 the time is
+ * set by moving the planes out of HBM (the explainer's §2 "Context").
+ * alpha must hold finite normal fp32 numbers (as mq_quantize writes them).
  *   packed  uint8 [N, K*r/8], 16-byte aligned
  *   alpha, zero  fp32 [N, K/group]
  *   x       bf16 bits [M, K], 16-byte aligned
@@ -160,8 +167,14 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
 
 /*
  * mq_gemm: the same product for any number of activation rows M >= 1 (small
- * batches and prefill), on bf16 matrix cores with fp32 accumulation.  Same
- * definitions and layouts as mq_gemv; M <= 8 takes the mq_gemv kernel.
+ * batches and prefill), on bf16 matrix cores with fp32 accumulation:
+ *   y[m, n] = sum_k x[m, k] * (S(q[n, k], r) - z[n, g]) * alpha[n, g]
+ * (the explainer's §3.4, Eq. 6 slicing and the Eq. 1 dequantization with the
+ * int8 code's alpha and z; group 128 is the per-group granularity of the
+ * "Pith review of ROSAQ").  Same definitions and layouts as mq_gemv; M <= 8
+ * takes the mq_gemv kernel.  alpha must hold finite normal fp32 numbers whose
+ * ratio between consecutive groups of a row is finite (true of every alpha
+ * mq_quantize writes for weights below 2^100 in magnitude).
  * Every r in {2, 3, 4, 6, 8} is served at every M (r = 3 and 6 from their
  * high- and low-bit planes).
  *   workspace  device scratch of at least mq_gemm_workspace_bytes(M, N, K, group)
@@ -171,6 +184,9 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
  *              few output columns, e.g. a 4096-wide down projection)
  * Sizes: M >= 1, N >= 1, K >= 64, K % 64 == 0, K <= 65536.
  */
+/* Workspace bytes of mq_gemm.  It takes N as well as M, K and group because
+ * the workspace holds one fp32 [M, N] partial product per K slice; 0 when the
+ * shape is served without a K split. */
 size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
 mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                   int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
@@ -278,12 +294,26 @@ mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, i
                                          size_t* offsets);
 
 /*
- * mq_mixnmatch_forward: run n_layers layers in place on the fp32 residual
- * stream h [M, H] (16-byte aligned).  1 <= M <= 8, 1 <= n_layers.
- * `layers` is a HOST array read during the call only.
+ * mq_mixnmatch_forward: run n_layers layers on the bf16 input x [M, H]:
+ * h = x (exact in fp32), then every layer in order; the final residual
+ * stream is written to h_out (fp32 [M, H]).  x and h_out 16-byte aligned and
+ * not overlapping.  1 <= M <= 8, 1 <= n_layers.  `layers` is a HOST array
+ * read during the call only.
  */
-mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, int64_t M,
-                               void* workspace, size_t workspace_bytes, void* stream);
+mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, const uint16_t* x,
+                               int64_t M, float* h_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * mq_mixnmatch_forward_inplace: the same layers run on an fp32 residual
+ * stream h [M, H] that the caller already holds (updated in place), to
+ * continue a stack over several calls (a block of layers per call, e.g. one
+ * pipeline stage, or one layer at a time): h keeps full fp32 precision
+ * between calls, which a bf16 input could not.  Same constraints otherwise.
+ */
+mq_status mq_mixnmatch_forward_inplace(const mq_layer* layers, int n_layers, float* h,
+                                       int64_t M, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /*
  * Decode MLP block on sliced planes (the FFN, the main decode cost: the

@@ -30,8 +30,9 @@ EXPORTS = (
     "mq_status_string", "mq_last_hip_error", "mq_version", "mq_packed_bytes",
     "mq_quantize", "mq_pack", "mq_gemv", "mq_gemv_grouped", "mq_gemv_mixed",
     "mq_gemm_workspace_bytes",
-    "mq_gemm", "mq_mixnmatch_workspace_bytes", "mq_mixnmatch_workspace_offsets",
-    "mq_mixnmatch_forward", "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
+    "mq_gemm", "mq_mixnmatch_workspace_bytes",
+    "mq_mixnmatch_workspace_offsets", "mq_mixnmatch_forward", "mq_mixnmatch_forward_inplace",
+    "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
     "mq_bitplanes_bytes", "mq_pack_bitplanes", "mq_gemv_bitplanes",
     "mq_mlp_workspace_bytes", "mq_mlp_decode",
 )
@@ -123,7 +124,9 @@ def lib() -> ctypes.CDLL:
     L.mq_mixnmatch_workspace_offsets.argtypes = [ctypes.POINTER(Layer), i32, i64,
                                                  ctypes.POINTER(sz)]
     L.mq_mixnmatch_forward.restype = i32
-    L.mq_mixnmatch_forward.argtypes = [ctypes.POINTER(Layer), i32, vp, i64, vp, sz, vp]
+    L.mq_mixnmatch_forward.argtypes = [ctypes.POINTER(Layer), i32, vp, i64, vp, vp, sz, vp]
+    L.mq_mixnmatch_forward_inplace.restype = i32
+    L.mq_mixnmatch_forward_inplace.argtypes = [ctypes.POINTER(Layer), i32, vp, i64, vp, sz, vp]
     _LIB = L
     return L
 
@@ -163,6 +166,57 @@ def _bits16(x):
     raise TypeError("activations must be bf16 (or their 16-bit patterns)")
 
 
+# ------------------------------------------------------------- argument checks
+# The library sizes its buffer resources from the integer arguments and trusts
+# the pointers; these checks make every tensor agree with those arguments
+# (dtype, element count, one device) before a pointer is passed.
+
+def _need(t, name, dtypes, numel=None, shape=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"mq: {name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"mq: {name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"mq: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"mq: {name} has {t.numel()} elements, expected {numel}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"mq: tensors on different devices: {sorted(map(str, devs))}")
+
+
+def _check_weights(packed, alpha, zero, N, K, group, r, planes=False):
+    """Sizes of a plane and its scales against N, K, group and r.  A group
+    or r the library does not serve is left for the library to refuse
+    (MQ_ERR_GROUP / MQ_ERR_PRECISION, before it reads any buffer)."""
+    import torch
+
+    nb = N * K if planes else packed_bytes(N, K, r)
+    _need(packed, "packed" if not planes else "planes", (torch.uint8,),
+          numel=nb if nb > 0 else None)
+    g = (K // group) if group in (K, 128) and group > 0 and K % group == 0 else None
+    _need(alpha, "alpha", (torch.float32,), numel=None if g is None else N * g)
+    _need(zero, "zero", (torch.float32,), numel=None if g is None else N * g)
+
+
+def _check_xy(x, y, M, N, K):
+    import torch
+
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), shape=(M, K))
+    if y is not None:
+        _need(y, "out", (torch.float32,), numel=M * N)
+
+
+def _check_linear(p, name="linear", r=None):
+    """A linear's dict {"packed", "alpha", "zero", "N", "K", "group"} at r."""
+    _check_weights(p["packed"], p["alpha"], p["zero"], p["N"], p["K"], p["group"], r)
+
+
 # ----------------------------------------------------------------- entry points
 
 def packed_bytes(N: int, K: int, r: int) -> int:
@@ -174,6 +228,9 @@ def quantize(w, group: int, stream=None):
     [N, K], alpha fp32 [N, K/group], zero fp32 [N, K/group])."""
     import torch
 
+    _need(w, "w", (torch.float32,))
+    if w.dim() != 2:
+        raise ValueError("mq: w must be [N, K]")
     n, k = w.shape
     g = k // group if group else 0
     codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
@@ -189,9 +246,14 @@ def pack(codes, r: int, out=None, stream=None):
     r = 3 and 6 the two sub-planes are back to back in that byte array)."""
     import torch
 
+    _need(codes, "codes", (torch.uint8,))
+    if codes.dim() != 2:
+        raise ValueError("mq: codes must be [N, K]")
     n, k = codes.shape
     if out is None:
         out = torch.empty((n, k * r // 8), dtype=torch.uint8, device=codes.device)
+    _need(out, "out", (torch.uint8,), numel=packed_bytes(n, k, r))
+    _same_device(codes, out)
     _check(lib().mq_pack(_ptr(codes), n, k, r, _ptr(out), _stream(stream)), "mq_pack")
     return out
 
@@ -204,14 +266,21 @@ def gemv(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, s
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _check_weights(packed, alpha, zero, N, K, group, r)
+    _check_xy(x, out, m, N, K)
+    _same_device(packed, alpha, zero, x, out)
     _check(lib().mq_gemv(_ptr(packed), r, _ptr(alpha), _ptr(zero), group, N, K, _ptr(x), m,
                          _ptr(out), _stream(stream)), "mq_gemv")
     return out
 
 
-def _problem_array(problems):
+def _problem_array(problems, rs):
     arr = (GemvProblem * len(problems))()
     for i, p in enumerate(problems):
+        x = _bits16(p["x"])
+        _check_weights(p["packed"], p["alpha"], p["zero"], p["N"], p["K"], p["group"], rs[i])
+        _check_xy(x, p["y"], x.shape[0], p["N"], p["K"])
+        _same_device(p["packed"], p["alpha"], p["zero"], x, p["y"])
         arr[i] = GemvProblem(_ptr(p["packed"]), _ptr(p["alpha"]), _ptr(p["zero"]),
                              _ptr(_bits16(p["x"])), _ptr(p["y"]), p["N"], p["K"], p["group"])
     return arr
@@ -231,7 +300,13 @@ class GemvGroupedPlan:
     The caller keeps every tensor alive while the plan is in use."""
 
     def __init__(self, problems, r, M: int, stream=None):
-        self.arr = _problem_array(problems)
+        rs = list(r) if isinstance(r, (list, tuple)) else [r] * len(problems)
+        if len(rs) != len(problems):
+            raise ValueError("one r per problem")
+        for p in problems:
+            if p["x"].shape[0] != M:
+                raise ValueError(f"mq: x has {p['x'].shape[0]} rows, expected M = {M}")
+        self.arr = _problem_array(problems, rs)
         self.count, self.M = len(problems), M
         self.stream = _stream(stream)
         if isinstance(r, (list, tuple)):
@@ -256,6 +331,7 @@ def overflow_lists(codes, r: int, stream=None):
     col_idx (a setup step)."""
     import torch
 
+    _need(codes, "codes", (torch.uint8,))
     n, k = codes.shape
     row_ptr = torch.empty(n + 1, dtype=torch.int32, device=codes.device)
     _check(lib().mq_overflow_rows(_ptr(codes), n, k, r, _ptr(row_ptr), _stream(stream)),
@@ -272,7 +348,15 @@ def overflow_lists(codes, r: int, stream=None):
 def overflow_apply(row_ptr, col_idx, r: int, alpha, group: int, N: int, K: int, x, y,
                    stream=None):
     """y += the extra-precision correction (after a product at the same r)."""
+    import torch
+
     x = _bits16(x)
+    g = (K // group) if group in (K, 128) and group > 0 and K % group == 0 else None
+    _need(row_ptr, "row_ptr", (torch.int32,), numel=N + 1)
+    _need(col_idx, "col_idx", (torch.int32,))
+    _need(alpha, "alpha", (torch.float32,), numel=None if g is None else N * g)
+    _check_xy(x, y, x.shape[0], N, K)
+    _same_device(row_ptr, col_idx, alpha, x, y)
     ci = col_idx if col_idx.numel() else row_ptr  # any valid pointer when the list is empty
     _check(lib().mq_overflow_apply(_ptr(row_ptr), _ptr(ci), r, _ptr(alpha), group, N, K, _ptr(x),
                                    x.shape[0], _ptr(y), _stream(stream)), "mq_overflow_apply")
@@ -287,9 +371,12 @@ def pack_bitplanes(codes, out=None, stream=None):
     """The eight bit-planes of uint8 codes [N, K]: uint8 [8, N, K/8]."""
     import torch
 
+    _need(codes, "codes", (torch.uint8,))
     n, k = codes.shape
     if out is None:
         out = torch.empty((8, n, k // 8), dtype=torch.uint8, device=codes.device)
+    _need(out, "out", (torch.uint8,), numel=n * k)
+    _same_device(codes, out)
     _check(lib().mq_pack_bitplanes(_ptr(codes), n, k, _ptr(out), _stream(stream)),
            "mq_pack_bitplanes")
     return out
@@ -305,6 +392,9 @@ def gemv_bitplanes(planes, r: int, alpha, zero, group: int, N: int, K: int, x, e
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _check_weights(planes, alpha, zero, N, K, group, r, planes=True)
+    _check_xy(x, out, m, N, K)
+    _same_device(planes, alpha, zero, x, out)
     _check(lib().mq_gemv_bitplanes(_ptr(planes), r, int(bool(extra)), _ptr(alpha), _ptr(zero),
                                    group, N, K, _ptr(x), m, _ptr(out), _stream(stream)),
            "mq_gemv_bitplanes")
@@ -324,6 +414,9 @@ def gemm(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, w
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _check_weights(packed, alpha, zero, N, K, group, r)
+    _check_xy(x, out, m, N, K)
+    _same_device(packed, alpha, zero, x, out, workspace)
     need = gemm_workspace_bytes(m, N, K, group)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -341,6 +434,7 @@ def make_layers(layers):
         kw = {"r": L["r"]}
         for n in LAYER_LINEARS:
             p = L[n]
+            _check_linear(p, n, L["r"])
             kw[n] = Linear(_ptr(p["packed"]), _ptr(p["alpha"]), _ptr(p["zero"]),
                            p["N"], p["K"], p["group"])
         arr[i] = Layer(**kw)
@@ -370,6 +464,9 @@ def mlp_decode(up, gate, down, r: int, x, act="identity", workspace=None, out=No
     x = _bits16(x)
     m = x.shape[0]
     F, H = up["N"], up["K"]
+    for p, nm in ((up, "up"), (gate, "gate"), (down, "down")):
+        _check_linear(p, nm, r)
+    _check_xy(x, out, m, H, H)
     need = mlp_workspace_bytes(m, F)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -394,10 +491,44 @@ def mixnmatch_workspace_offsets(layer_arr, M: int):
     return list(off)
 
 
-def mixnmatch_forward(layer_arr, h, workspace, stream=None):
-    """Run the stack in place on the fp32 residual stream h [M, H]."""
-    m = h.shape[0]
+def _stack_h(layer_arr):
+    return int(layer_arr[0].q.N) if len(layer_arr) else 0
+
+
+def mixnmatch_forward(layer_arr, x, workspace, out=None, stream=None):
+    """Run the stack on bf16 x [M, H]: returns the final fp32 residual stream
+    h [M, H] (written to `out` when given)."""
+    import torch
+
+    x = _bits16(x)
+    m, H = x.shape
+    if H != _stack_h(layer_arr):
+        raise ValueError(f"mq: x has {H} columns, the stack's width is {_stack_h(layer_arr)}")
+    if out is None:
+        out = torch.empty((m, H), dtype=torch.float32, device=x.device)
+    _check_xy(x, out, m, H, H)
+    _need(workspace, "workspace", (torch.uint8,))
+    _same_device(x, out, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().mq_mixnmatch_forward(layer_arr, len(layer_arr), _ptr(h), m, _ptr(workspace),
-                                      ws_bytes, _stream(stream)), "mq_mixnmatch_forward")
+    _check(lib().mq_mixnmatch_forward(layer_arr, len(layer_arr), _ptr(x), m, _ptr(out),
+                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "mq_mixnmatch_forward")
+    return out
+
+
+def mixnmatch_forward_inplace(layer_arr, h, workspace, stream=None):
+    """Run the stack in place on an fp32 residual stream h [M, H] (to continue
+    a stack over several calls)."""
+    import torch
+
+    m, H = h.shape
+    if H != _stack_h(layer_arr):
+        raise ValueError(f"mq: h has {H} columns, the stack's width is {_stack_h(layer_arr)}")
+    _need(h, "h", (torch.float32,))
+    _need(workspace, "workspace", (torch.uint8,))
+    _same_device(h, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().mq_mixnmatch_forward_inplace(layer_arr, len(layer_arr), _ptr(h), m,
+                                              _ptr(workspace), ws_bytes, _stream(stream)),
+           "mq_mixnmatch_forward_inplace")
     return h

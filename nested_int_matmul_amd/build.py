@@ -19,9 +19,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmq.so")
+PEAKS_LIB = os.path.join(HERE, "libmq_peaks.so")
 
 SOURCES = ["quant_pack.hip", "gemv.hip", "gemm.hip", "gemm_panel.hip", "gemm_big.hip",
            "mixnmatch.hip", "extra.hip", "bitplane.hip", "abi.hip"]
+# measured-peak probes (a library of their own, loaded by bench.py only)
+PEAKS_SOURCES = ["peaks.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -44,13 +47,21 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile all sources and link libmq.so; returns the library path."""
+    """Compile all sources and link libmq.so and libmq_peaks.so; returns the
+    path of libmq.so."""
+    _build_lib(SOURCES, LIB, verbose, extra_flags)
+    _build_lib(PEAKS_SOURCES, PEAKS_LIB, verbose, extra_flags)
+    return LIB
+
+
+def _build_lib(sources, lib_path, verbose, extra_flags):
     cc = hipcc()
     flags = HIPCC_FLAGS + list(extra_flags or [])
+    name = os.path.basename(lib_path)
     with tempfile.TemporaryDirectory(prefix="mq_build_") as tmp:
         objs = []
         procs = []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             cmd = [cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -69,13 +80,12 @@ def build(verbose: bool = False, extra_flags=None) -> str:
                 print(out)
         if failed:
             msg = "\n".join(f"--- {s}\n{o}" for s, o in failed)
-            raise RuntimeError("libmq build failed:\n" + msg)
-        tmp_lib = os.path.join(tmp, "libmq.so")
+            raise RuntimeError(f"{name} build failed:\n" + msg)
+        tmp_lib = os.path.join(tmp, name)
         cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         subprocess.run(cmd, check=True)
-        shutil.move(tmp_lib, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
-    return LIB
+        shutil.move(tmp_lib, lib_path + ".tmp")
+        os.replace(lib_path + ".tmp", lib_path)
 
 
 if __name__ == "__main__":

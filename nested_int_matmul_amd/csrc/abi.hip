@@ -195,12 +195,30 @@ size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
   return mq::gemm_workspace_bytes(M, N, K, group);
 }
 
-mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
-                  int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace mq {
+
+mq_status record_hip_error(hipError_t e) { return hip_fail(e); }
+
+mq_status gemm_check(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                     int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                     const float* y) {
   mq_status s = check_product(packed, r, alpha, zero, group, N, K, x, y);
   if (s != MQ_OK) return s;
   if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+  return MQ_OK;
+}
+
+}  // namespace mq
+
+extern "C" {
+
+mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                  int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  mq_status s = mq::gemm_check(packed, r, alpha, zero, group, N, K, x, M, y);
+  if (s != MQ_OK) return s;
   const size_t need = mq::gemm_workspace_bytes(M, N, K, group);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MQ_ERR_WORKSPACE;
   s = check_device();
@@ -310,12 +328,17 @@ struct StackDims {
   int64_t H, Hkv, F;
 };
 
-bool linear_ok(const mq_linear& l, int64_t n, int64_t k, int r) {
-  if (!l.packed || !l.alpha || !l.zero) return false;
-  if (l.N != n || l.K != k) return false;
-  if (check_matrix(l.N, l.K, l.group, r) != MQ_OK) return false;
-  if (!aligned16(l.packed)) return false;
-  return true;
+// MQ_OK, or the status check_product would return for this linear's shape,
+// precision, group and pointer alignment (MQ_ERR_SHAPE on a shape mismatch)
+mq_status linear_ok(const mq_linear& l, int64_t n, int64_t k, int r) {
+  if (!l.packed || !l.alpha || !l.zero) return MQ_ERR_NULL;
+  if (l.N != n || l.K != k) return MQ_ERR_SHAPE;
+  mq_status s = check_matrix(l.N, l.K, l.group, r);
+  if (s != MQ_OK) return s;
+  if (!aligned16(l.packed)) return MQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(l.alpha) & 3u) || (reinterpret_cast<uintptr_t>(l.zero) & 3u))
+    return MQ_ERR_ALIGN;
+  return MQ_OK;
 }
 
 mq_status check_stack(const mq_layer* layers, int n_layers, int64_t M, StackDims* d) {
@@ -328,11 +351,11 @@ mq_status check_stack(const mq_layer* layers, int n_layers, int64_t M, StackDims
     for (const mq_linear* l : all)
       if (!l->packed || !l->alpha || !l->zero) return MQ_ERR_NULL;
     if (!valid_r(L.r)) return MQ_ERR_PRECISION;
-    if (!linear_ok(L.q, H, H, L.r) || !linear_ok(L.k, Hkv, H, L.r) ||
-        !linear_ok(L.v, Hkv, H, L.r) || !linear_ok(L.o, H, H, L.r) ||
-        !linear_ok(L.up, F, H, L.r) || !linear_ok(L.gate, F, H, L.r) ||
-        !linear_ok(L.down, H, F, L.r))
-      return MQ_ERR_SHAPE;
+    const int64_t want[7][2] = {{H, H}, {Hkv, H}, {Hkv, H}, {H, H}, {F, H}, {F, H}, {H, F}};
+    for (int j = 0; j < 7; ++j) {
+      const mq_status s = linear_ok(*all[j], want[j][0], want[j][1], L.r);
+      if (s != MQ_OK) return s;
+    }
   }
   d->H = H;
   d->Hkv = Hkv;
@@ -387,20 +410,23 @@ mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, i
   return MQ_OK;
 }
 
-mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, int64_t M,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// The layer loop of both stack entry points.  x == nullptr: h holds the
+// residual stream on entry; else h = x (bf16) first.
+mq_status run_stack(const mq_layer* layers, int n_layers, const uint16_t* x, float* h, int64_t M,
+                    void* workspace, size_t workspace_bytes, hipStream_t st) {
   StackDims d;
   mq_status s = check_stack(layers, n_layers, M, &d);
   if (s != MQ_OK) return s;
   if (!h) return MQ_ERR_NULL;
-  if (!aligned16(h)) return MQ_ERR_ALIGN;
+  if (!aligned16(h) || (x && !aligned16(x))) return MQ_ERR_ALIGN;
   size_t off[kStackBuffers], total;
   stack_offsets(d, M, off, &total);
   if (!workspace || workspace_bytes < total) return MQ_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MQ_ERR_ALIGN;
   s = check_device();
   if (s != MQ_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   uint16_t* a = reinterpret_cast<uint16_t*>(ws + off[0]);
   float* q = reinterpret_cast<float*>(ws + off[1]);
@@ -413,7 +439,8 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, i
   uint16_t* qb = reinterpret_cast<uint16_t*>(ws + off[8]);
   uint16_t* ugb = reinterpret_cast<uint16_t*>(ws + off[9]);
 
-  hipError_t e = mq::launch_rmsnorm_bf16(h, a, M, d.H, st);
+  hipError_t e = x ? mq::launch_load_rmsnorm_bf16(x, h, a, M, d.H, st)
+                   : mq::launch_rmsnorm_bf16(h, a, M, d.H, st);
   if (e != hipSuccess) return hip_fail(e);
   for (int i = 0; i < n_layers; ++i) {
     const mq_layer& L = layers[i];
@@ -448,6 +475,23 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, float* h, i
   return MQ_OK;
 }
 
+}  // namespace
+
+mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, const uint16_t* x,
+                               int64_t M, float* h_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!x) return MQ_ERR_NULL;
+  return run_stack(layers, n_layers, x, h_out, M, workspace, workspace_bytes,
+                   (hipStream_t)stream);
+}
+
+mq_status mq_mixnmatch_forward_inplace(const mq_layer* layers, int n_layers, float* h,
+                                       int64_t M, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return run_stack(layers, n_layers, nullptr, h, M, workspace, workspace_bytes,
+                   (hipStream_t)stream);
+}
+
 // ---- decode MLP block
 
 size_t mq_mlp_workspace_bytes(int64_t M, int64_t F) {
@@ -465,8 +509,9 @@ mq_status mq_mlp_decode(const mq_linear* up, const mq_linear* gate, const mq_lin
   if (!valid_r(r) || act < mq::kActIdentity || act > mq::kActGeluTanh) return MQ_ERR_PRECISION;
   if (M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
   const int64_t F = up->N, H = up->K;
-  if (!linear_ok(*up, F, H, r) || !linear_ok(*gate, F, H, r) || !linear_ok(*down, H, F, r))
-    return MQ_ERR_SHAPE;
+  for (const mq_status s0 :
+       {linear_ok(*up, F, H, r), linear_ok(*gate, F, H, r), linear_ok(*down, H, F, r)})
+    if (s0 != MQ_OK) return s0;
   if (up->group != gate->group) return MQ_ERR_GROUP;
   if (!aligned16(x) || !aligned16(y)) return MQ_ERR_ALIGN;
   const size_t need = mq_mlp_workspace_bytes(M, F);

@@ -28,7 +28,7 @@
 //    memory, each column's value is a cache line of its own (columns are G
 //    floats apart);
 //  - r = 3 and 6 stage a high-plane and a low-plane sub-tile per iteration
-//    and assemble u = 128 + t from both (8-byte low rows at r = 3 go through
+//    and assemble u = 2^r + t from both (8-byte low rows at r = 3 go through
 //    4-byte buffer-to-LDS loads);
 //  - tiles are mapped to XCDs so that the workgroups of one XCD share
 //    activation rows (its L2 keeps them);

@@ -14,7 +14,7 @@
 //    DEPTH steps ahead of use, and unpacks them into exact bf16 integers
 //    (mq_device.h).  One unpacked operand feeds MB matrix-core products.
 //    r = 3 and 6 (a high-bit and a low-bit plane) take 32 codes per lane per
-//    step from both planes and assemble u = 128 + t in the same registers.
+//    step from both planes and assemble u = 2^r + t in the same registers.
 //  - alpha and z of the panel's groups are staged in LDS with the
 //    activations; group-128 scales are applied at each group end in fp32
 //    (y += alpha 2^(8-r) P_g - alpha (z + shift) sum_g x), per-channel scales
@@ -167,21 +167,24 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   }
   __syncthreads();
 
-  // ---- per-128 sums of the staged activations: thread -> (row, 8 codes),
-  //      16 consecutive threads cover one group
+  // ---- per-128 sums of the staged activations: one thread per (row,
+  //      group) sums its 16 chunks of 8 in order (no cross-lane reduction;
+  //      consecutive lanes take consecutive rows, whose 16-byte reads fall
+  //      on distinct banks)
   {
     const uint32_t ones = 0x3F803F80u;
-    const int cpr = kpad >> 3;             // 8-code chunks per row
-    const int total = ROWS * cpr;
-    for (int b = tid; b < total; b += 64 * NW) {
-      const int m = b / cpr, c = b - m * cpr;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + c * 8);
+    for (int t = tid; t < ROWS * ngl; t += 64 * NW) {
+      const int m = t % ROWS, gl = t / ROWS;
+      const uint16_t* p = xs + (size_t)m * xstride + gl * 128;
+      u32x4 w[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) w[c] = *reinterpret_cast<const u32x4*>(p + c * 8);
       float sp = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sp = dot2_bf16(w[q], ones, sp);
+      for (int c = 0; c < 16; ++c)
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) sp += __shfl_xor(sp, off);
-      if ((c & 15) == 0 && (c >> 4) < ngl) sxs[(c >> 4) * ROWS + m] = sp;
+        for (int q = 0; q < 4; ++q) sp = dot2_bf16(w[c][q], ones, sp);
+      sxs[gl * ROWS + m] = sp;
     }
   }
   __syncthreads();

@@ -58,9 +58,9 @@ constexpr int kSkinnyWaves = 4;   // waves per workgroup
 
 template <int R>
 __device__ __forceinline__ bf16x8 unpack_op(const uint32_t* d, int i, const UnpackK& k,
-                                            const UnpackK36& k36, const R2MConst& k2) {
+                                            const UnpackK36& k36) {
   if (R == 4) return unpack_r4(d[i], k);
-  if (R == 2) return (i & 1) ? unpack_r2m<1>(d[i >> 1], k2) : unpack_r2m<0>(d[i >> 1], k2);
+  if (R == 2) return (i & 1) ? unpack_r2<1>(d[i >> 1], k) : unpack_r2<0>(d[i >> 1], k);
   if (R == 6) return unpack_r6(d[i], d[4 + (i >> 1)], i & 1, k36);  // 4 high, 2 low words
   if (R == 3) return unpack_r3(d[i >> 1], d[2], i, k36);             // 2 high, 1 low word
   return unpack_r8(d[2 * i], d[2 * i + 1]);
@@ -185,8 +185,6 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
   const UnpackK uk = UnpackK::make();
   UnpackK36 uk36;
   if constexpr (C::SPLIT) uk36 = UnpackK36::make();
-  R2MConst uk2;
-  if constexpr (R == 2) uk2 = R2MConst::make();
   // all lanes read activations: columns past M duplicate column M - 1 (ignored)
   const int xcol = col < M ? col : M - 1;
 
@@ -271,35 +269,24 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     for (int j = 0; j < C::DEPTH; ++j) buf[j] = LD::load(wr, loff(lo + j), loff_lo(lo + j));
     __syncthreads();
     if constexpr (GROUPED) {
-      // per group of 128: sum of x and of offset * x (16 consecutive blocks
-      // of 8 values per group, summed across lanes)
-      const int bpr = clen / PB;
-      const int total = M * bpr;
+      // per group of 128: sum of x and of offset * x, one thread per
+      // (row, group) summing its 16 blocks of 8 in order (no cross-lane
+      // reduction)
+      const int gl_n = clen / 128;
       const uint32_t ones = 0x3F803F80u;
-      for (int b0 = 0; b0 < total; b0 += blockDim.x) {
-        const int b = b0 + threadIdx.x;
-        float s = 0.f, so = 0.f;
-        int m = 0, kb = 0;
-        if (b < total) {
-          m = b / bpr;
-          kb = (b - m * bpr) * PB;
-          const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + kb);
+      for (int t = threadIdx.x; t < M * gl_n; t += blockDim.x) {
+        const int m = t / gl_n, gl = t - m * gl_n;
+        const uint16_t* p = xs + (size_t)m * xstride + gl * 128;
+        u32x4 w4[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            s = dot2_bf16(w4[q], ones, s);
-            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q, (kb >> 3) & 1), so);
-          }
-          if (R != 2) so = (float)Enc<R>::kOffset * s;
-        }
+        for (int c = 0; c < 16; ++c) w4[c] = *reinterpret_cast<const u32x4*>(p + c * PB);
+        float s = 0.f;
 #pragma unroll
-        for (int off = 1; off < 128 / PB; off <<= 1) {
-          s += __shfl_xor(s, off);
-          so += __shfl_xor(so, off);
-        }
-        if (b < total && (kb % 128) == 0) {
-          sxs[m * g_per_chunk + kb / 128] = s;
-          sxos[m * g_per_chunk + kb / 128] = so;
-        }
+        for (int c = 0; c < 16; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s = dot2_bf16(w4[c][q], ones, s);
+        sxs[m * g_per_chunk + gl] = s;
+        sxos[m * g_per_chunk + gl] = (float)Enc<R>::kOffset * s;
       }
       __syncthreads();  // the streaming loop reads other threads' group sums
     } else {
@@ -315,16 +302,10 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
         for (int bi = threadIdx.x; bi < bpr; bi += blockDim.x) {
           const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + bi * PB);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            s = dot2_bf16(w4[q], ones, s);
-            if (R == 2) so = dot2_bf16(w4[q], R2MOffset::pair_bits(q, bi & 1), so);
-          }
+          for (int q = 0; q < 4; ++q) s = dot2_bf16(w4[q], ones, s);
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          s += __shfl_xor(s, off);
-          if (R == 2) so += __shfl_xor(so, off);
-        }
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
         if (lane == 0) {
           part_s[wave] = s;
           part_so[wave] = so;
@@ -337,7 +318,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
             tso += part_so[w];
           }
           sxt[m] += ts;
-          sxot[m] += (R == 2) ? tso : (float)Enc<R>::kOffset * ts;
+          sxot[m] += (float)Enc<R>::kOffset * ts;
         }
         __syncthreads();
       }
@@ -359,7 +340,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
             for (int i = 0; i < C::MFMAS; ++i) {
               const u32x4 w = *reinterpret_cast<const u32x4*>(xp + 8 * i);
-              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36, uk2),
+              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36),
                                                              __builtin_bit_cast(bf16x8, w), part,
                                                              0, 0, 0);
             }
@@ -384,7 +365,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 #pragma unroll
           for (int i = 0; i < C::MFMAS; ++i) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(xp + 8 * i);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36, uk2),
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_op<R>(d, i, uk, uk36),
                                                            __builtin_bit_cast(bf16x8, w), part,
                                                            0, 0, 0);
           }

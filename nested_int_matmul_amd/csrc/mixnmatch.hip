@@ -14,17 +14,26 @@ namespace mq {
 constexpr int kNormThreads = 1024;
 
 // One workgroup per activation row.  Fixed-order reduction (deterministic).
-template <bool RESIDUAL, bool NORM>
+// LOAD: h = x first (bf16 x0, exact in fp32); RESIDUAL: h = h + o + d first.
+template <bool RESIDUAL, bool NORM, bool LOAD = false>
 __global__ void __launch_bounds__(kNormThreads) norm_kernel(float* __restrict__ h,
                                                             const float* __restrict__ o,
                                                             const float* __restrict__ d,
-                                                            uint16_t* __restrict__ a, int H) {
+                                                            uint16_t* __restrict__ a, int H,
+                                                            const uint16_t* __restrict__ x0 =
+                                                                nullptr) {
   __shared__ float wsum[kNormThreads / 64];
   const int m = blockIdx.x;
   float* hr = h + (int64_t)m * H;
   float ss = 0.f;
   for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    float v = hr[i];
+    float v;
+    if (LOAD) {
+      v = bf16_to_f32(x0[(int64_t)m * H + i]);
+      hr[i] = v;
+    } else {
+      v = hr[i];
+    }
     if (RESIDUAL) {
       v = v + o[(int64_t)m * H + i];
       v = v + d[(int64_t)m * H + i];
@@ -48,6 +57,13 @@ hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H
                                hipStream_t stream) {
   hipLaunchKernelGGL((norm_kernel<false, true>), dim3((unsigned)M), dim3(kNormThreads), 0, stream,
                      const_cast<float*>(h), nullptr, nullptr, a, (int)H);
+  return hipGetLastError();
+}
+
+hipError_t launch_load_rmsnorm_bf16(const uint16_t* x, float* h, uint16_t* a, int64_t M,
+                                    int64_t H, hipStream_t stream) {
+  hipLaunchKernelGGL((norm_kernel<false, true, true>), dim3((unsigned)M), dim3(kNormThreads), 0,
+                     stream, h, nullptr, nullptr, a, (int)H, x);
   return hipGetLastError();
 }
 

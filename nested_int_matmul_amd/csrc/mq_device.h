@@ -8,11 +8,15 @@
 // and apply alpha, z, 2^(8-r) in fp32 afterwards, so no weight is ever
 // rounded to bf16.
 //
-// For r = 2 and r = 4 the index is turned into a bf16 by placing its bits in
-// the top of the mantissa of the bf16 constant 2^r: the result is exactly
-// u = 2^r + t (one AND-OR per two values).  The offset folds into the zero
-// point: alpha * (2^(8-r) * u - (z + 256)).  For r = 8 the byte is converted
-// through fp32 (exact: every integer below 256 is a bf16), u = t.
+// For r < 8 the index is turned into a bf16 by placing its bits in the top
+// of the mantissa of the bf16 constant 2^r: the result is exactly
+// u = 2^r + t (one AND-OR per two values; r = 3 and 6 assemble the bits of
+// two planes the same way).  The offset folds into the zero point:
+// alpha * (2^(8-r) * u - (z + 256)), the same 256 on the int8 scale for
+// every r, so that the fp32 sums the kernels form stay within a small factor
+// of the dequantized weights (|S - z| + 256 on the int8 scale).  For r = 8
+// the byte is converted through fp32 (exact: every integer below 256 is a
+// bf16), u = t.
 //
 // Plane layout: a 32-bit word holds 32/r consecutive indices, the even-
 // positioned ones in its low 16 bits and the odd-positioned ones in its high
@@ -58,7 +62,7 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
 // (u * 2^(8-r) = S + shift).
 template <int R>
 struct Enc {
-  static constexpr int kOffset = R == 8 ? 0 : (R == 4 ? 16 : (R == 2 ? 4 : 128));
+  static constexpr int kOffset = R == 8 ? 0 : (1 << R);
   static constexpr float kStep = (float)(1 << (8 - R));                 // 2^(8-r)
   static constexpr float kOffsetShift = (float)kOffset * kStep;         // z' = z + shift
 };
@@ -122,55 +126,11 @@ __device__ __forceinline__ bf16x8 unpack_r2(uint32_t w, const UnpackK& k) {
 template <int H>
 __device__ __forceinline__ bf16x8 unpack_r2(uint32_t w) { return unpack_r2<H>(w, UnpackK::make()); }
 
-// --- r = 2 with the fields read where they are stored (10 instead of 16
-//     operations per word).  In a half, field j (element 2j or 2j+1 of the
-//     word) sits at bits [2j, 2j+2).  Fields 0, 1, 2 are read in place,
-//     fields 3, 4, 5 after >> 6 and fields 6, 7 after >> 12, each then at bit
-//     p = 0, 2 or 4 of its half, under the bf16 constant 2^(7-p) (128, 32, 8),
-//     whose mantissa step at bit p is 1: the operand is u = offset + t with a
-//     per-register offset.  Registers 0..3 of the operand of elements 0..7 of
-//     the word (h = 0) carry 128, 32, 8, 128; of elements 8..15 (h = 1) 32, 8,
-//     128, 32.  The caller removes sum_k offset(k) * x[k] (R2MOffset) in fp32.
-struct R2MConst {
-  uint32_t m0, m2, m4, c128, c32, c8;
-  __device__ __forceinline__ static R2MConst make() {
-    R2MConst k{0x00030003u, 0x000C000Cu, 0x00300030u, 0x43004300u, 0x42004200u, 0x41004100u};
-    asm volatile("" : "+v"(k.m0), "+v"(k.m2), "+v"(k.m4), "+v"(k.c128), "+v"(k.c32), "+v"(k.c8));
-    return k;
-  }
-};
-struct R2MOffset {
-  // bf16 pair (offset, offset) of register q of half h, for v_dot2 sums
-  __device__ __forceinline__ static uint32_t pair_bits(int q, int h) {
-    const int p = h ? (q == 2 ? 0 : (q == 1 ? 4 : 2)) : (q == 0 || q == 3 ? 0 : (q == 1 ? 2 : 4));
-    return p == 0 ? 0x43004300u : (p == 2 ? 0x42004200u : 0x41004100u);
-  }
-};
-
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
-template <int H>
-__device__ __forceinline__ bf16x8 unpack_r2m(uint32_t w, const R2MConst& k) {
-  const uint32_t w6 = w >> 6;
-  if (H == 0) {  // elements 0..7: fields 0, 1, 2 in place, field 3 from w >> 6
-    uint32_t p0 = and_or(w, k.m0, k.c128);
-    uint32_t p1 = and_or(w, k.m2, k.c32);
-    uint32_t p2 = and_or(w, k.m4, k.c8);
-    uint32_t p3 = and_or(w6, k.m0, k.c128);
-    return as_bf16x8(p0, p1, p2, p3);
-  } else {       // elements 8..15: fields 4, 5 from w >> 6, fields 6, 7 from w >> 12
-    const uint32_t w12 = w >> 12;
-    uint32_t p0 = and_or(w6, k.m2, k.c32);
-    uint32_t p1 = and_or(w6, k.m4, k.c8);
-    uint32_t p2 = and_or(w12, k.m0, k.c128);
-    uint32_t p3 = and_or(w12, k.m2, k.c32);
-    return as_bf16x8(p0, p1, p2, p3);
-  }
-}
-
 // --- r = 8: two words (8 bytes) -> one operand.  A word holds elements
 //     (e0, e2) in bytes 0, 1 and (e1, e3) in bytes 2, 3.
 __device__ __forceinline__ uint32_t bf16_pair_of_bytes(uint32_t lo, uint32_t hi) {
@@ -189,13 +149,15 @@ __device__ __forceinline__ bf16x8 unpack_r8(uint32_t w0, uint32_t w1) {
 
 // --- r = 6 and r = 3: the index is stored as two planes (high bits t >> r_lo
 //     in the word layout of width r - r_lo, low bits in that of width r_lo).
-//     The two fields are assembled at bits [0, r) of each half under the bf16
-//     constant 128, whose mantissa unit is 1: u = 128 + t, exact.
+//     The two fields are assembled at mantissa bits [7 - r, 7) of each half
+//     under the bf16 constant 2^r (64 or 8), whose mantissa step there is 1:
+//     u = 2^r + t, exact.
 struct UnpackK36 {
-  uint32_t mhi6, mlo6, mhi3, mlo3, one128;
+  uint32_t mhi6, mlo6, one6, mhi3, mlo3, one3;
   __device__ __forceinline__ static UnpackK36 make() {
-    UnpackK36 k{0x003C003Cu, 0x00030003u, 0x00060006u, 0x00010001u, 0x43004300u};
-    asm volatile("" : "+v"(k.mhi6), "+v"(k.mlo6), "+v"(k.mhi3), "+v"(k.mlo3), "+v"(k.one128));
+    UnpackK36 k{0x00780078u, 0x00060006u, 0x42804280u, 0x00600060u, 0x00100010u, 0x41004100u};
+    asm volatile("" : "+v"(k.mhi6), "+v"(k.mlo6), "+v"(k.one6), "+v"(k.mhi3), "+v"(k.mlo3),
+                 "+v"(k.one3));
     return k;
   }
 };
@@ -206,25 +168,29 @@ __device__ __forceinline__ uint32_t shift_signed(uint32_t w, int s) {  // s > 0:
 
 // r = 6, operand i (elements 8i .. 8i+7 of a lane's 32): hi = the 4-bit word
 // of those 8 elements, lo = the 2-bit word of elements 16*(i/2) .. +16.
+// Register j holds elements 2j, 2j+1: the low field (bits 2j' of the r = 2
+// layout) goes to bits 1..2, the high field (bits 4j of the r = 4 layout) to
+// bits 3..6, under 64.
 __device__ __forceinline__ bf16x8 unpack_r6(uint32_t hi, uint32_t lo, int i_odd,
                                             const UnpackK36& k) {
   uint32_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t l = and_or(lo >> (2 * j + 8 * i_odd), k.mlo6, k.one128);
-    p[j] = and_or(shift_signed(hi, 4 * j - 2), k.mhi6, l);
+    const uint32_t l = and_or(shift_signed(lo, 2 * j + 8 * i_odd - 1), k.mlo6, k.one6);
+    p[j] = and_or(shift_signed(hi, 4 * j - 3), k.mhi6, l);
   }
   return as_bf16x8(p[0], p[1], p[2], p[3]);
 }
 // r = 3, operand i of a lane's 32 elements: hi = the 2-bit word of elements
-// 16*(i/2) .. +16, lo = the 1-bit word of the lane's 32 elements.
+// 16*(i/2) .. +16, lo = the 1-bit word of the lane's 32 elements.  The low
+// bit goes to bit 4, the two high bits to bits 5..6, under 8.
 __device__ __forceinline__ bf16x8 unpack_r3(uint32_t hi, uint32_t lo, int i,
                                             const UnpackK36& k) {
   uint32_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t l = and_or(lo >> (4 * i + j), k.mlo3, k.one128);
-    p[j] = and_or(shift_signed(hi, 2 * (4 * (i & 1) + j) - 1), k.mhi3, l);
+    const uint32_t l = and_or(shift_signed(lo, 4 * i + j - 4), k.mlo3, k.one3);
+    p[j] = and_or(shift_signed(hi, 2 * (4 * (i & 1) + j) - 5), k.mhi3, l);
   }
   return as_bf16x8(p[0], p[1], p[2], p[3]);
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mq.h"
+
 namespace mq {
 
 // How a skinny-kernel problem reads its activations.
@@ -78,6 +80,12 @@ size_t gemm_big_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                        int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        void* workspace, hipStream_t stream);
+// Records e as this thread's last HIP error (mq_last_hip_error); returns MQ_ERR_HIP.
+mq_status record_hip_error(hipError_t e);
+// Argument checks of mq_gemm other than the workspace and the device.
+mq_status gemm_check(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                     int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                     const float* y);
 
 // Extra-Precision lists and the sparse addition.
 hipError_t launch_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int* row_ptr,
@@ -91,6 +99,9 @@ hipError_t launch_overflow_apply(const int* row_ptr, const int* col_idx, int r, 
 // Mix'n'Match helpers.
 hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H,
                                hipStream_t stream);
+// h = x (bf16, exact in fp32), then a = bf16(h / rms(h))
+hipError_t launch_load_rmsnorm_bf16(const uint16_t* x, float* h, uint16_t* a, int64_t M,
+                                    int64_t H, hipStream_t stream);
 hipError_t launch_residual_rmsnorm(float* h, const float* o, const float* d, uint16_t* a,
                                    int64_t M, int64_t H, hipStream_t stream);
 

@@ -13,7 +13,8 @@ namespace mq {
 // float64 from the stored fp32 alpha and z, in this order:
 //   alpha = fp32((max - min) / 255), z = fp32(-min / alpha),
 //   q = clamp(floor((w / alpha + z) + 0.5), 0, 255).
-// A constant vector takes alpha = 1, z = -min.
+// A constant vector takes alpha = 1, z = -min, and so does a vector whose
+// fp32 alpha would be zero or subnormal (no usable scale).
 // ---------------------------------------------------------------------------
 #pragma clang fp contract(off)
 __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ w, int64_t n_vec,
@@ -34,14 +35,13 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__
     mn = fminf(mn, __shfl_xor(mn, off));
     mx = fmaxf(mx, __shfl_xor(mx, off));
   }
-  float a32;
+  float a32 = (float)(((double)mx - (double)mn) / 255.0);
   float z32;
-  if (mx == mn) {
+  if (mx == mn || !(a32 >= 0x1p-126f)) {
+    // a constant vector, or a range too small for a normal fp32 scale
     a32 = 1.0f;
     z32 = -mn;
   } else {
-    double a64 = ((double)mx - (double)mn) / 255.0;
-    a32 = (float)a64;
     z32 = (float)(-(double)mn / (double)a32);
   }
   if (lane == 0) {

@@ -72,6 +72,10 @@ def quantize_minmax(w, group: int):
     rounded to fp32; the codes use those stored fp32 values, evaluated in
     float64; round() is floor(v + 1/2); a constant vector (max == min) takes
     alpha = 1, z = -min, so every code is 0 and dequantizes to min exactly.
+    The same holds for a vector whose range is too small for a normal fp32
+    alpha (alpha32 zero or subnormal, below 2^-126): Eq. 1 divides by alpha,
+    and such an alpha is no usable scale, so the vector is treated as
+    constant (every code 0, dequantized to min, off by less than 2^-118).
 
     Returns (q uint8 [N, K], alpha float32 [N, G], zero float32 [N, G]).
     """
@@ -86,7 +90,7 @@ def quantize_minmax(w, group: int):
     mx = wv.max(axis=2)
     alpha64 = (mx - mn) / float(levels)
     alpha32 = alpha64.astype(np.float32)
-    constant = (mx == mn)
+    constant = (mx == mn) | (alpha32 < np.float32(2.0 ** -126))
     alpha32 = np.where(constant, np.float32(1.0), alpha32)
     zero32 = (-mn / alpha32.astype(np.float64)).astype(np.float32)
     a = alpha32.astype(np.float64)[:, :, None]

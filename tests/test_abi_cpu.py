@@ -35,6 +35,30 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_peaks_library_exports_every_declared_symbol():
+    """libmq_peaks.so (the measured-peak probes bench.py times) loads and
+    exports what include/mq_peaks.h declares; its argument checks refuse bad
+    input before any launch."""
+    from nested_int_matmul_amd import build as b
+
+    if not os.path.exists(b.PEAKS_LIB):
+        pytest.skip("libmq_peaks.so not built")
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mq_peaks.h")).read(),
+                 flags=re.S)
+    declared = sorted(set(re.findall(r"\b(mqp_[a-z_0-9]+)\s*\(", src)))
+    assert declared == ["mqp_empty", "mqp_mfma_loop", "mqp_mfma_loop_flops", "mqp_stream_read"]
+    P = ctypes.CDLL(b.PEAKS_LIB)
+    for name in declared:
+        assert hasattr(P, name), name
+    P.mqp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    assert P.mqp_stream_read(None, 1024, 8, P16, None) == 1
+    assert P.mqp_stream_read(P16, 1000, 8, P16, None) == 1      # not a multiple of 16
+    assert P.mqp_stream_read(P1, 1024, 8, P16, None) == 1       # misaligned
+    P.mqp_mfma_loop_flops.restype = ctypes.c_double
+    assert P.mqp_mfma_loop_flops(2, 3) == 2 * 4 * 3 * 4 * 2 * 32 * 32 * 16
+
+
 def test_status_strings_and_sizes(L):
     for code, name in mq.STATUS_NAMES.items():
         assert L.mq_status_string(code).decode().startswith(name)
@@ -119,11 +143,42 @@ def test_gemm_and_grouped_validation(L):
     assert L.mq_gemv_mixed(probs, rs, 17, 1, NULL) == 2
 
 
+def _layer(H=64, Hkv=64, F=128, r=4, **override):
+    """A Layer of dummy aligned pointers; override={"q": Linear(...)} etc."""
+    lin = lambda n, k: mq.Linear(0x10000, 0x10000, 0x10000, n, k, k)
+    shapes = {"q": (H, H), "k": (Hkv, H), "v": (Hkv, H), "o": (H, H), "up": (F, H),
+              "gate": (F, H), "down": (H, F)}
+    kw = {n: override.get(n, lin(*shapes[n])) for n in mq.LAYER_LINEARS}
+    arr = (mq.Layer * 1)()
+    arr[0] = mq.Layer(r=r, **kw)
+    return arr
+
+
 def test_mixnmatch_validation(L):
-    layers = (mq.Layer * 1)()
-    assert L.mq_mixnmatch_forward(layers, 1, P16, 1, P16, 1 << 20, NULL) == 1
-    assert L.mq_mixnmatch_workspace_bytes(layers, 1, 1) == 0
-    assert L.mq_mixnmatch_forward(layers, 0, P16, 1, P16, 1 << 20, NULL) == 2
+    empty = (mq.Layer * 1)()
+    ws = 1 << 20
+    # the bf16-input form (x -> h_out) and the in-place form
+    assert L.mq_mixnmatch_forward(empty, 1, P16, 1, P16, P16, ws, NULL) == 1
+    assert L.mq_mixnmatch_forward_inplace(empty, 1, P16, 1, P16, ws, NULL) == 1
+    assert L.mq_mixnmatch_workspace_bytes(empty, 1, 1) == 0
+    assert L.mq_mixnmatch_forward(empty, 0, P16, 1, P16, P16, ws, NULL) == 2
+    ok = _layer()
+    assert L.mq_mixnmatch_workspace_bytes(ok, 1, 1) > 0
+    assert L.mq_mixnmatch_forward(ok, 1, NULL, 1, P16, P16, ws, NULL) == 1     # no x
+    assert L.mq_mixnmatch_forward(ok, 1, P16, 1, NULL, P16, ws, NULL) == 1     # no h_out
+    assert L.mq_mixnmatch_forward(ok, 1, P1, 1, P16, P16, ws, NULL) == 5       # x misaligned
+    assert L.mq_mixnmatch_forward(ok, 1, P16, 1, P1, P16, ws, NULL) == 5       # h_out misaligned
+    assert L.mq_mixnmatch_forward(ok, 1, P16, 9, P16, P16, ws, NULL) == 2      # M > 8
+    assert L.mq_mixnmatch_forward(ok, 1, P16, 1, P16, NULL, ws, NULL) == 6     # no workspace
+    assert L.mq_mixnmatch_forward(ok, 1, P16, 1, P16, P16, 16, NULL) == 6      # too small
+    assert L.mq_mixnmatch_forward(_layer(r=5), 1, P16, 1, P16, P16, ws, NULL) == 3
+    # a linear's scales must be 4-byte aligned, as for every product
+    bad = mq.Linear(0x10000, 0x10002, 0x10000, 64, 64, 64)
+    assert L.mq_mixnmatch_forward(_layer(q=bad), 1, P16, 1, P16, P16, ws, NULL) == 5
+    bad = mq.Linear(0x10008, 0x10000, 0x10000, 64, 64, 64)                    # packed not 16-aligned
+    assert L.mq_mixnmatch_forward(_layer(o=bad), 1, P16, 1, P16, P16, ws, NULL) == 5
+    bad = mq.Linear(0x10000, 0x10000, 0x10000, 64, 128, 128)                   # down-shaped o
+    assert L.mq_mixnmatch_forward(_layer(o=bad), 1, P16, 1, P16, P16, ws, NULL) == 2
 
 
 def test_quantize_validation(L):
@@ -186,6 +241,51 @@ def test_mlp_validation(L):
     assert call(u=lin(128, 256, 128), g=lin(128, 256, 256), d=lin(256, 128)) == 4
     assert call(w=NULL) == 6
     assert call(y=P1) == 5
+
+
+def test_binding_checks_tensors_against_sizes(L):
+    """The binding refuses, before any C call, tensors whose dtype or size
+    disagrees with the integer arguments the library sizes its buffers from
+    (CPU tensors: the checks come before the device check)."""
+    torch = pytest.importorskip("torch")
+    N, K, r, g = 8, 128, 4, 128
+    packed = torch.zeros(N * K * r // 8, dtype=torch.uint8)
+    alpha = torch.ones((N, K // g), dtype=torch.float32)
+    zero = torch.zeros((N, K // g), dtype=torch.float32)
+    x = torch.zeros((2, K), dtype=torch.bfloat16)
+    y = torch.zeros((2, N), dtype=torch.float32)
+    for f in (mq.gemv, mq.gemm):
+        with pytest.raises(ValueError, match="packed"):
+            f(packed[:-1], r, alpha, zero, g, N, K, x, out=y)
+        with pytest.raises(ValueError, match="packed"):
+            f(packed, 2, alpha, zero, g, N, K, x, out=y)        # plane of r = 4 served at r = 2
+        with pytest.raises(ValueError, match="alpha"):
+            f(packed, r, alpha[:, :0], zero, K, N, K, x, out=y)  # per-channel: N scales
+        with pytest.raises(TypeError, match="alpha"):
+            f(packed, r, alpha.double(), zero, g, N, K, x, out=y)
+        with pytest.raises(ValueError, match="zero"):
+            f(packed, r, alpha, zero[:4], g, N, K, x, out=y)
+        with pytest.raises(ValueError, match="x"):
+            f(packed, r, alpha, zero, g, N, K, x[:, :64], out=y)
+        with pytest.raises(TypeError, match="out"):
+            f(packed, r, alpha, zero, g, N, K, x, out=y.to(torch.bfloat16))
+        with pytest.raises(ValueError, match="out"):
+            f(packed, r, alpha, zero, g, N, K, x, out=y[:1])
+    with pytest.raises(TypeError, match="activations"):
+        mq.gemm(packed, r, alpha, zero, g, N, K, x.float(), out=y)
+    with pytest.raises(TypeError, match="w"):
+        mq.quantize(torch.zeros((N, K), dtype=torch.bfloat16), g)
+    with pytest.raises(ValueError, match="out"):
+        mq.pack(torch.zeros((N, K), dtype=torch.uint8), r,
+                out=torch.zeros(N * K * r // 8 - 16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="planes"):
+        mq.gemv_bitplanes(torch.zeros(N * K - 1, dtype=torch.uint8), 2, alpha, zero, g, N, K, x,
+                          out=y)
+    with pytest.raises(ValueError, match="different devices"):
+        mq._same_device(x, torch.zeros(1, device="meta"))
+    lin = {"packed": packed, "alpha": alpha, "zero": zero, "N": N, "K": K, "group": g}
+    with pytest.raises(ValueError, match="packed"):
+        mq.make_layers([{"r": 2, **{n: lin for n in mq.LAYER_LINEARS}}])
 
 
 def test_binding_rejects_host_tensors(L):

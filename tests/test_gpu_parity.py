@@ -13,7 +13,8 @@ import nested_int_matmul_amd as mq
 import oracle
 from nested_int_matmul_amd import inputs
 
-from gpu_helpers import compare, dev, note, quantized, x_device
+from gpu_helpers import (compare, compare_linear, dev, guarded_f32, note, quantized, term_scale,
+                         upload, x_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +31,10 @@ def test_quantize_bit_exact(shape, group, outliers):
     note(f"quantize {shape} group {group}")
     w = inputs.gaussian_weights("tiny_linear", n, k, outlier_frac=outliers)
     w[3, :] = 0.125                     # a constant vector (alpha = 1 case)
+    w[5, :] = 0.0
+    w[5, 1::2] = 1e-38                  # range too small for a normal fp32 alpha
+    w[6, :] = 0.0
+    w[6, 7::64] = np.float32(255 * 2.0 ** -126)   # alpha exactly 2^-126: normal
     q, a, z = oracle.quantize_minmax(w, group)
     codes, alpha, zero = mq.quantize(torch.from_numpy(w).to(dev()), group)
     torch.cuda.synchronize()
@@ -71,7 +76,7 @@ def test_gemv_tiny_linear(r, M):
     plane = mq.pack(m["q_d"], r)
     y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], 512, 256, 512, x_device(xb))
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 512, r), f"tiny r{r} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], 512, r, f"tiny r{r} M{M}")
 
 
 @pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
@@ -85,9 +90,11 @@ def test_gemv_ragged(r, group, M):
     m = quantized("tiny_linear", n, k, g, matrix=7)
     xb = inputs.activations_bf16("tiny_linear", M, k, matrix=7)
     plane = mq.pack(m["q_d"], r)
-    y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    y, check = guarded_f32(M, n)
+    mq.gemv(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"ragged r{r} g{g} M{M}")
+    check(f"ragged r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"ragged r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [4, 2])
@@ -101,7 +108,7 @@ def test_gemv_long_k_chunked(r):
         plane = mq.pack(m["q_d"], r)
         y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
         torch.cuda.synchronize()
-        compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"chunked r{r} g{g}")
+        compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"chunked r{r} g{g}")
 
 
 def _sample_rows(n, count=384, seed=0):
@@ -130,8 +137,7 @@ def test_gemv_gemma_mlp_full_size(r):
     torch.cuda.synchronize()
     for i, m in enumerate(mats):
         rows = _sample_rows(m["N"], seed=i)
-        ref = oracle.linear(m["xb"], m["q"][rows], m["alpha"][rows], m["zero"][rows], m["K"], r)
-        compare(m["y"][:, rows], ref, f"gemma mat{i} r{r}")
+        compare_linear(m["y"][:, rows], m["xb"], m["q"][rows], m["alpha"][rows], m["zero"][rows], m["K"], r, f"gemma mat{i} r{r}")
 
 
 def test_gemv_mixed_precisions_one_launch():
@@ -159,8 +165,7 @@ def test_gemv_mixed_precisions_one_launch():
     for i, r, y in outs:
         m = mats[i]
         rows = _sample_rows(m["N"], 128, seed=10 * i + r)
-        ref = oracle.linear(m["xb"], m["q"][rows], m["alpha"][rows], m["zero"][rows], m["K"], r)
-        compare(y[:, rows], ref, f"mixed mat{i} r{r}")
+        compare_linear(y[:, rows], m["xb"], m["q"][rows], m["alpha"][rows], m["zero"][rows], m["K"], r, f"mixed mat{i} r{r}")
 
 
 @pytest.mark.parametrize("M", [1, 5])
@@ -178,11 +183,11 @@ def test_gemv_mixed_granularities(M):
         probs.append({"packed": mq.pack(m["q_d"], r), "alpha": m["alpha_d"], "zero": m["zero_d"],
                       "x": x_device(xb), "y": y, "N": n, "K": k, "group": gg})
         rs.append(r)
-        refs.append((y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], gg, r), f"case{j} r{r}"))
+        refs.append((y, (xb, m["q"], m["alpha"], m["zero"], gg, r), f"case{j} r{r}"))
     mq.gemv_grouped(probs, rs, M)
     torch.cuda.synchronize()
-    for y, ref, what in refs:
-        compare(y, ref, what)
+    for y, args, what in refs:
+        compare_linear(y, *args, what)
 
 
 @pytest.mark.parametrize("r", [6, 3])
@@ -198,7 +203,7 @@ def test_gemm_split_precision_large_batch(r, group, M):
     xb = inputs.activations_bf16("mistral_small", M, k, matrix=7, heavy_channels=8)
     y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [6, 3])
@@ -214,7 +219,7 @@ def test_gemm_split_precision_small_batch(r, group, M):
     xb = inputs.activations_bf16("mistral_small", M, k, matrix=6, heavy_channels=8)
     y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [6, 3])
@@ -227,8 +232,8 @@ def test_gemm_split_precision_mistral_full_size(r):
         y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
         torch.cuda.synchronize()
         rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(r).choice(n, 150, replace=False)]))
-        compare(y[:, rows], oracle.linear(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], 128, r),
-                f"gemm mistral r{r} {n}x{k}")
+        compare_linear(y[:, rows], xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], 128, r,
+                       f"gemm mistral r{r} {n}x{k}")
 
 
 def test_gemv_deterministic():
@@ -257,7 +262,7 @@ def test_gemv_grouped_repeated_launches_identical(r):
     plane = mq.pack(m["q_d"], r)
     y0 = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x)
     torch.cuda.synchronize()
-    compare(y0, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 128, r), f"grouped r{r}")
+    compare_linear(y0, xb, m["q"], m["alpha"], m["zero"], 128, r, f"grouped r{r}")
     lin = dict(packed=plane, alpha=m["alpha_d"], zero=m["zero_d"], N=n, K=k, group=128, x=x)
     for i in range(40):
         y = mq.gemv(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x)
@@ -349,9 +354,11 @@ def test_gemm_small(r, group, M):
     m = quantized("mistral_small", n, k, g, matrix=5)
     xb = inputs.activations_bf16("mistral_small", M, k, matrix=5, heavy_channels=8)
     plane = mq.pack(m["q_d"], r)
-    y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    y, check = guarded_f32(M, n)
+    mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+    check(f"gemm small r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [8, 4, 2])
@@ -367,9 +374,11 @@ def test_gemm_mid_batch_split_k(r, group, M):
     note(f"gemm mid batch split-K r={r} g={g} M={M}")
     m = quantized("mistral_small", n, k, g, matrix=8)
     xb = inputs.activations_bf16("mistral_small", M, k, matrix=8, heavy_channels=8)
-    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    y, check = guarded_f32(M, n)
+    mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"gemm r{r} g{g} M{M}")
+    check(f"gemm mid r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [4, 8, 3])
@@ -384,9 +393,11 @@ def test_gemm_split_k_unaligned_slices(r, M):
     note(f"gemm split-K unaligned slices r={r} M={M}")
     m = quantized("mistral_small", n, k, 128, matrix=10)
     xb = inputs.activations_bf16("mistral_small", M, k, matrix=10, heavy_channels=8)
-    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
+    y, check = guarded_f32(M, n)
+    mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb), out=y)
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], 128, r), f"gemm r{r} M{M}")
+    check(f"gemm unaligned r{r} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], 128, r, f"gemm r{r} M{M}")
 
 
 @pytest.mark.parametrize("r", [8, 6, 4])
@@ -401,7 +412,7 @@ def test_gemm_prefill_split_k_odd_iterations(r):
     xb = inputs.activations_bf16("mistral_small", M, k, matrix=9, heavy_channels=8)
     y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], k, n, k, x_device(xb))
     torch.cuda.synchronize()
-    compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], k, r), f"gemm odd r{r}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], k, r, f"gemm odd r{r}")
 
 
 @pytest.mark.parametrize("r", [4, 6])
@@ -418,8 +429,7 @@ def test_gemm_small_batch_ragged_last_panel(r, group, M):
     y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([_sample_rows(n, 200, seed=M), np.arange(n - 230, n)]))
-    ref = oracle.linear(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], g, r)
-    compare(y[:, rows], ref, f"ragged panel r{r} g{g} M{M}")
+    compare_linear(y[:, rows], xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], g, r, f"ragged panel r{r} g{g} M{M}")
 
 
 @pytest.mark.parametrize("r", [4, 2])
@@ -434,8 +444,7 @@ def test_gemm_mistral_small_full_size(r, M, shape):
     y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
     torch.cuda.synchronize()
     rows = _sample_rows(n, 256)
-    ref = oracle.linear(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], 128, r)
-    compare(y[:, rows], ref, f"mistral small r{r} M{M} {shape}")
+    compare_linear(y[:, rows], xb, m["q"][rows], m["alpha"][rows], m["zero"][rows], 128, r, f"mistral small r{r} M{M} {shape}")
 
 
 @pytest.mark.parametrize("r", [4, 2, 8, 6, 3])
@@ -448,8 +457,7 @@ def test_gemm_prefill_full_size(r):
     y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb))
     torch.cuda.synchronize()
     cols = _sample_rows(n, 128)
-    ref = oracle.linear(xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], 128, r)
-    compare(y[:, cols], ref, f"prefill r{r}")
+    compare_linear(y[:, cols], xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], 128, r, f"prefill r{r}")
 
 
 @pytest.mark.parametrize("r", [4, 2, 8, 6, 3])
@@ -467,8 +475,7 @@ def test_gemm_prefill_down_projection_split_k(r, M, group):
     y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
     torch.cuda.synchronize()
     cols = _sample_rows(n, 128, seed=r)
-    ref = oracle.linear(xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], g, r)
-    compare(y[:, cols], ref, f"prefill down r{r} M{M} g{g}")
+    compare_linear(y[:, cols], xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], g, r, f"prefill down r{r} M{M} g{g}")
 
 
 # ---------------------------------------------------------------- Mix'n'Match
@@ -517,7 +524,7 @@ def test_mixnmatch_small_stack(group_kind, M, rs):
     for li in range(len(rs)):
         h_in = h.clone()
         one = mq.make_layers(devl[li:li + 1])
-        mq.mixnmatch_forward(one, h, ws)
+        mq.mixnmatch_forward_inplace(one, h, ws)
         torch.cuda.synchronize()
         L = host[li]
         a_bits = ws[off[0]:off[0] + M * H * 2].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -535,8 +542,7 @@ def test_mixnmatch_small_stack(group_kind, M, rs):
                 "gate": fetch(5, 512)}
         for name, y in outs.items():
             p = L[name]
-            compare(y, oracle.linear(a_bits, p["q"], p["alpha"], p["zero"], p["group"], L["r"]),
-                    f"layer {li} {name}")
+            compare_linear(y, a_bits, p["q"], p["alpha"], p["zero"], p["group"], L["r"], f"layer {li} {name}")
         qb = _bf16_bits_of_f32(outs["q"])
         ugb = _bf16_bits_of_f32(outs["up"] * outs["gate"])
 
@@ -552,18 +558,24 @@ def test_mixnmatch_small_stack(group_kind, M, rs):
                                           err_msg=f"layer {li} bf16(u*g)")
         o = fetch(6, H)
         d = fetch(7, H)
-        compare(o, oracle.linear(qb, L["o"]["q"], L["o"]["alpha"], L["o"]["zero"],
-                                 L["o"]["group"], L["r"]), f"layer {li} o")
-        compare(d, oracle.linear(ugb, L["down"]["q"], L["down"]["alpha"], L["down"]["zero"],
-                                 L["down"]["group"], L["r"]), f"layer {li} down")
+        compare_linear(o, qb, L["o"]["q"], L["o"]["alpha"], L["o"]["zero"],
+                                 L["o"]["group"], L["r"], f"layer {li} o")
+        compare_linear(d, ugb, L["down"]["q"], L["down"]["alpha"], L["down"]["zero"],
+                                 L["down"]["group"], L["r"], f"layer {li} down")
         h_ref = hin + o.double().cpu().numpy() + d.double().cpu().numpy()
         compare(h, h_ref, f"layer {li} residual")
 
-    # end to end: all layers in one call, against the float64 stack
-    h = torch.from_numpy(h0.astype(np.float32)).to(dev())
-    mq.mixnmatch_forward(arr, h, ws)
+    # end to end: all layers in one call from the bf16 input, against the
+    # float64 stack; the in-place form from h = x gives the same bits
+    h_out, check = guarded_f32(M, H)
+    mq.mixnmatch_forward(arr, x_device(xb), ws, out=h_out)
     torch.cuda.synchronize()
-    compare(h, oracle.mixnmatch_forward(host, xb), "stack end-to-end")
+    check("stack h_out")
+    compare(h_out, oracle.mixnmatch_forward(host, xb), "stack end-to-end", reg=1e-3)
+    h = torch.from_numpy(h0.astype(np.float32)).to(dev())
+    mq.mixnmatch_forward_inplace(arr, h, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_out)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -580,7 +592,7 @@ def test_gemv_maximum_k(r, group):
         xb = inputs.activations_bf16("tiny_linear", M, k, matrix=30)
         y = mq.gemv(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
         torch.cuda.synchronize()
-        compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r), f"max K r{r} M{M}")
+        compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"max K r{r} M{M}")
 
 
 @pytest.mark.parametrize("M", [1, 8, 16, 64, 65, 255, 256, 300])
@@ -594,8 +606,7 @@ def test_single_row_and_minimum_k(M):
         for r in (8, 2):
             y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
             torch.cuda.synchronize()
-            compare(y, oracle.linear(xb, m["q"], m["alpha"], m["zero"], g, r),
-                    f"N{n} K{k} g{g} r{r} M{M}")
+            compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"N{n} K{k} g{g} r{r} M{M}")
 
 
 def test_constant_rows_quantize_and_product():
@@ -618,4 +629,91 @@ def test_constant_rows_quantize_and_product():
         for r in (8, 4, 2):
             y = mq.gemv(mq.pack(codes, r), r, alpha, zero, g, n, k, x_device(xb))
             torch.cuda.synchronize()
-            compare(y, oracle.linear(xb, q, a, z, g, r), f"constant rows g{g} r{r}")
+            compare_linear(y, xb, q, a, z, g, r, f"constant rows g{g} r{r}")
+
+
+def _constant_group_weights(n, k, seed):
+    """Gaussian weights with constant vectors where the GEMM kernels change
+    groups: a constant row, a zero row, a constant first, middle and last
+    group of 128, and a row whose even groups are constant (the scale then
+    alternates between 1 and about 5e-4 from group to group)."""
+    w = inputs.gaussian_weights("mistral_small", n, k, matrix=seed)
+    w[3] = 0.25
+    w[5] = 0.0
+    w[7, 128:256] = 0.0
+    w[11, :128] = -1.5
+    w[13, k - 128:] = 0.5
+    for g0 in range(0, k, 256):
+        w[17, g0:g0 + 128] = 0.1
+    w[n - 1, 1024:1152] = -0.03125
+    return w
+
+
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
+@pytest.mark.parametrize("M", [16, 64, 300, 2048])
+def test_gemm_constant_groups(r, M):
+    """Constant rows and groups (alpha = 1, z = -min) next to Gaussian groups
+    (alpha about 5e-4) through mq_gemm at group 128: the panel kernel's group
+    restarts (M = 16, 64; K split in 4), and the prefill kernel's rescale of
+    its accumulators by alpha_g / alpha_{g+1} (M = 300, 2048; K split over
+    workgroups).  Every output element against the oracle."""
+    n, k = 300, 4096
+    note(f"gemm constant groups r={r} M={M}")
+    w = _constant_group_weights(n, k, 40)
+    q, a, z = oracle.quantize_minmax(w, 128)
+    assert np.sum(a == 1.0) == 2 * 32 + 16 + 4
+    m = upload(q, a, z, 128)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=40, heavy_channels=8)
+    y, check = guarded_f32(M, n)
+    mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], 128, n, k, x_device(xb), out=y)
+    torch.cuda.synchronize()
+    check(f"constant groups r{r} M{M}")
+    compare_linear(y, xb, q, a, z, 128, r, f"constant groups r{r} M{M}")
+    # the constant rows alone (a whole-matrix norm would hide one of them)
+    rows = [3, 5, 7, 11, 13, 17, n - 1]
+    compare_linear(y[:, rows], xb, q[rows], a[rows], z[rows], 128, r, f"constant rows r{r} M{M}")
+
+
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+def test_one_hot_rows_read_back_every_weight(r, group):
+    """Activation rows that are one-hot (x[m, k_m] = 1) make each output
+    element a single dequantized weight: y[m, n] = (S(q[n, k_m], r) - z) *
+    alpha.  Every weight of an 80 x 1536 matrix is read back this way through
+    every route of mq_gemm (the decode kernel at M = 1 and 8 on a sample of
+    columns, the small-batch kernel at M = 16 and 64, the tiled kernel at
+    M = 128, 300 and 2048, K splits included), each within a few fp32
+    roundings of its own size, far below one slice level alpha * 2^(8-r)."""
+    n, k = 80, 1536
+    g = k if group == "K" else 128
+    note(f"one-hot read-back r={r} g={g}")
+    m = quantized("mistral_small", n, k, g, matrix=60, outlier_frac=1e-2)
+    plane = mq.pack(m["q_d"], r)
+    w = oracle.dequant(m["q"], m["alpha"], m["zero"], g, r)
+    s = oracle.slice_value(m["q"], r).astype(np.float64)
+    abar = np.repeat(m["alpha"].astype(np.float64), g, axis=1)
+    zbar = np.repeat(m["zero"].astype(np.float64), g, axis=1)
+    tol = 2.0 ** -18 * abar * (np.abs(s - zbar) + 512.0)
+    one = np.uint16(0x3F80)  # bf16 1.0
+    rg = np.random.default_rng(r)
+    sampled = np.unique(np.concatenate([np.arange(128), np.arange(k - 128, k),
+                                        rg.choice(k, 128, replace=False)]))
+    for M in (1, 8, 16, 64, 128, 300, 2048):
+        cols = sampled if M <= 8 else np.arange(k)
+        got = np.zeros((n, cols.size))
+        outs = []
+        for start in range(0, cols.size, M):
+            chunk = cols[start:start + M]
+            xb = np.zeros((M, k), dtype=np.uint16)
+            xb[np.arange(chunk.size), chunk] = one
+            y = mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+            outs.append((start, chunk.size, y))
+        torch.cuda.synchronize()
+        for start, c, y in outs:
+            got[:, start:start + c] = y[:c].double().cpu().numpy().T
+        err = np.abs(got - w[:, cols])
+        ratio = err / tol[:, cols]
+        worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+        note(f"  M={M}: max error / tolerance {ratio.max():.3e} at row {worst[0]} "
+             f"col {cols[worst[1]]}")
+        assert ratio.max() <= 1.0, f"r{r} g{g} M{M}: weight {worst} read back off by {err[worst]}"

@@ -184,6 +184,22 @@ def test_quantizer_exact_rationals():
             assert q[n, k] == want
 
 
+def test_tiny_range_vector_is_treated_as_constant():
+    """A vector whose fp32 alpha would be subnormal or zero takes the
+    constant-vector reading (alpha = 1, z = -min, every code 0); a range of
+    exactly 255 * 2^-126 gives the smallest normal alpha, 2^-126, and the
+    ordinary codes 0 and 255."""
+    w = np.zeros((3, 128), dtype=np.float32)
+    w[0, 1::2] = np.float32(1e-38)                   # alpha64 = 3.9e-41: subnormal in fp32
+    w[1, 5] = np.float32(2.0 ** -149)                 # alpha64 rounds to 0 in fp32
+    w[2, 7] = np.float32(255 * 2.0 ** -126)           # alpha = 2^-126 exactly
+    q, a, z = oracle.quantize_minmax(w, 128)
+    assert a[0, 0] == 1.0 and a[1, 0] == 1.0 and np.all(q[:2] == 0)
+    assert z[0, 0] == 0.0 and z[1, 0] == 0.0
+    assert a[2, 0] == np.float32(2.0 ** -126)
+    assert q[2, 7] == 255 and np.count_nonzero(q[2]) == 1
+
+
 def test_constant_vector():
     w = np.full((2, 128), -0.25, dtype=np.float32)
     w[1] = 0.0
@@ -450,6 +466,21 @@ def _const_layer(h_dim, f_dim, consts, r):
 
 def _bf16(v):
     return torch.tensor(np.asarray(v, dtype=np.float64)).float().to(torch.bfloat16).double().numpy()
+
+
+def test_rms_normalize_hand_values():
+    """Hand values of the gain-free RMS normalization h / sqrt(mean(h^2)),
+    per row: [3, 4] has mean square 12.5, so it maps to (sqrt(2)/5) [3, 4]
+    (a sum instead of the mean would give [0.6, 0.8]); [0, 5] in a second
+    row has the same mean square (rows are independent); [2, 2, 2, 2] maps to
+    ones and [1, -1, 1, -1] to itself."""
+    got = oracle.rms_normalize(np.array([[3.0, 4.0], [0.0, 5.0]]))
+    c = np.sqrt(2.0) / 5.0
+    assert np.allclose(got, [[3 * c, 4 * c], [0.0, 5 * c]], rtol=1e-15, atol=0)
+    assert not np.allclose(got[0], [0.6, 0.8])
+    assert np.array_equal(oracle.rms_normalize(np.array([[2.0, 2.0, 2.0, 2.0]])), [[1.0] * 4])
+    assert np.array_equal(oracle.rms_normalize(np.array([[1.0, -1.0, 1.0, -1.0]])),
+                          [[1.0, -1.0, 1.0, -1.0]])
 
 
 def test_mixnmatch_constant_weights_closed_form():
