@@ -30,7 +30,9 @@
  *    MQ_ERR_HIP and records the hipError_t (see mq_last_hip_error).  Faults
  *    during execution surface at the caller's next synchronization.
  *  - No entry point allocates device memory.  The library keeps no state
- *    except cached device properties.  Calls are thread-safe.
+ *    except cached device properties and, once mq_gemm_noalloc has run on a
+ *    device, that device's scratch array.  Calls are thread-safe (except
+ *    that overlapping mq_gemm_noalloc calls on one device share its scratch).
  */
 #ifndef MQ_H
 #define MQ_H
@@ -191,6 +193,24 @@ size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
 mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                   int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mq_gemm_noalloc: mq_gemm for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, result and validation as
+ * mq_gemm without the workspace: the K-slice partial products go to a scratch
+ * array inside the library, MQ_GEMM_NOALLOC_MAX_BYTES (64 MiB) per device,
+ * held from the first call on that device until the process ends.  Returns
+ * MQ_ERR_WORKSPACE, enqueuing nothing, when the shape needs more than that
+ * (mq_gemm_workspace_bytes(M, N, K, group) > MQ_GEMM_NOALLOC_MAX_BYTES).
+ * The call allocates nothing.  Every call on one device shares that device's
+ * array: calls that may overlap in time on one device (other streams, other
+ * threads) race and must be serialized by the caller.
+ */
+#define MQ_GEMM_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+mq_status mq_gemm_noalloc(const uint8_t* packed, int r, const float* alpha, const float* zero,
+                          int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                          float* y, void* stream);
 
 /*
  * Extra-Precision MatQuant: the slice without the clamp (the errata Eq. 8 of

@@ -30,7 +30,7 @@ EXPORTS = (
     "mq_status_string", "mq_last_hip_error", "mq_version", "mq_packed_bytes",
     "mq_quantize", "mq_pack", "mq_gemv", "mq_gemv_grouped", "mq_gemv_mixed",
     "mq_gemm_workspace_bytes",
-    "mq_gemm", "mq_mixnmatch_workspace_bytes",
+    "mq_gemm", "mq_gemm_noalloc", "mq_mixnmatch_workspace_bytes",
     "mq_mixnmatch_workspace_offsets", "mq_mixnmatch_forward", "mq_mixnmatch_forward_inplace",
     "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
     "mq_bitplanes_bytes", "mq_pack_bitplanes", "mq_gemv_bitplanes",
@@ -118,6 +118,8 @@ def lib() -> ctypes.CDLL:
     L.mq_gemm_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.mq_gemm.restype = i32
     L.mq_gemm.argtypes = [vp, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]
+    L.mq_gemm_noalloc.restype = i32
+    L.mq_gemm_noalloc.argtypes = [vp, i32, vp, vp, i64, i64, i64, vp, i64, vp, vp]
     L.mq_mixnmatch_workspace_bytes.restype = sz
     L.mq_mixnmatch_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i32, i64]
     L.mq_mixnmatch_workspace_offsets.restype = i32
@@ -423,6 +425,23 @@ def gemm(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out=None, w
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mq_gemm(_ptr(packed), r, _ptr(alpha), _ptr(zero), group, N, K, _ptr(x), m,
                          _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)), "mq_gemm")
+    return out
+
+
+GEMM_NOALLOC_MAX_BYTES = 64 << 20  # MQ_GEMM_NOALLOC_MAX_BYTES of mq.h
+
+
+def gemm_noalloc(packed, r: int, alpha, zero, group: int, N: int, K: int, x, out, stream=None):
+    """mq_gemm_noalloc: gemm() with the K-slice partials in the library's
+    per-device scratch array (no workspace, nothing allocated; `out` is
+    required).  Overlapping calls on one device race on that array."""
+    x = _bits16(x)
+    m = x.shape[0]
+    _check_weights(packed, alpha, zero, N, K, group, r)
+    _check_xy(x, out, m, N, K)
+    _same_device(packed, alpha, zero, x, out)
+    _check(lib().mq_gemm_noalloc(_ptr(packed), r, _ptr(alpha), _ptr(zero), group, N, K, _ptr(x),
+                                 m, _ptr(out), _stream(stream)), "mq_gemm_noalloc")
     return out
 
 

@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libmq.so")
 PEAKS_LIB = os.path.join(HERE, "libmq_peaks.so")
 
 SOURCES = ["quant_pack.hip", "gemv.hip", "gemm.hip", "gemm_panel.hip", "gemm_big.hip",
-           "mixnmatch.hip", "extra.hip", "bitplane.hip", "abi.hip"]
+           "mixnmatch.hip", "extra.hip", "bitplane.hip", "abi.hip", "gemm_noalloc.hip"]
 # measured-peak probes (a library of their own, loaded by bench.py only)
 PEAKS_SOURCES = ["peaks.hip"]
 

@@ -181,6 +181,23 @@ def test_mixnmatch_validation(L):
     assert L.mq_mixnmatch_forward(_layer(o=bad), 1, P16, 1, P16, P16, ws, NULL) == 2
 
 
+def test_gemm_noalloc_validation(L):
+    """The no-workspace GEMM validates like mq_gemm and refuses shapes whose
+    K-slice partials exceed its 64 MiB scratch, before touching the GPU."""
+    call = lambda r=4, g=64, N=4, K=64, M=16, p=P16, y=P16: L.mq_gemm_noalloc(
+        p, r, P16, P16, g, N, K, P16, M, y, NULL)
+    assert call(p=NULL) == 1
+    assert call(y=P1) == 5
+    assert call(r=5) == 3
+    assert call(M=0) == 2
+    assert call(g=32) == 4
+    # 64 slices of 64 x 14336 fp32 partials (235 MB) at K = 65536
+    assert L.mq_gemm_workspace_bytes(64, 14336, 65536, 128) > mq.GEMM_NOALLOC_MAX_BYTES
+    assert call(M=64, N=14336, K=65536, g=128) == 6
+    # the prefill down projection at M = 2048 needs exactly the 64 MiB
+    assert L.mq_gemm_workspace_bytes(2048, 4096, 14336, 128) == mq.GEMM_NOALLOC_MAX_BYTES
+
+
 def test_quantize_validation(L):
     assert L.mq_quantize(NULL, 4, 64, 64, P16, P16, P16, NULL) == 1
     assert L.mq_quantize(P16, 4, 64, 32, P16, P16, P16, NULL) == 4
@@ -273,6 +290,8 @@ def test_binding_checks_tensors_against_sizes(L):
             f(packed, r, alpha, zero, g, N, K, x, out=y[:1])
     with pytest.raises(TypeError, match="activations"):
         mq.gemm(packed, r, alpha, zero, g, N, K, x.float(), out=y)
+    with pytest.raises(ValueError, match="out"):
+        mq.gemm_noalloc(packed, r, alpha, zero, g, N, K, x, y[:1])
     with pytest.raises(TypeError, match="w"):
         mq.quantize(torch.zeros((N, K), dtype=torch.bfloat16), g)
     with pytest.raises(ValueError, match="out"):
