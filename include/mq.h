@@ -40,6 +40,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The library is built with hidden visibility; these entry points are the
+ * only symbols it exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MQ_API __attribute__((visibility("default")))
+#else
+#define MQ_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -57,18 +65,18 @@ typedef enum mq_status {
 } mq_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char* mq_status_string(int status);
+MQ_API const char* mq_status_string(int status);
 
 /* hipError_t value recorded by the last MQ_ERR_HIP returned on this thread
  * (0 if none). */
-int mq_last_hip_error(void);
+MQ_API int mq_last_hip_error(void);
 
 /* Library version string, e.g. "mq 0.1 gfx950". */
-const char* mq_version(void);
+MQ_API const char* mq_version(void);
 
 /* Bytes of one packed r-bit plane of an [N, K] matrix: N * K * r / 8.
  * Returns 0 for r not in {2, 3, 4, 6, 8} or negative sizes. */
-size_t mq_packed_bytes(int64_t N, int64_t K, int r);
+MQ_API size_t mq_packed_bytes(int64_t N, int64_t K, int r);
 
 /*
  * mq_quantize: min-max quantization of fp32 weights to 8-bit codes
@@ -85,7 +93,7 @@ size_t mq_packed_bytes(int64_t N, int64_t K, int r);
  *   alpha  fp32 [N, K/group] (output), zero fp32 [N, K/group] (output)
  * Sizes: N >= 1, K >= 1, group divides K and group == K or group == 128.
  */
-mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group,
+MQ_API mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group,
                       uint8_t* codes, float* alpha, float* zero, void* stream);
 
 /*
@@ -107,7 +115,7 @@ mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group,
  *   packed  uint8, N*K*r/8 bytes (output), 16-byte aligned
  * Sizes: N >= 1, K >= 64, K % 64 == 0; r in {2, 3, 4, 6, 8}.
  */
-mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
+MQ_API mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* packed,
                   void* stream);
 
 /*
@@ -130,7 +138,7 @@ mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* pa
  * Sizes: 1 <= M <= 8, N >= 1, K >= 64, K % 64 == 0, K <= 65536;
  * r in {2, 3, 4, 6, 8}.
  */
-mq_status mq_gemv(const uint8_t* packed, int r, const float* alpha, const float* zero,
+MQ_API mq_status mq_gemv(const uint8_t* packed, int r, const float* alpha, const float* zero,
                   int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                   float* y, void* stream);
 
@@ -151,7 +159,7 @@ typedef struct mq_gemv_problem {
  * result as calling mq_gemv on each problem; outputs must not overlap.
  * 1 <= count <= 16.
  */
-mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int64_t M,
+MQ_API mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int64_t M,
                           void* stream);
 
 /*
@@ -164,7 +172,7 @@ mq_status mq_gemv_grouped(const mq_gemv_problem* problems, int count, int r, int
  * Problems with per-channel and group-128 scales may be mixed; they take one
  * launch per granularity.  1 <= count <= 16.
  */
-mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
+MQ_API mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count, int64_t M,
                         void* stream);
 
 /*
@@ -189,8 +197,8 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
 /* Workspace bytes of mq_gemm.  It takes N as well as M, K and group because
  * the workspace holds one fp32 [M, N] partial product per K slice; 0 when the
  * shape is served without a K split. */
-size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
-mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
+MQ_API size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+MQ_API mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float* zero,
                   int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                   void* workspace, size_t workspace_bytes, void* stream);
 
@@ -208,7 +216,7 @@ mq_status mq_gemm(const uint8_t* packed, int r, const float* alpha, const float*
  * threads) race and must be serialized by the caller.
  */
 #define MQ_GEMM_NOALLOC_MAX_BYTES ((size_t)64 << 20)
-mq_status mq_gemm_noalloc(const uint8_t* packed, int r, const float* alpha, const float* zero,
+MQ_API mq_status mq_gemm_noalloc(const uint8_t* packed, int r, const float* alpha, const float* zero,
                           int64_t group, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                           float* y, void* stream);
 
@@ -223,22 +231,42 @@ mq_status mq_gemm_noalloc(const uint8_t* packed, int r, const float* alpha, cons
  *
  * mq_overflow_rows: row_ptr int32 [N + 1] (output): row_ptr[0] = 0 and
  *   row_ptr[n + 1] - row_ptr[n] = number of such codes in row n.
- * mq_overflow_cols: col_idx int32 [row_ptr[N]] (output): their column k, row
- *   by row, increasing within a row (row_ptr as written by mq_overflow_rows;
- *   the caller reads row_ptr[N] to size col_idx).
+ * mq_overflow_cols: col_idx uint16 [row_ptr[N]] (output, 2-byte aligned):
+ *   their column k, row by row, increasing within a row (row_ptr as written
+ *   by mq_overflow_rows; the caller reads row_ptr[N] to size col_idx).  The
+ *   lists cost 16 bits per listed code plus 32 per row.
  * mq_overflow_apply: y[m, n] += 2^(8-r) * sum over row n's listed k of
  *   alpha[n, k/group] * x[m, k], summed in a fixed order (deterministic).
  *   Run after mq_gemv / mq_gemm at the same r on the same y.
  * codes uint8 [N, K] 16-byte aligned; x bf16 bits [M, K]; y fp32 [M, N].
  * Sizes: N >= 1, K >= 64, K % 64 == 0, K <= 65536, N * K < 2^31; M >= 1.
  */
-mq_status mq_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int32_t* row_ptr,
+MQ_API mq_status mq_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int32_t* row_ptr,
                            void* stream);
-mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
-                           const int32_t* row_ptr, int32_t* col_idx, void* stream);
-mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int r,
+MQ_API mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
+                           const int32_t* row_ptr, uint16_t* col_idx, void* stream);
+MQ_API mq_status mq_overflow_apply(const int32_t* row_ptr, const uint16_t* col_idx, int r,
                             const float* alpha, int64_t group, int64_t N, int64_t K,
                             const uint16_t* x, int64_t M, float* y, void* stream);
+
+/* One matrix of a grouped sparse addition (see mq_overflow_apply_grouped). */
+typedef struct mq_overflow_problem {
+  const int32_t* row_ptr;  /* int32 [N + 1]                     */
+  const uint16_t* col_idx; /* uint16 [row_ptr[N]]              */
+  const float* alpha;      /* fp32 [N, K/group]                 */
+  const uint16_t* x;       /* bf16 bits [M, K]                  */
+  float* y;                /* fp32 [M, N] (updated)             */
+  int64_t N, K, group;
+} mq_overflow_problem;
+
+/*
+ * mq_overflow_apply_grouped: mq_overflow_apply for several matrices at the
+ * same r and M in one launch (for example the three matrices of a
+ * feed-forward block); same definitions, checks and result per matrix.
+ * Outputs must not overlap.  1 <= count <= 16.
+ */
+MQ_API mq_status mq_overflow_apply_grouped(const mq_overflow_problem* problems, int count, int r,
+                                    int64_t M, void* stream);
 
 /*
  * Bit-plane storage: one stored copy of the codes, as eight planes of one bit
@@ -265,10 +293,10 @@ mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int 
  * Sizes: N >= 1, K % 512 == 0, 512 <= K <= 65536, N * K <= 2^31;
  * 1 <= M <= 8; 1 <= r <= 8; group = K or 128; extra in {0, 1}.
  */
-size_t mq_bitplanes_bytes(int64_t N, int64_t K);
-mq_status mq_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uint8_t* planes,
+MQ_API size_t mq_bitplanes_bytes(int64_t N, int64_t K);
+MQ_API mq_status mq_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uint8_t* planes,
                             void* stream);
-mq_status mq_gemv_bitplanes(const uint8_t* planes, int r, int extra, const float* alpha,
+MQ_API mq_status mq_gemv_bitplanes(const uint8_t* planes, int r, int extra, const float* alpha,
                             const float* zero, int64_t group, int64_t N, int64_t K,
                             const uint16_t* x, int64_t M, float* y, void* stream);
 
@@ -300,7 +328,7 @@ typedef struct mq_layer {
 } mq_layer;
 
 /* Workspace bytes for mq_mixnmatch_forward (0 on invalid shapes). */
-size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_t M);
+MQ_API size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_t M);
 
 /*
  * Byte offsets inside the workspace of the intermediates of the LAST layer
@@ -310,7 +338,7 @@ size_t mq_mixnmatch_workspace_bytes(const mq_layer* layers, int n_layers, int64_
  * and gate have the same group, which lets one launch compute both and their
  * product).  offsets must have room for 10 entries, in that order.
  */
-mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, int64_t M,
+MQ_API mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, int64_t M,
                                          size_t* offsets);
 
 /*
@@ -320,7 +348,7 @@ mq_status mq_mixnmatch_workspace_offsets(const mq_layer* layers, int n_layers, i
  * not overlapping.  1 <= M <= 8, 1 <= n_layers.  `layers` is a HOST array
  * read during the call only.
  */
-mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, const uint16_t* x,
+MQ_API mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, const uint16_t* x,
                                int64_t M, float* h_out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -331,7 +359,7 @@ mq_status mq_mixnmatch_forward(const mq_layer* layers, int n_layers, const uint1
  * pipeline stage, or one layer at a time): h keeps full fp32 precision
  * between calls, which a bf16 input could not.  Same constraints otherwise.
  */
-mq_status mq_mixnmatch_forward_inplace(const mq_layer* layers, int n_layers, float* h,
+MQ_API mq_status mq_mixnmatch_forward_inplace(const mq_layer* layers, int n_layers, float* h,
                                        int64_t M, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
@@ -353,8 +381,8 @@ mq_status mq_mixnmatch_forward_inplace(const mq_layer* layers, int n_layers, flo
  *   and a (bf16 [M, F]) at 2A, with A = M*F*4 rounded up to 256.
  * Returns MQ_ERR_GROUP if up and gate differ in group.
  */
-size_t mq_mlp_workspace_bytes(int64_t M, int64_t F);
-mq_status mq_mlp_decode(const mq_linear* up, const mq_linear* gate, const mq_linear* down, int r,
+MQ_API size_t mq_mlp_workspace_bytes(int64_t M, int64_t F);
+MQ_API mq_status mq_mlp_decode(const mq_linear* up, const mq_linear* gate, const mq_linear* down, int r,
                         int act, const uint16_t* x, int64_t M, float* y, void* workspace,
                         size_t workspace_bytes, void* stream);
 

@@ -15,6 +15,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__GNUC__) || defined(__clang__)
+#define MQP_API __attribute__((visibility("default")))
+#else
+#define MQP_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -22,17 +28,17 @@ extern "C" {
 /* Read `bytes` (a multiple of 16, buf 16-byte aligned) with `blocks`
  * workgroups of 256 threads, 16-byte loads, 8 in flight per thread; writes
  * one word per workgroup to sink (uint32 [blocks]). */
-int mqp_stream_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, void* stream);
+MQP_API int mqp_stream_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, void* stream);
 
 /* `blocks` workgroups of 4 waves, each wave `iters` x 4 independent
  * v_mfma_f32_32x32x16_bf16 on register operands; out: fp32 [blocks * 256]. */
-int mqp_mfma_loop(float* out, int blocks, int iters, void* stream);
+MQP_API int mqp_mfma_loop(float* out, int blocks, int iters, void* stream);
 
 /* Flops of one mqp_mfma_loop launch (2 * 32 * 32 * 16 per product). */
-double mqp_mfma_loop_flops(int blocks, int iters);
+MQP_API double mqp_mfma_loop_flops(int blocks, int iters);
 
 /* One empty kernel (one 64-thread workgroup): the per-launch cadence. */
-int mqp_empty(void* stream);
+MQP_API int mqp_empty(void* stream);
 
 #ifdef __cplusplus
 }

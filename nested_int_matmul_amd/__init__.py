@@ -32,7 +32,7 @@ EXPORTS = (
     "mq_gemm_workspace_bytes",
     "mq_gemm", "mq_gemm_noalloc", "mq_mixnmatch_workspace_bytes",
     "mq_mixnmatch_workspace_offsets", "mq_mixnmatch_forward", "mq_mixnmatch_forward_inplace",
-    "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply",
+    "mq_overflow_rows", "mq_overflow_cols", "mq_overflow_apply", "mq_overflow_apply_grouped",
     "mq_bitplanes_bytes", "mq_pack_bitplanes", "mq_gemv_bitplanes",
     "mq_mlp_workspace_bytes", "mq_mlp_decode",
 )
@@ -50,6 +50,12 @@ class MQError(RuntimeError):
 class GemvProblem(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
                 ("zero", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("group", ctypes.c_int64)]
+
+
+class OverflowProblem(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("group", ctypes.c_int64)]
 
 
@@ -100,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.mq_overflow_cols.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     L.mq_overflow_apply.restype = i32
     L.mq_overflow_apply.argtypes = [vp, vp, i32, vp, i64, i64, i64, vp, i64, vp, vp]
+    L.mq_overflow_apply_grouped.restype = i32
+    L.mq_overflow_apply_grouped.argtypes = [ctypes.POINTER(OverflowProblem), i32, i32, i64, vp]
     L.mq_bitplanes_bytes.restype = sz
     L.mq_bitplanes_bytes.argtypes = [i64, i64]
     L.mq_pack_bitplanes.restype = i32
@@ -329,8 +337,9 @@ class GemvGroupedPlan:
 
 def overflow_lists(codes, r: int, stream=None):
     """Extra-Precision lists of a code matrix at precision r: (row_ptr int32
-    [N + 1], col_idx int32 [nnz]) on the device.  Synchronizes once to size
-    col_idx (a setup step)."""
+    [N + 1], col_idx [nnz] of 16-bit column indices, stored as int16 (read
+    them as uint16)) on the device.  Synchronizes once to size col_idx (a
+    setup step)."""
     import torch
 
     _need(codes, "codes", (torch.uint8,))
@@ -341,7 +350,7 @@ def overflow_lists(codes, r: int, stream=None):
     # the count was written on `stream`: wait for it there before reading it
     (stream if stream is not None else torch.cuda.current_stream()).synchronize()
     nnz = int(row_ptr[n].item())
-    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=codes.device)
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int16, device=codes.device)
     _check(lib().mq_overflow_cols(_ptr(codes), n, k, r, _ptr(row_ptr), _ptr(col_idx),
                                   _stream(stream)), "mq_overflow_cols")
     return row_ptr, col_idx[:nnz]
@@ -355,7 +364,7 @@ def overflow_apply(row_ptr, col_idx, r: int, alpha, group: int, N: int, K: int, 
     x = _bits16(x)
     g = (K // group) if group in (K, 128) and group > 0 and K % group == 0 else None
     _need(row_ptr, "row_ptr", (torch.int32,), numel=N + 1)
-    _need(col_idx, "col_idx", (torch.int32,))
+    _need(col_idx, "col_idx", (torch.int16, torch.uint16))
     _need(alpha, "alpha", (torch.float32,), numel=None if g is None else N * g)
     _check_xy(x, y, x.shape[0], N, K)
     _same_device(row_ptr, col_idx, alpha, x, y)
@@ -363,6 +372,28 @@ def overflow_apply(row_ptr, col_idx, r: int, alpha, group: int, N: int, K: int, 
     _check(lib().mq_overflow_apply(_ptr(row_ptr), _ptr(ci), r, _ptr(alpha), group, N, K, _ptr(x),
                                    x.shape[0], _ptr(y), _stream(stream)), "mq_overflow_apply")
     return y
+
+
+def overflow_apply_grouped(problems, r: int, M: int, stream=None):
+    """The sparse addition for several matrices in one launch.  problems: dicts
+    with row_ptr, col_idx, alpha, x, y (tensors), N, K, group."""
+    import torch
+
+    arr = (OverflowProblem * len(problems))()
+    for i, p in enumerate(problems):
+        x = _bits16(p["x"])
+        N, K, group = p["N"], p["K"], p["group"]
+        g = (K // group) if group in (K, 128) and group > 0 and K % group == 0 else None
+        _need(p["row_ptr"], "row_ptr", (torch.int32,), numel=N + 1)
+        _need(p["col_idx"], "col_idx", (torch.int16, torch.uint16))
+        _need(p["alpha"], "alpha", (torch.float32,), numel=None if g is None else N * g)
+        _check_xy(x, p["y"], M, N, K)
+        _same_device(p["row_ptr"], p["col_idx"], p["alpha"], x, p["y"])
+        ci = p["col_idx"] if p["col_idx"].numel() else p["row_ptr"]
+        arr[i] = OverflowProblem(_ptr(p["row_ptr"]), _ptr(ci), _ptr(p["alpha"]), _ptr(x),
+                                 _ptr(p["y"]), N, K, group)
+    _check(lib().mq_overflow_apply_grouped(arr, len(problems), r, M, _stream(stream)),
+           "mq_overflow_apply_grouped")
 
 
 def bitplanes_bytes(N: int, K: int) -> int:

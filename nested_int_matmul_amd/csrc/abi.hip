@@ -41,11 +41,15 @@ bool valid_r(int r) { return r == 2 || r == 3 || r == 4 || r == 6 || r == 8; }
 constexpr int64_t kMaxK = 65536;
 constexpr int64_t kMaxPlaneBytes = (int64_t)1 << 31;
 
+// a * b > lim for a, b >= 1, without forming the product (sizes come from
+// the caller unchecked and may be anywhere in int64)
+bool mul_gt(int64_t a, int64_t b, int64_t lim) { return a > lim / b; }
+
 // Shape checks shared by the products.
 mq_status check_matrix(int64_t N, int64_t K, int64_t group, int r) {
   if (!valid_r(r)) return MQ_ERR_PRECISION;
   if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK) return MQ_ERR_SHAPE;
-  if (N * K > kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (mul_gt(N, K, kMaxPlaneBytes)) return MQ_ERR_SHAPE;
   if (!(group == K || (group == 128 && K % 128 == 0))) return MQ_ERR_GROUP;
   return MQ_OK;
 }
@@ -129,13 +133,14 @@ const char* mq_version(void) { return "mq 0.1 gfx950"; }
 
 size_t mq_packed_bytes(int64_t N, int64_t K, int r) {
   if (!valid_r(r) || N < 0 || K < 0) return 0;
+  if (N > 0 && K > 0 && mul_gt(N, K, (int64_t)1 << 56)) return 0;
   return (size_t)(N * K * r / 8);
 }
 
 mq_status mq_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* codes,
                       float* alpha, float* zero, void* stream) {
   if (!w || !codes || !alpha || !zero) return MQ_ERR_NULL;
-  if (N < 1 || K < 1 || N * K > kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (N < 1 || K < 1 || mul_gt(N, K, kMaxPlaneBytes)) return MQ_ERR_SHAPE;
   if (!(group == K || (group == 128 && K % 128 == 0))) return MQ_ERR_GROUP;
   if ((reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
       (reinterpret_cast<uintptr_t>(zero) & 3u))
@@ -150,7 +155,7 @@ mq_status mq_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_t* pa
                   void* stream) {
   if (!codes || !packed) return MQ_ERR_NULL;
   if (!valid_r(r)) return MQ_ERR_PRECISION;
-  if (N < 1 || K < 64 || K % 64 != 0 || N * K > kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (N < 1 || K < 64 || K % 64 != 0 || mul_gt(N, K, kMaxPlaneBytes)) return MQ_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(packed)) return MQ_ERR_ALIGN;
   mq_status s = check_device();
   if (s != MQ_OK) return s;
@@ -192,6 +197,9 @@ mq_status mq_gemv_mixed(const mq_gemv_problem* problems, const int* r, int count
 }
 
 size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+  // 0 for shapes mq_gemm refuses (the planners assume valid shapes)
+  if (check_matrix(N, K, group, 8) != MQ_OK) return 0;
+  if (M < 1 || mul_gt(M, K, (int64_t)1 << 30) || mul_gt(M, N, (int64_t)1 << 31)) return 0;
   return mq::gemm_workspace_bytes(M, N, K, group);
 }
 
@@ -206,7 +214,7 @@ mq_status gemm_check(const uint8_t* packed, int r, const float* alpha, const flo
                      const float* y) {
   mq_status s = check_product(packed, r, alpha, zero, group, N, K, x, y);
   if (s != MQ_OK) return s;
-  if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+  if (M < 1 || mul_gt(M, K, (int64_t)1 << 30) || mul_gt(M, N, (int64_t)1 << 31)) return MQ_ERR_SHAPE;
   return MQ_OK;
 }
 
@@ -235,7 +243,7 @@ mq_status mq_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, in
                            void* stream) {
   if (!codes || !row_ptr) return MQ_ERR_NULL;
   if (!valid_r(r)) return MQ_ERR_PRECISION;
-  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || N * K >= kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || mul_gt(N, K, kMaxPlaneBytes - 1)) return MQ_ERR_SHAPE;
   if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(row_ptr) & 3u)) return MQ_ERR_ALIGN;
   mq_status s = check_device();
   if (s != MQ_OK) return s;
@@ -244,12 +252,12 @@ mq_status mq_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, in
 }
 
 mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
-                           const int32_t* row_ptr, int32_t* col_idx, void* stream) {
+                           const int32_t* row_ptr, uint16_t* col_idx, void* stream) {
   if (!codes || !row_ptr || !col_idx) return MQ_ERR_NULL;
   if (!valid_r(r)) return MQ_ERR_PRECISION;
-  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || N * K >= kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || mul_gt(N, K, kMaxPlaneBytes - 1)) return MQ_ERR_SHAPE;
   if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(row_ptr) & 3u) ||
-      (reinterpret_cast<uintptr_t>(col_idx) & 3u))
+      (reinterpret_cast<uintptr_t>(col_idx) & 1u))
     return MQ_ERR_ALIGN;
   mq_status s = check_device();
   if (s != MQ_OK) return s;
@@ -260,7 +268,7 @@ mq_status mq_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
 // ---- bit-plane storage
 
 static mq_status check_bitplane_shape(int64_t N, int64_t K) {
-  if (N < 1 || K < 512 || K % 512 != 0 || K > kMaxK || N * K > kMaxPlaneBytes)
+  if (N < 1 || K < 512 || K % 512 != 0 || K > kMaxK || mul_gt(N, K, kMaxPlaneBytes))
     return MQ_ERR_SHAPE;
   return MQ_OK;
 }
@@ -301,22 +309,48 @@ mq_status mq_gemv_bitplanes(const uint8_t* planes, int r, int extra, const float
   return e == hipSuccess ? MQ_OK : hip_fail(e);
 }
 
-mq_status mq_overflow_apply(const int32_t* row_ptr, const int32_t* col_idx, int r,
-                            const float* alpha, int64_t group, int64_t N, int64_t K,
-                            const uint16_t* x, int64_t M, float* y, void* stream) {
+static mq_status check_overflow_apply(const int32_t* row_ptr, const uint16_t* col_idx, int r,
+                                       const float* alpha, int64_t group, int64_t N, int64_t K,
+                                       const uint16_t* x, int64_t M, const float* y) {
   if (!row_ptr || !col_idx || !alpha || !x || !y) return MQ_ERR_NULL;
   if (!valid_r(r)) return MQ_ERR_PRECISION;
-  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || N * K >= kMaxPlaneBytes) return MQ_ERR_SHAPE;
+  if (N < 1 || K < 64 || K % 64 != 0 || K > kMaxK || mul_gt(N, K, kMaxPlaneBytes - 1))
+    return MQ_ERR_SHAPE;
   if (!(group == K || (group == 128 && K % 128 == 0))) return MQ_ERR_GROUP;
-  if (M < 1 || M * K > ((int64_t)1 << 30) || M * N > ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+  if (M < 1 || mul_gt(M, K, (int64_t)1 << 30) || mul_gt(M, N, (int64_t)1 << 31)) return MQ_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 1u) ||
       (reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
       (reinterpret_cast<uintptr_t>(y) & 3u))
     return MQ_ERR_ALIGN;
+  return MQ_OK;
+}
+
+mq_status mq_overflow_apply(const int32_t* row_ptr, const uint16_t* col_idx, int r,
+                            const float* alpha, int64_t group, int64_t N, int64_t K,
+                            const uint16_t* x, int64_t M, float* y, void* stream) {
+  mq_overflow_problem p{row_ptr, col_idx, alpha, x, y, N, K, group};
+  return mq_overflow_apply_grouped(&p, 1, r, M, stream);
+}
+
+mq_status mq_overflow_apply_grouped(const mq_overflow_problem* problems, int count, int r,
+                                    int64_t M, void* stream) {
+  if (!problems) return MQ_ERR_NULL;
+  if (count < 1 || count > mq::kMaxProblems) return MQ_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    const mq_overflow_problem& p = problems[i];
+    const mq_status st =
+        check_overflow_apply(p.row_ptr, p.col_idx, r, p.alpha, p.group, p.N, p.K, p.x, M, p.y);
+    if (st != MQ_OK) return st;
+  }
   mq_status s = check_device();
   if (s != MQ_OK) return s;
-  hipError_t e = mq::launch_overflow_apply(row_ptr, col_idx, r, alpha, group, N, K, x, M, y,
-                                           (hipStream_t)stream);
+  mq::OverflowProblem probs[mq::kMaxProblems];
+  for (int i = 0; i < count; ++i) {
+    const mq_overflow_problem& p = problems[i];
+    probs[i] = mq::OverflowProblem{p.row_ptr, p.col_idx, p.alpha, p.x, p.y, (int)p.N, (int)p.K,
+                                   (int)p.group, 0};
+  }
+  hipError_t e = mq::launch_overflow_apply(probs, count, r, M, (hipStream_t)stream);
   return e == hipSuccess ? MQ_OK : hip_fail(e);
 }
 
@@ -495,7 +529,7 @@ mq_status mq_mixnmatch_forward_inplace(const mq_layer* layers, int n_layers, flo
 // ---- decode MLP block
 
 size_t mq_mlp_workspace_bytes(int64_t M, int64_t F) {
-  if (M < 1 || M > mq::kSkinnyMaxM || F < 1) return 0;
+  if (M < 1 || M > mq::kSkinnyMaxM || F < 1 || F > kMaxPlaneBytes) return 0;
   return 2 * up256((size_t)(M * F * 4)) + up256((size_t)(M * F * 2));
 }
 

@@ -68,10 +68,11 @@ __global__ void __launch_bounds__(1024) overflow_scan_kernel(int* __restrict__ r
   }
 }
 
-// col_idx[row_ptr[n] ...] = the k of row n's codes at or above thr, increasing.
+// col_idx[row_ptr[n] ...] = the k of row n's codes at or above thr, increasing
+// (16-bit: K <= 65536).
 __global__ void __launch_bounds__(64 * kRowWaves) overflow_fill_kernel(
     const uint8_t* __restrict__ codes, int N, int K, uint32_t thr, const int* __restrict__ row_ptr,
-    int* __restrict__ col_idx) {
+    uint16_t* __restrict__ col_idx) {
   const int lane = threadIdx.x & 63;
   for (int n = blockIdx.x * kRowWaves + (threadIdx.x >> 6); n < N; n += gridDim.x * kRowWaves) {
     const uint8_t* row = codes + (int64_t)n * K;
@@ -91,7 +92,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) overflow_fill_kernel(
       uint32_t mm = m;
       while (mm) {
         const int b = __ffs(mm) - 1;
-        col_idx[pos++] = k + b;
+        col_idx[pos++] = (uint16_t)(k + b);
         mm &= mm - 1;
       }
       out += __shfl(incl, 63);
@@ -100,34 +101,45 @@ __global__ void __launch_bounds__(64 * kRowWaves) overflow_fill_kernel(
 }
 
 // y[m, n] += step * sum over row n's list of alpha[n, k >> gshift] * x[m, k]
-// (gshift = 7 for groups of 128, 31 for one group per row).  One wave per
-// row (four rows per 256-thread workgroup).  A lane takes every 64th entry of
-// its row, eight at a time: the eight index loads are issued together, then
-// the eight gathers (no branch between them), so one round trip serves 512
-// entries of the row.  The 64 lanes are then summed in a fixed xor order
-// (deterministic).  Activation rows go in blocks of 8; y is read before the
-// list so that its latency overlaps.  (A runtime integer division for the
-// group index cost more than the rest of the kernel: the shift replaces it.)
+// (gshift = 7 for groups of 128; per-channel scales are one alpha per row,
+// applied once to the row's sum).  One wave per row, four rows per 256-thread
+// workgroup.  A lane takes every 64th entry of its row, eight at a time: the
+// eight index loads are issued together, then the gathers (no branch between
+// them), so one round trip serves 512 entries of a row.  The 64 lanes are
+// then summed in a fixed xor order (deterministic).  Activation rows go in
+// blocks of 8; y and the row's scale are read before the list so that their
+// latency overlaps.  The kernel is a chain of dependent round trips (row
+// bounds, indices, gathers), so one launch takes several matrices (their rows
+// concatenated) rather than one launch per matrix.  (A runtime integer
+// division for the group index cost more than the rest of the kernel: the
+// shift replaces it.)
 constexpr int kApplyLanes = 64;
 constexpr int kApplyRows = 256 / kApplyLanes;
 constexpr int kApplyBatch = 8;
 
-__global__ void __launch_bounds__(256) overflow_apply_kernel(
-    const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
-    const float* __restrict__ alpha, const uint16_t* __restrict__ x, float* __restrict__ y,
-    int N, int K, int G, int gshift, int M, float step) {
+struct ApplyArgs {
+  OverflowProblem p[kMaxProblems];
+  int count;
+  int M;
+  float step;
+};
+
+template <bool PER_ROW>
+__device__ __forceinline__ void apply_rows(const OverflowProblem& P, int n, int M, float step) {
   const int sub = threadIdx.x & (kApplyLanes - 1);
-  const int n = blockIdx.x * kApplyRows + (int)(threadIdx.x / kApplyLanes);
+  const int N = P.N, K = P.K;
+  const int G = PER_ROW ? 1 : K / 128;
   int b = 0, e = 0;
   if (n < N) {
-    b = row_ptr[n];
-    e = row_ptr[n + 1];
+    b = P.row_ptr[n];
+    e = P.row_ptr[n + 1];
   }
-  const float* arow = alpha + (int64_t)(n < N ? n : 0) * G;
+  const float* arow = P.alpha + (int64_t)(n < N ? n : 0) * G;
+  const float a_row = PER_ROW ? *arow : 1.f;
   for (int m0 = 0; m0 < M; m0 += 8) {
     // this lane's output, read before the list so that its latency overlaps
     const bool writer = n < N && sub < 8 && m0 + sub < M;
-    float* yp = y + (int64_t)(m0 + (writer ? sub : 0)) * N + (n < N ? n : 0);
+    float* yp = P.y + (int64_t)(m0 + (writer ? sub : 0)) * N + (n < N ? n : 0);
     const float y0 = writer ? *yp : 0.f;
     float acc[8];
 #pragma unroll
@@ -138,15 +150,17 @@ __global__ void __launch_bounds__(256) overflow_apply_kernel(
 #pragma unroll
       for (int u = 0; u < kApplyBatch; ++u) {
         const int j = j0 + u * kApplyLanes;
-        k[u] = col_idx[j < e ? j : j0];  // j0 < e: a valid entry of the row
+        k[u] = P.col_idx[j < e ? j : j0];  // j0 < e: a valid entry of the row
         w[u] = j < e ? 1.f : 0.f;
       }
+      if (!PER_ROW) {
 #pragma unroll
-      for (int u = 0; u < kApplyBatch; ++u) w[u] *= arow[k[u] >> gshift];
+        for (int u = 0; u < kApplyBatch; ++u) w[u] *= arow[k[u] >> 7];
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (m0 + q < M) {
-          const uint16_t* xr = x + (int64_t)(m0 + q) * K;
+          const uint16_t* xr = P.x + (int64_t)(m0 + q) * K;
 #pragma unroll
           for (int u = 0; u < kApplyBatch; ++u) acc[q] += w[u] * bf16_to_f32(xr[k[u]]);
         }
@@ -163,9 +177,20 @@ __global__ void __launch_bounds__(256) overflow_apply_kernel(
       float v = acc[0];
 #pragma unroll
       for (int q = 1; q < 8; ++q) v = sub == q ? acc[q] : v;
-      *yp = y0 + step * v;
+      *yp = y0 + step * (a_row * v);
     }
   }
+}
+
+__global__ void __launch_bounds__(256) overflow_apply_kernel(const ApplyArgs a) {
+  int pi = 0;
+#pragma unroll 1
+  for (int i = 1; i < a.count; ++i)
+    if ((int)blockIdx.x >= a.p[i].tile0) pi = i;
+  const OverflowProblem& P = a.p[pi];
+  const int n = ((int)blockIdx.x - P.tile0) * kApplyRows + (int)(threadIdx.x / kApplyLanes);
+  if (P.group == P.K) apply_rows<true>(P, n, a.M, a.step);
+  else apply_rows<false>(P, n, a.M, a.step);
 }
 
 static unsigned row_blocks(int64_t N) {
@@ -188,19 +213,25 @@ hipError_t launch_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int 
 }
 
 hipError_t launch_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
-                                const int* row_ptr, int* col_idx, hipStream_t s) {
+                                const int* row_ptr, uint16_t* col_idx, hipStream_t s) {
   hipLaunchKernelGGL(overflow_fill_kernel, dim3(row_blocks(N)), dim3(64 * kRowWaves), 0, s, codes,
                      (int)N, (int)K, extra_threshold(r), row_ptr, col_idx);
   return hipGetLastError();
 }
 
-hipError_t launch_overflow_apply(const int* row_ptr, const int* col_idx, int r, const float* alpha,
-                                 int64_t group, int64_t N, int64_t K, const uint16_t* x,
-                                 int64_t M, float* y, hipStream_t s) {
-  const unsigned blocks = (unsigned)((N + kApplyRows - 1) / kApplyRows);
-  hipLaunchKernelGGL(overflow_apply_kernel, dim3(blocks), dim3(256), 0, s,
-                     row_ptr, col_idx, alpha, x, y, (int)N, (int)K, (int)(K / group),
-                     group == K ? 31 : 7, (int)M, (float)(1 << (8 - r)));
+hipError_t launch_overflow_apply(OverflowProblem* probs, int count, int r, int64_t M,
+                                 hipStream_t s) {
+  ApplyArgs a;
+  a.count = count;
+  a.M = (int)M;
+  a.step = (float)(1 << (8 - r));
+  int tile0 = 0;
+  for (int i = 0; i < count; ++i) {
+    a.p[i] = probs[i];
+    a.p[i].tile0 = tile0;
+    tile0 += (int)((probs[i].N + kApplyRows - 1) / kApplyRows);
+  }
+  hipLaunchKernelGGL(overflow_apply_kernel, dim3((unsigned)tile0), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -31,9 +31,8 @@ namespace mq {
 
 namespace panel {
 
-constexpr int kKSliceMax = 1024;  // codes of K per workgroup (activations resident in LDS)
+constexpr int kKSlice = 1024;     // codes of K per workgroup (activations resident in LDS)
 constexpr int kXPadE = 8;         // bf16 padding per staged activation row
-constexpr int DEPTH = 8;          // weight loads in flight per lane
 
 template <int R>
 struct Pc {
@@ -45,6 +44,11 @@ struct Pc {
   static constexpr int STEP = 2 * CPL;      // codes per row per step (two lane slots)
   static constexpr int MFMAS = CPL / 8;     // 16-deep products per step per m-block
   static constexpr int SPG = 128 / STEP;    // steps per group of 128
+  static constexpr int STEPS = kKSlice / STEP;  // steps of a full slice
+  // weight loads in flight per lane: the whole slice at r = 2 (8 steps),
+  // 16 steps at r = 4 (the whole slice) and r = 8; 8 for the split planes
+  // (their two loads per step take 6 or 3 registers each)
+  static constexpr int DEPTH = SPLIT ? 8 : (STEPS < 16 ? STEPS : 16);
   using LD = LoadT<R, SPLIT ? 0 : 16>;      // one lane's loads of a step
 };
 
@@ -55,12 +59,16 @@ struct Args {
   const uint16_t* x;
   float* y;     // output [M, N] (one K slice) or the partial slices [S][M][N]
   int M, N, K, G;
-  int kslice;   // codes of K per workgroup (multiple of 512)
+  int kslice;   // codes of K per workgroup (kKSlice)
 };
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
 template <int R>
@@ -82,16 +90,16 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, s = lane >> 5;
   const int M = a.M, N = a.N, K = a.K, G = a.G;
-  const int k0 = (int)blockIdx.y * a.kslice;
-  const int klen = min(a.kslice, K - k0);
-  const int kpad = (klen + 511) & ~511;           // staged codes (zeros past K)
+  constexpr int DEPTH = C::DEPTH;
+  const int k0 = (int)blockIdx.y * kKSlice;
+  const int klen = min(kKSlice, K - k0);
   const int ngl = (klen + 127) >> 7;              // groups of 128 in the slice
   const int steps = (klen + C::STEP - 1) / C::STEP;
-  const int xstride = a.kslice + kXPadE;          // elements
+  constexpr int xstride = kKSlice + kXPadE;       // elements
 
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [ROWS][xstride]
   float* sxs = reinterpret_cast<float*>(smem + (size_t)ROWS * xstride * 2);      // [ngl][ROWS]
-  float* azs = sxs + (kKSliceMax / 128) * ROWS;                                  // [2][NW*32][8]
+  float* azs = sxs + (kKSlice / 128) * ROWS;                                     // [2][NW*32][8]
 
   const int n0 = (int)blockIdx.x * NW * 32;
   const int n = n0 + wave * 32 + l32;  // weight row of this lane
@@ -100,43 +108,47 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.packed, plane);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)M * K * 2));
 
-  // ---- scales of the panel: per-channel in registers; group-128 staged in
-  //      LDS as [alpha | zero][row][group of the slice] (loads issued first,
-  //      unconditionally: entries past N or past the slice read entry 0)
+  // The loads are issued in the order the workgroup needs them: the staged
+  // activations and group scales (which the first barrier waits for), then
+  // the weights (which it does not).  Every loop here is unrolled, so no
+  // wait is placed before a load is issued.
+  // ---- activations of the slice: two 1 KiB pieces (512 codes) per row,
+  //      one per wave instruction; rows past M and columns past K read zeros
+#pragma unroll
+  for (int q = 0; q < ROWS * 2 / NW; ++q) {
+    const int pc = wave + q * NW;
+    const int m = pc >> 1, j = pc & 1;
+    const int k = k0 + j * 512 + lane * 8;
+    const uint32_t off = (m < M && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
+    lds_dma16(xr, xs + (size_t)m * xstride + j * 512, off);
+  }
+  // ---- scales of the panel: group-128 ones staged in LDS as
+  //      [alpha | zero][row][group of the slice] by 4-byte buffer-to-LDS
+  //      loads (entries past N or past the slice read zeros); per-channel
+  //      ones in registers (needed at the end only)
   float pa = 0.f, pz = 0.f;
-  float ga4[4], gz4[4];
-  if (!GROUPED) {
-    const int nc = n < N ? n : N - 1;
-    pa = a.alpha[nc];
-    pz = a.zero[nc];
-  } else {
+  if (GROUPED) {
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.alpha, (uint32_t)((int64_t)N * G * 4));
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.zero, (uint32_t)((int64_t)N * G * 4));
     const int g0 = k0 >> 7;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int idx = tid + e * 64 * NW;  // NW*32 rows x 8 groups, 4 entries per thread
+      const int base = (wave + e * NW) * 64;  // NW*32 rows x 8 groups, one entry per lane
+      const int idx = base + lane;
       const int rr = idx >> 3, gg = idx & 7;
       const int nn = n0 + rr;
-      const bool ok = nn < N && gg < ngl;
-      const int64_t off = ok ? (int64_t)nn * G + g0 + gg : 0;
-      const float av = a.alpha[off], zv = a.zero[off];
-      ga4[e] = ok ? av : 0.f;
-      gz4[e] = ok ? zv : 0.f;
+      const uint32_t off =
+          (nn < N && gg < ngl) ? (uint32_t)(((int64_t)nn * G + g0 + gg) * 4) : 0x80000000u;
+      lds_dma4(ar, azs + base, off);
+      lds_dma4(zr, azs + NW * 32 * 8 + base, off);
     }
+  } else {
+    const int nc = n < N ? n : N - 1;
+    pa = a.alpha[nc];
+    pz = a.zero[nc];
   }
 
-  // ---- activations of the slice: one 1 KiB piece (512 codes of one row)
-  //      per wave instruction
-  {
-    const int pieces = kpad >> 9;  // per row
-    for (int pc = wave; pc < ROWS * pieces; pc += NW) {
-      const int m = pc / pieces, j = pc - m * pieces;
-      const int k = k0 + j * 512 + lane * 8;
-      const uint32_t off = (m < M && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
-      lds_dma16(xr, xs + (size_t)m * xstride + j * 512, off);
-    }
-  }
-
-  // ---- first DEPTH weight loads (behind the staging loads)
+  // ---- the first DEPTH weight loads
   // split planes: the lane's high-plane bytes, and its low-plane bytes after
   // all N rows of the high plane
   constexpr int WH = C::SPLIT ? C::RH : R;  // bits per code in the (high) plane
@@ -156,15 +168,6 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   typename LD::T buf[DEPTH];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) buf[j] = LD::load(wr, loff(j), loff_lo(j));
-
-  if (GROUPED) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = tid + e * 64 * NW;
-      azs[idx] = ga4[e];
-      azs[NW * 32 * 8 + idx] = gz4[e];
-    }
-  }
   __syncthreads();
 
   // ---- per-128 sums of the staged activations: one thread per (row,
@@ -254,8 +257,8 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
           start_group(gl + 1 < ngl ? gl + 1 : gl);
         }
       }
-      // refill this slot after its last use
-      buf[j] = LD::load(wr, loff(st + DEPTH), loff_lo(st + DEPTH));
+      // refill this slot after its last use (while steps remain)
+      if (st + DEPTH < steps) buf[j] = LD::load(wr, loff(st + DEPTH), loff_lo(st + DEPTH));
     }
   }
 
@@ -327,7 +330,7 @@ static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
   // K slice: the largest the activations allow in LDS (1024 codes): longer
   // workgroups and fewer partial slices measured faster than more, shorter
   // ones at the Mistral shapes (M = 16 and 64)
-  p.kslice = panel::kKSliceMax;
+  p.kslice = panel::kKSlice;
   p.slices = (int)((K + p.kslice - 1) / p.kslice);
   return p;
 }
@@ -341,7 +344,7 @@ template <int R, int MB, bool GROUPED>
 static hipError_t launch_panel_t(const panel::Args& a, const PanelPlan& p, hipStream_t s) {
   constexpr int NW = 8;
   const size_t lds = (size_t)32 * MB * (p.kslice + panel::kXPadE) * 2 +
-                     (size_t)(panel::kKSliceMax / 128) * 32 * MB * 4 + (size_t)2 * NW * 32 * 8 * 4;
+                     (size_t)(panel::kKSlice / 128) * 32 * MB * 4 + (size_t)2 * NW * 32 * 8 * 4;
   // the LDS limit is raised once per process (a function-local static is
   // initialized exactly once, also when several host threads launch)
   static const hipError_t attr = hipFuncSetAttribute(

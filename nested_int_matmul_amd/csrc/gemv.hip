@@ -493,6 +493,30 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
     p.tiles = (rblocks + p.rbpw - 1) / p.rbpw;
     steps_per_wave[i] = steps / ks;
   }
+  // balance: the waves of one precision should carry about the same number
+  // of steps, or the longer ones set the launch's tail (at r = 2 the rule
+  // above leaves the 14336-long down projection 28 steps per wave against 14
+  // for up and gate; splitting it to 14 took that launch from 18.0 to
+  // 17.0 us).  Problems at different r keep their own lengths: the launch
+  // runs the longest first.
+  for (int i = 0; i < args.count; ++i) {
+    SkinnyProblem& p = args.p[i];
+    int tmin = 1 << 30;
+    for (int j = 0; j < args.count; ++j)
+      if (args.p[j].r == p.r && steps_per_wave[j] < tmin) tmin = steps_per_wave[j];
+    const int step = step_codes(p.r, grouped);
+    const int steps = ((p.K + 511) / 512) * 512 / step;
+    const int spg = grouped ? 128 / step : 1;
+    const int ks_max = p.y2 ? waves / 2 : waves;
+    while (p.ks < ks_max && 2 * steps_per_wave[i] > 3 * tmin &&
+           ((steps / spg) / (p.ks * 2)) * spg >= 8) {
+      p.ks *= 2;
+      p.rbpw = waves / p.ks;
+      const int rblocks = (p.N + 15) / 16 * (p.y2 ? 2 : 1);
+      p.tiles = (rblocks + p.rbpw - 1) / p.rbpw;
+      steps_per_wave[i] = steps / p.ks;
+    }
+  }
   // longest workgroups first: they start early and the short ones fill in
   for (int i = 1; i < args.count; ++i)
     for (int j = i; j > 0 && steps_per_wave[j] > steps_per_wave[j - 1]; --j) {

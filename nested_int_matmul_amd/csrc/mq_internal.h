@@ -91,10 +91,21 @@ mq_status gemm_check(const uint8_t* packed, int r, const float* alpha, const flo
 hipError_t launch_overflow_rows(const uint8_t* codes, int64_t N, int64_t K, int r, int* row_ptr,
                                 hipStream_t s);
 hipError_t launch_overflow_cols(const uint8_t* codes, int64_t N, int64_t K, int r,
-                                const int* row_ptr, int* col_idx, hipStream_t s);
-hipError_t launch_overflow_apply(const int* row_ptr, const int* col_idx, int r, const float* alpha,
-                                 int64_t group, int64_t N, int64_t K, const uint16_t* x,
-                                 int64_t M, float* y, hipStream_t s);
+                                const int* row_ptr, uint16_t* col_idx, hipStream_t s);
+// One matrix's lists, scales, activations and output for the sparse addition.
+struct OverflowProblem {
+  const int* row_ptr;
+  const uint16_t* col_idx;
+  const float* alpha;
+  const uint16_t* x;
+  float* y;
+  int N, K, group;
+  int tile0;  // first workgroup of this matrix (set by the launcher)
+};
+// The sparse addition for `count` (<= kMaxProblems) matrices at precision r
+// and M activation rows, in one launch.
+hipError_t launch_overflow_apply(OverflowProblem* probs, int count, int r, int64_t M,
+                                 hipStream_t s);
 
 // Mix'n'Match helpers.
 hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H,

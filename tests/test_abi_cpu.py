@@ -27,12 +27,28 @@ def L():
     return mq.lib()
 
 
+def _exported_text_symbols(path):
+    """Functions a shared library exports (nm -D), or None without nm."""
+    import shutil
+    import subprocess
+
+    if not shutil.which("nm"):
+        return None
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+
+
 def test_exports_every_declared_symbol(L):
     declared = _declared_functions()
     assert declared, "no declarations parsed"
     assert set(declared) == set(mq.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
+    # and nothing else: the library is built with hidden visibility
+    exported = _exported_text_symbols(mq.LIB_PATH)
+    if exported is not None:
+        assert exported == declared
 
 
 def test_peaks_library_exports_every_declared_symbol():
@@ -47,6 +63,9 @@ def test_peaks_library_exports_every_declared_symbol():
                  flags=re.S)
     declared = sorted(set(re.findall(r"\b(mqp_[a-z_0-9]+)\s*\(", src)))
     assert declared == ["mqp_empty", "mqp_mfma_loop", "mqp_mfma_loop_flops", "mqp_stream_read"]
+    exported = _exported_text_symbols(b.PEAKS_LIB)
+    if exported is not None:
+        assert exported == declared
     P = ctypes.CDLL(b.PEAKS_LIB)
     for name in declared:
         assert hasattr(P, name), name
@@ -214,6 +233,17 @@ def test_overflow_validation(L):
     assert L.mq_overflow_apply(P16, P16, 2, P16, 32, 4, 64, P16, 1, P16, NULL) == 4
     assert L.mq_overflow_apply(P16, P16, 2, P16, 64, 4, 64, P16, 0, P16, NULL) == 2
     assert L.mq_overflow_apply(P16, P16, 7, P16, 64, 4, 64, P16, 1, P16, NULL) == 3
+    assert L.mq_overflow_apply(P16, P1, 2, P16, 64, 4, 64, P16, 1, P16, NULL) == 5  # 2-byte col_idx
+    probs = (mq.OverflowProblem * 17)()
+    assert L.mq_overflow_apply_grouped(probs, 2, 2, 1, NULL) == 1          # null members
+    assert L.mq_overflow_apply_grouped(probs, 0, 2, 1, NULL) == 2
+    assert L.mq_overflow_apply_grouped(probs, 17, 2, 1, NULL) == 2
+    assert L.mq_overflow_apply_grouped(None, 1, 2, 1, NULL) == 1
+    for i in range(2):
+        probs[i] = mq.OverflowProblem(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 4, 64, 64)
+    assert L.mq_overflow_apply_grouped(probs, 2, 5, 1, NULL) == 3
+    probs[1].group = 32
+    assert L.mq_overflow_apply_grouped(probs, 2, 2, 1, NULL) == 4
 
 
 def test_bitplane_validation(L):

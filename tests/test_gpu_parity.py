@@ -301,7 +301,7 @@ def test_overflow_lists_bit_exact(r):
     torch.cuda.synchronize()
     want_ptr, want_idx = oracle.overflow_lists(q, r)
     assert row_ptr.cpu().numpy().tolist() == want_ptr.tolist()
-    assert col_idx.cpu().numpy().tolist() == want_idx.tolist()
+    assert col_idx.cpu().numpy().view(np.uint16).tolist() == want_idx.tolist()
 
 
 @pytest.mark.parametrize("r", [6, 4, 3, 2])
@@ -323,6 +323,57 @@ def test_extra_precision_product(r, group, M):
     torch.cuda.synchronize()
     compare(y, oracle.linear_extra_precision(xb, m["q"], m["alpha"], m["zero"], g, r),
             f"extra r{r} g{g} M{M}")
+
+
+@pytest.mark.parametrize("r", [2, 4])
+def test_extra_precision_grouped_gemma_mlp(r):
+    """The three Gemma-2-9B MLP matrices (per-channel, 0.1% x10 outliers) at
+    full size: plane products, then the three sparse additions in one
+    launch (mq_overflow_apply_grouped); sampled rows against the unclamped
+    oracle product."""
+    note(f"extra precision grouped gemma mlp r={r}")
+    mats, probs = [], []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        m = quantized("gemma9b_mlp", n, k, k, matrix=i, outlier_frac=1e-3)
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        y = mq.gemv(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], k, n, k, x_device(xb))
+        row_ptr, col_idx = mq.overflow_lists(m["q_d"], r)
+        probs.append(dict(row_ptr=row_ptr, col_idx=col_idx, alpha=m["alpha_d"], x=x_device(xb),
+                          y=y, N=n, K=k, group=k))
+        mats.append((m, xb, y))
+    mq.overflow_apply_grouped(probs, r, 1)
+    torch.cuda.synchronize()
+    for i, (m, xb, y) in enumerate(mats):
+        rows = _sample_rows(m["N"], 200, seed=40 + i)
+        ref = oracle.linear_extra_precision(xb, m["q"][rows], m["alpha"][rows], m["zero"][rows],
+                                            m["K"], r)
+        compare(y[:, rows], ref, f"extra grouped mat{i} r{r}")
+
+
+@pytest.mark.parametrize("group", ["K", 128])
+def test_extra_precision_maximum_k(group):
+    """K = 65536, the largest the library serves: column indices up to 65535
+    fill the 16 bits of the lists; lists bit-exact and the product with the
+    sparse addition against the unclamped oracle product, r = 2, M = 3."""
+    n, k, r, M = 24, 65536, 2, 3
+    g = k if group == "K" else 128
+    note(f"extra precision max K g={g}")
+    m = quantized("gemma9b_mlp", n, k, g, matrix=33, outlier_frac=2e-2)
+    q = m["q"]
+    assert q[:, -4096:].max() >= 256 - 32  # entries listed near the end of the rows
+    row_ptr, col_idx = mq.overflow_lists(m["q_d"], r)
+    torch.cuda.synchronize()
+    want_ptr, want_idx = oracle.overflow_lists(q, r)
+    assert row_ptr.cpu().numpy().tolist() == want_ptr.tolist()
+    assert col_idx.cpu().numpy().view(np.uint16).tolist() == want_idx.tolist()
+    assert want_idx.max() > 65000
+    xb = inputs.activations_bf16("gemma9b_mlp", M, k, matrix=33)
+    y = mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb))
+    mq.overflow_apply(row_ptr, col_idx, r, m["alpha_d"], g, n, k, x_device(xb), y)
+    torch.cuda.synchronize()
+    compare(y, oracle.linear_extra_precision(xb, q, m["alpha"], m["zero"], g, r),
+            f"extra max K g{g}")
 
 
 def test_extra_precision_gemma_up_full_size():
