@@ -129,19 +129,14 @@ def run_main(torch, mq, inputs, dev, steps, warmup):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     # for reference: each r alone (three products per launch), back to back
+    # (replayed from a graph: see time_loop)
     per_r_us = {}
+    side = torch.cuda.Stream()
     for r in RS:
-        single = [mq.GemvGroupedPlan(gemma_problems(mq, mats, ps), r, 1, stream)
+        single = [mq.GemvGroupedPlan(gemma_problems(mq, mats, ps), r, 1, side)
                   for ps in planes[r]]
-        n = max(steps, 50)
-        for i in range(3):
-            single[i % len(single)]()
-        a = T.event()
-        for i in range(n):
-            single[i % len(single)]()
-        b = T.event()
-        torch.cuda.synchronize()
-        per_r_us[r] = a.elapsed_time(b) * 1e3 / n
+        per_r_us[r] = time_loop(torch, lambda i: single[i % len(single)](), max(steps, 50),
+                                stream=side)
     return dict(total_ms=total_ms, step_bytes=step_bytes, per_r_us=per_r_us, mats=mats)
 
 
@@ -170,18 +165,35 @@ def sha256(path):
 
 # --------------------------------------------------------------------------- extra rows
 
-def time_loop(torch, fn, iters, warmup=3):
-    for i in range(warmup):
-        fn(i)
+def time_loop(torch, fn, iters, warmup=3, stream=None, reps=3):
+    """GPU microseconds per call of fn(i), i = 0 .. iters - 1: the calls are
+    captured once into a HIP graph on `stream` (a new stream if None) and the
+    graph is replayed `reps` times between two events, so that the host's
+    per-call argument checks and marshalling (several microseconds in the
+    Python binding) do not pace kernels that are only 10-20 us long.  The
+    library's entry points launch kernels only (no allocation, copy, memset
+    or synchronization), so each call captures as plain kernel nodes."""
+    s = stream if stream is not None else torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            fn(i)
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(iters):
-        fn(i)
-    e.record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(iters):
+            fn(i)
+    g.replay()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) * 1e3 / iters  # us
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e3 / (reps * iters)  # us
 
 
 def run_rows(torch, mq, inputs, dev):

@@ -4,17 +4,24 @@
 // dequantization).  At these M the product still streams the planes out of
 // HBM (every packed byte is used M times, on the matrix cores).
 //
-// Design (gfx950, v_mfma_f32_32x32x16_bf16, A = activations, B = weights):
-//  - A workgroup owns a panel of 32 * NW weight rows (one 32-row block per
-//    wave) and a slice of K of at most 1024 codes.  The activations of that
-//    slice (all M rows, padded to 32 * MB) are brought into LDS once with
+// Design (gfx950, v_mfma_f32_16x16x32_bf16, A = weights, B = activations):
+//  - A workgroup owns a panel of 256 weight rows (8 waves x two 16-row
+//    blocks) and a slice of K of at most 1024 codes.  The activations of that
+//    slice (all M rows, padded to 16 * MB) are brought into LDS once with
 //    buffer-to-LDS loads; the per-128 sums of x are formed from LDS.
-//  - Each lane streams 16 contiguous packed bytes of one weight row per step
-//    straight into registers (no LDS for weights: every row has one reader),
-//    DEPTH steps ahead of use, and unpacks them into exact bf16 integers
-//    (mq_device.h).  One unpacked operand feeds MB matrix-core products.
+//  - Four lanes share a weight row and load 16 contiguous packed bytes each
+//    per step, so one load instruction reads 64 contiguous bytes of each of
+//    16 rows (measured: 32-byte row pieces per instruction stream HBM at
+//    about two thirds of the rate of 64-byte pieces).  The bytes go straight
+//    into registers (every row has one reader), DEPTH steps ahead of use,
+//    and are unpacked into exact bf16 integers (mq_device.h); one unpacked
+//    operand feeds MB matrix-core products (16 activation rows each).
 //    r = 3 and 6 (a high-bit and a low-bit plane) take 32 codes per lane per
 //    step from both planes and assemble u = 2^r + t in the same registers.
+//  - r = 2 with groups of 128: a step (256 codes of a row) spans two groups,
+//    lanes 0-31 holding the first and lanes 32-63 the second; half of each
+//    lane's words are exchanged with the lane 32 away (v_permlane32_swap) so
+//    that every product takes codes of one group only.
 //  - alpha and z of the panel's groups are staged in LDS with the
 //    activations; group-128 scales are applied at each group end in fp32
 //    (y += alpha 2^(8-r) P_g - alpha (z + shift) sum_g x), per-channel scales
@@ -31,24 +38,27 @@ namespace mq {
 
 namespace panel {
 
-constexpr int kKSlice = 1024;     // codes of K per workgroup (activations resident in LDS)
-constexpr int kXPadE = 8;         // bf16 padding per staged activation row
+constexpr int kKSlice = 1024;          // codes of K per workgroup (activations resident in LDS)
+constexpr int kXPadE = 8;              // bf16 padding per staged activation row
+constexpr int kNW = 8;                 // waves per workgroup
+constexpr int kRBW = 2;                // 16-row weight blocks per wave
+constexpr int kRows = kNW * kRBW * 16;  // weight rows per workgroup
 
-template <int R>
+template <int R, bool GROUPED>
 struct Pc {
   // r = 3 and 6: a high-bit and a low-bit plane (rows of the high plane, then
   // rows of the low plane), 32 codes per lane per step from each
   static constexpr bool SPLIT = (R == 3 || R == 6);
   static constexpr int RL = R == 6 ? 2 : 1, RH = R - RL;  // split: plane widths
   static constexpr int CPL = SPLIT ? 32 : 16 * 8 / R;    // codes per lane per step
-  static constexpr int STEP = 2 * CPL;      // codes per row per step (two lane slots)
-  static constexpr int MFMAS = CPL / 8;     // 16-deep products per step per m-block
-  static constexpr int SPG = 128 / STEP;    // steps per group of 128
+  static constexpr int STEP = 4 * CPL;      // codes per row per step (four lanes)
+  static constexpr int MFMAS = CPL / 8;     // 32-deep products per step per operand pair
+  static constexpr bool SWAP = (R == 2 && GROUPED);      // two groups per step
+  static constexpr int SPG = STEP >= 128 ? 1 : 128 / STEP;  // steps per group (r = 8: 2)
   static constexpr int STEPS = kKSlice / STEP;  // steps of a full slice
-  // weight loads in flight per lane: the whole slice at r = 2 (8 steps),
-  // 16 steps at r = 4 (the whole slice) and r = 8; 8 for the split planes
-  // (their two loads per step take 6 or 3 registers each)
-  static constexpr int DEPTH = SPLIT ? 8 : (STEPS < 16 ? STEPS : 16);
+  // weight loads in flight per lane and row block: the whole slice at r = 2
+  // and 4, half of it at r = 8, 4 steps of the split planes (two loads each)
+  static constexpr int DEPTH = SPLIT ? 4 : (STEPS < 8 ? STEPS : 8);
   using LD = LoadT<R, SPLIT ? 0 : 16>;      // one lane's loads of a step
 };
 
@@ -59,7 +69,6 @@ struct Args {
   const uint16_t* x;
   float* y;     // output [M, N] (one K slice) or the partial slices [S][M][N]
   int M, N, K, G;
-  int kslice;   // codes of K per workgroup (kKSlice)
 };
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
@@ -81,16 +90,16 @@ __device__ __forceinline__ bf16x8 unpack_b(const uint32_t* d, int i, const Unpac
   return unpack_r8(d[2 * i], d[2 * i + 1]);
 }
 
-template <int R, int MB, int NW, bool GROUPED>
-__global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
-  using C = Pc<R>;
-  constexpr int ROWS = 32 * MB;
+template <int R, int MB, bool GROUPED>
+__global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
+  using C = Pc<R, GROUPED>;
+  constexpr int ROWS = 16 * MB;   // staged activation rows
+  constexpr int DEPTH = C::DEPTH;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, s = lane >> 5;
+  const int col = lane & 15, slot = lane >> 4;
   const int M = a.M, N = a.N, K = a.K, G = a.G;
-  constexpr int DEPTH = C::DEPTH;
   const int k0 = (int)blockIdx.y * kKSlice;
   const int klen = min(kKSlice, K - k0);
   const int ngl = (klen + 127) >> 7;              // groups of 128 in the slice
@@ -99,10 +108,9 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
 
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [ROWS][xstride]
   float* sxs = reinterpret_cast<float*>(smem + (size_t)ROWS * xstride * 2);      // [ngl][ROWS]
-  float* azs = sxs + (kKSlice / 128) * ROWS;                                     // [2][NW*32][8]
+  float* azs = sxs + (kKSlice / 128) * ROWS;                                     // [2][kRows][8]
 
-  const int n0 = (int)blockIdx.x * NW * 32;
-  const int n = n0 + wave * 32 + l32;  // weight row of this lane
+  const int n0 = (int)blockIdx.x * kRows;
   const int rowbytes = K * R / 8;
   const uint32_t plane = (uint32_t)((int64_t)N * rowbytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.packed, plane);
@@ -115,60 +123,85 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   // ---- activations of the slice: two 1 KiB pieces (512 codes) per row,
   //      one per wave instruction; rows past M and columns past K read zeros
 #pragma unroll
-  for (int q = 0; q < ROWS * 2 / NW; ++q) {
-    const int pc = wave + q * NW;
+  for (int q = 0; q < ROWS * 2 / kNW; ++q) {
+    const int pc = wave + q * kNW;
     const int m = pc >> 1, j = pc & 1;
     const int k = k0 + j * 512 + lane * 8;
     const uint32_t off = (m < M && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
     lds_dma16(xr, xs + (size_t)m * xstride + j * 512, off);
   }
-  // ---- scales of the panel: group-128 ones staged in LDS as
+  // ---- group-128 scales of the panel staged in LDS as
   //      [alpha | zero][row][group of the slice] by 4-byte buffer-to-LDS
-  //      loads (entries past N or past the slice read zeros); per-channel
-  //      ones in registers (needed at the end only)
-  float pa = 0.f, pz = 0.f;
+  //      loads (entries past N or past the slice read zeros)
   if (GROUPED) {
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.alpha, (uint32_t)((int64_t)N * G * 4));
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.zero, (uint32_t)((int64_t)N * G * 4));
     const int g0 = k0 >> 7;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int base = (wave + e * NW) * 64;  // NW*32 rows x 8 groups, one entry per lane
+    for (int e = 0; e < kRows * 8 / (64 * kNW); ++e) {
+      const int base = (wave + e * kNW) * 64;  // kRows rows x 8 groups, one entry per lane
       const int idx = base + lane;
       const int rr = idx >> 3, gg = idx & 7;
       const int nn = n0 + rr;
       const uint32_t off =
           (nn < N && gg < ngl) ? (uint32_t)(((int64_t)nn * G + g0 + gg) * 4) : 0x80000000u;
       lds_dma4(ar, azs + base, off);
-      lds_dma4(zr, azs + NW * 32 * 8 + base, off);
+      lds_dma4(zr, azs + kRows * 8 + base, off);
     }
-  } else {
-    const int nc = n < N ? n : N - 1;
-    pa = a.alpha[nc];
-    pz = a.zero[nc];
   }
 
-  // ---- the first DEPTH weight loads
+  // ---- the first DEPTH weight loads of both row blocks
   // split planes: the lane's high-plane bytes, and its low-plane bytes after
   // all N rows of the high plane
   constexpr int WH = C::SPLIT ? C::RH : R;  // bits per code in the (high) plane
   const uint32_t hrow = (uint32_t)(K * WH / 8), lrow = (uint32_t)(K * C::RL / 8);
-  const uint32_t row_off = n < N ? (uint32_t)n * hrow : plane;
-  const uint32_t base_off = row_off + (uint32_t)((k0 + s * C::CPL) * WH / 8);
-  const uint32_t base_lo = n < N ? (uint32_t)N * hrow + (uint32_t)n * lrow +
-                                       (uint32_t)((k0 + s * C::CPL) * C::RL / 8)
-                                 : plane;
-  auto loff = [&](int st) -> uint32_t {
-    return st < steps ? base_off + (uint32_t)(st * (C::STEP * WH / 8)) : 0x80000000u;
+  uint32_t base_hi[kRBW], base_lo[kRBW];
+#pragma unroll
+  for (int b = 0; b < kRBW; ++b) {
+    const int n = n0 + wave * 32 + b * 16 + col;  // weight row this lane loads
+    const uint32_t kb = (uint32_t)((k0 + slot * C::CPL) * WH / 8);
+    base_hi[b] = n < N ? (uint32_t)n * hrow + kb : plane;
+    base_lo[b] = n < N ? (uint32_t)N * hrow + (uint32_t)n * lrow +
+                             (uint32_t)((k0 + slot * C::CPL) * C::RL / 8)
+                       : plane;
+  }
+  auto loff = [&](int b, int st) -> uint32_t {
+    return st < steps ? base_hi[b] + (uint32_t)(st * (C::STEP * WH / 8)) : 0x80000000u;
   };
-  auto loff_lo = [&](int st) -> uint32_t {
-    return st < steps ? base_lo + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
+  auto loff_lo = [&](int b, int st) -> uint32_t {
+    return st < steps ? base_lo[b] + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
   };
   using LD = typename C::LD;
-  typename LD::T buf[DEPTH];
+  typename LD::T buf[kRBW][DEPTH];
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) buf[j] = LD::load(wr, loff(j), loff_lo(j));
+  for (int j = 0; j < DEPTH; ++j)
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b) buf[b][j] = LD::load(wr, loff(b, j), loff_lo(b, j));
+
+  // per-channel scales of this lane's output rows (needed at the end only;
+  // issued after the weights so that no wait before the loop covers them)
+  float pa[kRBW][4], pz[kRBW][4];
+  if (!GROUPED) {
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n0 + wave * 32 + b * 16 + 4 * slot + e;
+        const int nc = n < N ? n : N - 1;
+        pa[b][e] = a.alpha[nc];
+        pz[b][e] = a.zero[nc];
+      }
+  }
   __syncthreads();
+
+  // ---- group factors in place: alpha 2^(8-r) and -alpha (z + shift)
+  if (GROUPED) {
+    for (int t = tid; t < kRows * 8; t += 64 * kNW) {
+      const float al = azs[t], ze = azs[kRows * 8 + t];
+      azs[t] = al * Enc<R>::kStep;
+      azs[kRows * 8 + t] = -al * (ze + Enc<R>::kOffsetShift);
+    }
+  }
 
   // ---- per-128 sums of the staged activations: one thread per (row,
   //      group) sums its 16 chunks of 8 in order (no cross-lane reduction;
@@ -176,7 +209,7 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   //      on distinct banks)
   {
     const uint32_t ones = 0x3F803F80u;
-    for (int t = tid; t < ROWS * ngl; t += 64 * NW) {
+    for (int t = tid; t < ROWS * ngl; t += 64 * kNW) {
       const int m = t % ROWS, gl = t / ROWS;
       const uint16_t* p = xs + (size_t)m * xstride + gl * 128;
       u32x4 w[16];
@@ -196,32 +229,57 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
   const UnpackK uk = UnpackK::make();
   UnpackK36 uk36;
   if constexpr (C::SPLIT) uk36 = UnpackK36::make();
-  f32x16 acc[MB], part[MB];
+  // accumulators: lane holds rows 4 * slot + e of each 16-row block, for
+  // activation row mb * 16 + col; per-channel: acc only; group-128: part
+  // collects one group (two at r = 2: part and part2), acc the scaled sum
+  f32x4 acc[kRBW][MB], part[kRBW][MB], part2[kRBW][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      acc[mb][e] = 0.f;
-      part[mb][e] = 0.f;
-    }
-  const uint16_t* xa = xs + (size_t)l32 * xstride + s * C::CPL;
-  const float* az_row = azs + (wave * 32 + l32) * 8;
-  // group-128: each group's products accumulate onto -cz * sum_g x, with
-  // cz = (z + shift) / 2^(8-r), so that at the group's end
-  // part = sum_g x u - cz sum_g x and y += alpha 2^(8-r) part
-  auto start_group = [&](int gl) {
-    const float cz = (az_row[NW * 32 * 8 + gl] + Enc<R>::kOffsetShift) * (1.0f / Enc<R>::kStep);
+  for (int b = 0; b < kRBW; ++b)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int eq = 0; eq < 4; ++eq) {
-        const f32x4 sv =
-            *reinterpret_cast<const f32x4*>(sxs + gl * ROWS + mb * 32 + eq * 8 + s * 4);
-#pragma unroll
-        for (int e3 = 0; e3 < 4; ++e3) part[mb][eq * 4 + e3] = -cz * sv[e3];
+      for (int e = 0; e < 4; ++e) {
+        acc[b][mb][e] = 0.f;
+        part[b][mb][e] = 0.f;
+        part2[b][mb][e] = 0.f;
       }
+  // this lane's activation column offset within a step: the codes it
+  // multiplies are those of its own 16-byte piece (slot * CPL ...), or at
+  // r = 2 with groups, after the exchange, the first group's codes at xa_sw
+  // (products 0-3) and the second group's 128 codes later (products 4-7)
+  const int xa_sw = slot < 2 ? 64 * slot + 32 : 64 * (slot - 2);
+  const uint16_t* xa = xs + (size_t)col * xstride + (C::SWAP ? xa_sw : slot * C::CPL);
+
+  // group end: acc += alpha 2^(8-r) * P - alpha (z + shift) * sum_g x for
+  // the lane's four rows of each block (both factors formed once above),
+  // then the group's products restart
+  auto group_end = [&](int gl, f32x4 (&p)[kRBW][MB]) {
+    if (gl < ngl) {
+#pragma unroll
+      for (int b = 0; b < kRBW; ++b) {
+        const float* azr = azs + (wave * 32 + b * 16 + 4 * slot) * 8 + gl;
+        float av[4], nb[4];  // alpha 2^(8-r), -alpha (z + shift)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          av[e] = azr[e * 8];
+          nb[e] = azr[kRows * 8 + e * 8];
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const float sx = sxs[gl * ROWS + mb * 16 + col];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[b][mb][e] = fmaf(av[e], p[b][mb][e], fmaf(nb[e], sx, acc[b][mb][e]));
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[b][mb][e] = 0.f;
   };
-  if (GROUPED) start_group(0);
 
 #pragma unroll 1
   for (int base = 0; base < steps; base += DEPTH) {
@@ -229,66 +287,93 @@ __global__ void __launch_bounds__(64 * NW) panel_kernel(const Args a) {
     for (int j = 0; j < DEPTH; ++j) {
       const int st = base + j;
       if (st < steps) {
-        uint32_t d[LD::NW];
-        LD::words(buf[j], d);
+        uint32_t d[kRBW][LD::NW];
+#pragma unroll
+        for (int b = 0; b < kRBW; ++b) {
+          LD::words(buf[b][j], d[b]);
+          if constexpr (C::SWAP) {
+            // after the exchange words 0-1 hold first-group codes and words
+            // 2-3 second-group codes in every lane
+            const auto s02 = __builtin_amdgcn_permlane32_swap(d[b][2], d[b][0], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(d[b][3], d[b][1], false, false);
+            d[b][0] = s02[0];
+            d[b][1] = s13[0];
+            d[b][2] = s02[1];
+            d[b][3] = s13[1];
+          }
+        }
         const uint16_t* xp = xa + st * C::STEP;
 #pragma unroll
         for (int i = 0; i < C::MFMAS; ++i) {
-          const bf16x8 b = unpack_b<R>(d, i, uk, uk36);
+          bf16x8 xv[MB];
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 v =
-                *reinterpret_cast<const u32x4*>(xp + (size_t)mb * 32 * xstride + 8 * i);
-            const bf16x8 av = __builtin_bit_cast(bf16x8, v);
-            if (GROUPED) {
-              part[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, part[mb], 0, 0, 0);
-            } else {
-              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[mb], 0, 0, 0);
+            const int xo = C::SWAP ? 8 * (i & 3) + 128 * (i >> 2) : 8 * i;
+            xv[mb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(xp + (size_t)mb * 16 * xstride + xo));
+          }
+#pragma unroll
+          for (int b = 0; b < kRBW; ++b) {
+            const bf16x8 w = unpack_b<R>(d[b], i, uk, uk36);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              if (!GROUPED)
+                acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xv[mb], acc[b][mb], 0, 0, 0);
+              else if (C::SWAP && i >= 4)
+                part2[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xv[mb], part2[b][mb], 0, 0, 0);
+              else
+                part[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xv[mb], part[b][mb], 0, 0, 0);
             }
           }
         }
-        if (GROUPED && (j % C::SPG) == C::SPG - 1) {
-          const int gl = st / C::SPG;
-          const float av = az_row[gl] * Enc<R>::kStep;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[mb][e] = fmaf(av, part[mb][e], acc[mb][e]);
-          start_group(gl + 1 < ngl ? gl + 1 : gl);
-        }
-      }
-      // refill this slot after its last use (while steps remain)
-      if (st + DEPTH < steps) buf[j] = LD::load(wr, loff(st + DEPTH), loff_lo(st + DEPTH));
-    }
-  }
-
-  // ---- epilogue: lane holds column n, rows mb*32 + eq*8 + s*4 + e3
-  float* out = a.y + (size_t)blockIdx.y * M * N;
-  if (n < N) {
-    float ep_a = 0.f, ep_b = 0.f;
-    if (!GROUPED) {
-      ep_a = pa * Enc<R>::kStep;
-      ep_b = pa * (pz + Enc<R>::kOffsetShift);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int eq = 0; eq < 4; ++eq) {
-        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-        if (!GROUPED) {
-          for (int gl = 0; gl < ngl; ++gl)
-            tot += *reinterpret_cast<const f32x4*>(sxs + gl * ROWS + mb * 32 + eq * 8 + s * 4);
-        }
-#pragma unroll
-        for (int e3 = 0; e3 < 4; ++e3) {
-          const int m = mb * 32 + eq * 8 + s * 4 + e3;
-          if (m < M) {
-            const float v = GROUPED ? acc[mb][eq * 4 + e3]
-                                    : ep_a * acc[mb][eq * 4 + e3] - ep_b * tot[e3];
-            out[(size_t)m * N + n] = v;
+        if constexpr (GROUPED) {
+          if constexpr (C::SWAP) {
+            group_end(2 * st, part);
+            group_end(2 * st + 1, part2);
+          } else if ((j % C::SPG) == C::SPG - 1) {
+            group_end(st / C::SPG, part);
           }
         }
       }
+      // refill this slot after its last use (while steps remain)
+      if (st + DEPTH < steps) {
+#pragma unroll
+        for (int b = 0; b < kRBW; ++b)
+          buf[b][j] = LD::load(wr, loff(b, st + DEPTH), loff_lo(b, st + DEPTH));
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds rows n = row block + 4 * slot + e (e = 0..3)
+  //      of activation row m = mb * 16 + col
+  float* out = a.y + (size_t)blockIdx.y * M * N;
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = mb * 16 + col;
+    if (m >= M) continue;
+    float tot = 0.f;
+    if (!GROUPED) {
+      for (int gl = 0; gl < ngl; ++gl) tot += sxs[gl * ROWS + m];
+    }
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b) {
+      const int nb0 = n0 + wave * 32 + b * 16 + 4 * slot;
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = GROUPED ? acc[b][mb][e]
+                       : pa[b][e] * Enc<R>::kStep * acc[b][mb][e] -
+                             pa[b][e] * (pz[b][e] + Enc<R>::kOffsetShift) * tot;
+      float* o = out + (size_t)m * N + nb0;
+      if (vec && nb0 + 3 < N) {
+        *reinterpret_cast<f32x4*>(o) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb0 + e < N) o[e] = v[e];
+      }
+    }
   }
 }
 
@@ -319,19 +404,17 @@ __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ p
 // ---------------------------------------------------------------------------
 
 struct PanelPlan {
-  int nw, kslice, slices, panels;
+  int slices, panels;
 };
 
 static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
   (void)M;
   PanelPlan p;
-  p.nw = 8;
-  p.panels = (int)((N + 32 * p.nw - 1) / (32 * p.nw));
+  p.panels = (int)((N + panel::kRows - 1) / panel::kRows);
   // K slice: the largest the activations allow in LDS (1024 codes): longer
   // workgroups and fewer partial slices measured faster than more, shorter
   // ones at the Mistral shapes (M = 16 and 64)
-  p.kslice = panel::kKSlice;
-  p.slices = (int)((K + p.kslice - 1) / p.kslice);
+  p.slices = (int)((K + panel::kKSlice - 1) / panel::kKSlice);
   return p;
 }
 
@@ -342,18 +425,29 @@ size_t panel_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 template <int R, int MB, bool GROUPED>
 static hipError_t launch_panel_t(const panel::Args& a, const PanelPlan& p, hipStream_t s) {
-  constexpr int NW = 8;
-  const size_t lds = (size_t)32 * MB * (p.kslice + panel::kXPadE) * 2 +
-                     (size_t)(panel::kKSlice / 128) * 32 * MB * 4 + (size_t)2 * NW * 32 * 8 * 4;
+  using namespace panel;
+  const size_t lds = (size_t)16 * MB * (kKSlice + kXPadE) * 2 + (size_t)(kKSlice / 128) * 16 * MB * 4 +
+                     (size_t)2 * kRows * 8 * 4;
   // the LDS limit is raised once per process (a function-local static is
   // initialized exactly once, also when several host threads launch)
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)panel::panel_kernel<R, MB, NW, GROUPED>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      (const void*)panel_kernel<R, MB, GROUPED>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((panel::panel_kernel<R, MB, NW, GROUPED>), dim3(p.panels, p.slices),
-                     dim3(64 * NW), lds, s, a);
+  hipLaunchKernelGGL((panel_kernel<R, MB, GROUPED>), dim3(p.panels, p.slices), dim3(64 * kNW), lds,
+                     s, a);
   return hipGetLastError();
+}
+
+// activation rows in blocks of 16: 1, 2 or 4 blocks (33 <= M <= 48 takes 4)
+template <int R>
+static hipError_t launch_panel_r(const panel::Args& a, const PanelPlan& p, bool grouped,
+                                 hipStream_t s) {
+  if (a.M <= 16)
+    return grouped ? launch_panel_t<R, 1, true>(a, p, s) : launch_panel_t<R, 1, false>(a, p, s);
+  if (a.M <= 32)
+    return grouped ? launch_panel_t<R, 2, true>(a, p, s) : launch_panel_t<R, 2, false>(a, p, s);
+  return grouped ? launch_panel_t<R, 4, true>(a, p, s) : launch_panel_t<R, 4, false>(a, p, s);
 }
 
 hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, const float* zero,
@@ -370,31 +464,14 @@ hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, c
   a.N = (int)N;
   a.K = (int)K;
   a.G = (int)(K / group);
-  a.kslice = p.kslice;
   const bool grouped = group != K;
-  const int mb = M > 32 ? 2 : 1;
   hipError_t e;
-  switch (r * 4 + (mb - 1) * 2 + (grouped ? 1 : 0)) {
-    case 8: e = launch_panel_t<2, 1, false>(a, p, s); break;
-    case 9: e = launch_panel_t<2, 1, true>(a, p, s); break;
-    case 10: e = launch_panel_t<2, 2, false>(a, p, s); break;
-    case 11: e = launch_panel_t<2, 2, true>(a, p, s); break;
-    case 12: e = launch_panel_t<3, 1, false>(a, p, s); break;
-    case 13: e = launch_panel_t<3, 1, true>(a, p, s); break;
-    case 14: e = launch_panel_t<3, 2, false>(a, p, s); break;
-    case 15: e = launch_panel_t<3, 2, true>(a, p, s); break;
-    case 16: e = launch_panel_t<4, 1, false>(a, p, s); break;
-    case 17: e = launch_panel_t<4, 1, true>(a, p, s); break;
-    case 18: e = launch_panel_t<4, 2, false>(a, p, s); break;
-    case 19: e = launch_panel_t<4, 2, true>(a, p, s); break;
-    case 24: e = launch_panel_t<6, 1, false>(a, p, s); break;
-    case 25: e = launch_panel_t<6, 1, true>(a, p, s); break;
-    case 26: e = launch_panel_t<6, 2, false>(a, p, s); break;
-    case 27: e = launch_panel_t<6, 2, true>(a, p, s); break;
-    case 32: e = launch_panel_t<8, 1, false>(a, p, s); break;
-    case 33: e = launch_panel_t<8, 1, true>(a, p, s); break;
-    case 34: e = launch_panel_t<8, 2, false>(a, p, s); break;
-    default: e = launch_panel_t<8, 2, true>(a, p, s); break;
+  switch (r) {
+    case 2: e = launch_panel_r<2>(a, p, grouped, s); break;
+    case 3: e = launch_panel_r<3>(a, p, grouped, s); break;
+    case 4: e = launch_panel_r<4>(a, p, grouped, s); break;
+    case 6: e = launch_panel_r<6>(a, p, grouped, s); break;
+    default: e = launch_panel_r<8>(a, p, grouped, s); break;
   }
   if (e != hipSuccess || p.slices == 1) return e;
   return launch_reduce_slices(static_cast<const float*>(workspace), y, M * N, p.slices, s);
