@@ -196,9 +196,8 @@ def time_loop(torch, fn, iters, warmup=3, stream=None, reps=3):
     return a.elapsed_time(b) * 1e3 / (reps * iters)  # us
 
 
-def run_rows(torch, mq, inputs, dev):
-    rows = {}
-    # a1: slice-and-pack of the Gemma down matrix (reads N*K, writes N*K*r/8)
+def row_pack(torch, mq, inputs, dev):
+    """a1: slice-and-pack of the Gemma down matrix (reads N*K, writes N*K*r/8)."""
     n, k = inputs.GEMMA9B_MLP["down"]
     w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=2, outlier_frac=1e-3)
     codes, _, _ = mq.quantize(w, k)
@@ -210,9 +209,12 @@ def run_rows(torch, mq, inputs, dev):
         us = time_loop(torch, lambda i: mq.pack(copies[i % 7], r, out=outs[i % 7]), 21)
         b = n * k * (1 + r / 8)
         pack[f"r{r}"] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1)}
-    rows["pack_gemma_down"] = pack
     del copies, codes
-    # a3: small-batch GEMM, Mistral shapes, group 128
+    return pack
+
+
+def row_small(torch, mq, inputs, dev):
+    """a3: small-batch GEMM, Mistral shapes, group 128."""
     small = {}
     for (N2, K2) in inputs.MISTRAL_SMALL_SHAPES:
         w = inputs.device_gaussian_weights("mistral_small", N2, K2, dev, matrix=N2 // 4096)
@@ -237,8 +239,11 @@ def run_rows(torch, mq, inputs, dev):
                     "TFLOP/s": round(2 * M2 * N2 * K2 / us / 1e6, 2)}
             del pls, pl
         del c2, a2, z2
-    rows["gemm_mistral_small"] = small
-    # a4: prefill GEMM
+    return small
+
+
+def row_prefill(torch, mq, inputs, dev):
+    """a4: prefill GEMM, group 128."""
     M, K, N = inputs.PREFILL_SHAPE
     w = inputs.device_gaussian_weights("prefill", N, K, dev)
     c5, a5, z5 = mq.quantize(w, 128)
@@ -256,10 +261,13 @@ def run_rows(torch, mq, inputs, dev):
         tf = 2 * M * N * K / us / 1e6
         pre[f"r{r}"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
                         "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
-    rows["gemm_prefill_M2048"] = pre
-    del c5, a5, z5, x5, y5
-    # a4, the 4096-wide down projection of the same layer (K = 14336): 128
-    # output tiles at M = 2048, so the kernel splits K over workgroups
+    return pre
+
+
+def row_prefill_down(torch, mq, inputs, dev):
+    """a4, the 4096-wide down projection of the same layer (K = 14336): 128
+    output tiles at M = 2048, so the kernel splits K over workgroups."""
+    M, K, N = inputs.PREFILL_SHAPE
     w = inputs.device_gaussian_weights("prefill", K, N, dev, matrix=1)
     c6, a6, z6 = mq.quantize(w, 128)
     del w
@@ -275,16 +283,31 @@ def run_rows(torch, mq, inputs, dev):
         tf = 2 * M * N * K / us / 1e6
         down[f"r{r}"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
                          "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
-    rows["gemm_prefill_down_M2048"] = down
     del c6, a6, z6, x6, y6, ws6
-    # a5: Mix'n'Match stack, 32 Mistral-7B layers, batch 1
-    rows["mixnmatch_mistral7b_32l"] = run_stack(torch, mq, inputs, dev)
-    # f2: Extra-Precision r = 2 on the Gemma MLP: the sparse addition after the plane product
-    rows["extra_precision_gemma_r2"] = run_extra(torch, mq, inputs, dev)
-    # f3: bit-plane storage, one copy served at several r
-    rows["bitplanes_gemma9b_mlp"] = run_bitplanes(torch, mq, inputs, dev)
-    # f4: the decode MLP block (up/gate paired, gated product in the epilogue, then down)
-    rows["mlp_decode_gemma9b"] = run_mlp(torch, mq, inputs, dev)
+    return down
+
+
+# name -> (function, what it measures); run in this order
+ROWS = {
+    "pack_gemma_down": (row_pack, "a1 slice-and-pack"),
+    "gemm_mistral_small": (row_small, "a3 small-batch GEMM"),
+    "gemm_prefill_M2048": (row_prefill, "a4 prefill GEMM"),
+    "gemm_prefill_down_M2048": (row_prefill_down, "a4 prefill down projection"),
+    "mixnmatch_mistral7b_32l": (lambda t, m, i, d: run_stack(t, m, i, d), "a5 Mix'n'Match stack"),
+    "extra_precision_gemma_r2": (lambda t, m, i, d: run_extra(t, m, i, d), "f2 Extra-Precision"),
+    "bitplanes_gemma9b_mlp": (lambda t, m, i, d: run_bitplanes(t, m, i, d), "f3 bit-planes"),
+    "mlp_decode_gemma9b": (lambda t, m, i, d: run_mlp(t, m, i, d), "f4 decode MLP block"),
+}
+
+
+def run_rows(torch, mq, inputs, dev, only=None):
+    rows = {}
+    for name, (fn, what) in ROWS.items():
+        if only is not None and name not in only:
+            continue
+        log(f"row {name}: {what}")
+        rows[name] = fn(torch, mq, inputs, dev)
+        torch.cuda.synchronize()
     return rows
 
 
@@ -565,6 +588,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-rows", action="store_true", help="skip the extra per-row timings")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rows", default=None,
+                    help="comma-separated subset of the extra rows (default: all): " +
+                         ", ".join(ROWS))
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -631,8 +657,11 @@ def main():
 
     rows = None
     if not args.no_rows:
-        log("extra rows: pack, small GEMM, prefill GEMM, Mix'n'Match stack")
-        rows = run_rows(torch, mq, inputs, dev)
+        only = None if args.rows is None else set(args.rows.split(","))
+        if only is not None and not only <= set(ROWS):
+            print(f"bench.py: unknown rows {sorted(only - set(ROWS))}", flush=True)
+            sys.exit(2)
+        rows = run_rows(torch, mq, inputs, dev, only)
     cpu = None
     if not args.no_cpu:
         log("CPU baseline: float64 oracle")

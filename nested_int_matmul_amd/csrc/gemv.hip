@@ -50,7 +50,10 @@ struct Sk {
   static constexpr int MFMAS = CPL / 8;                   // MFMAs per step
   static constexpr int SPG = GROUPED ? 128 / STEP : 1;    // steps per group of 128
   static constexpr int PB = 8;                            // staging block (values)
-  static constexpr int DEPTH = 8;                         // loads in flight per lane
+  // loads in flight per lane: 8, and 4 at r = 2 (measured on the Gemma MLP
+  // launch at r = 2: 15.0 against 16.6 us with 8; r = 4 and 8 unchanged or
+  // slower with 4)
+  static constexpr int DEPTH = R == 2 ? 4 : 8;
 };
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
