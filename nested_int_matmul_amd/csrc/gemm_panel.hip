@@ -38,11 +38,21 @@ namespace mq {
 
 namespace panel {
 
-constexpr int kKSlice = 1024;          // codes of K per workgroup (activations resident in LDS)
+constexpr int kKSlice = 1024;          // codes of K per workgroup when K is split over workgroups
+constexpr int kKFull = 4096;           // longest K one workgroup takes whole (M <= 16)
 constexpr int kXPadE = 8;              // bf16 padding per staged activation row
 constexpr int kNW = 8;                 // waves per workgroup
-constexpr int kRBW = 2;                // 16-row weight blocks per wave
-constexpr int kRows = kNW * kRBW * 16;  // weight rows per workgroup
+
+// Workgroup shapes.  Split: 8 waves x two 16-row blocks = 256 weight rows,
+// K in slices of kKSlice over blockIdx.y (partials summed by reduce_slices).
+// Whole K (M <= 16, K <= kKFull): 4 row blocks x 2 halves of K = 64 weight
+// rows; the two halves are summed in LDS (fixed order), no second launch.
+template <int KSL, int RBW, int KH>
+struct Shape {
+  static constexpr int WPK = kNW / KH;         // waves per part of K
+  static constexpr int ROWS_WG = WPK * RBW * 16;  // weight rows per workgroup
+  static constexpr int GPS = KSL / 128;        // groups of 128 per slice
+};
 
 template <int R, bool GROUPED>
 struct Pc {
@@ -55,12 +65,16 @@ struct Pc {
   static constexpr int MFMAS = CPL / 8;     // 32-deep products per step per operand pair
   static constexpr bool SWAP = (R == 2 && GROUPED);      // two groups per step
   static constexpr int SPG = STEP >= 128 ? 1 : 128 / STEP;  // steps per group (r = 8: 2)
-  static constexpr int STEPS = kKSlice / STEP;  // steps of a full slice
-  // weight loads in flight per lane and row block: the whole slice at r = 2
-  // and 4, half of it at r = 8, 4 steps of the split planes (two loads each)
-  static constexpr int DEPTH = SPLIT ? 4 : (STEPS < 8 ? STEPS : 8);
   using LD = LoadT<R, SPLIT ? 0 : 16>;      // one lane's loads of a step
 };
+// weight loads in flight per lane and row block: a wave's whole share at
+// r = 2 and 4 of a 1024-code slice, else 8; 4 steps of the split planes
+// (two loads each)
+template <int R, bool GROUPED, int KSL, int KH>
+constexpr int depth() {
+  using C = Pc<R, GROUPED>;
+  return C::SPLIT ? 4 : (KSL / (C::STEP * KH) < 8 ? KSL / (C::STEP * KH) : 8);
+}
 
 struct Args {
   const uint8_t* packed;
@@ -90,27 +104,38 @@ __device__ __forceinline__ bf16x8 unpack_b(const uint32_t* d, int i, const Unpac
   return unpack_r8(d[2 * i], d[2 * i + 1]);
 }
 
-template <int R, int MB, bool GROUPED>
+template <int R, int MB, bool GROUPED, int KSL, int RBW, int KH>
 __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   using C = Pc<R, GROUPED>;
+  using S = Shape<KSL, RBW, KH>;
   constexpr int ROWS = 16 * MB;   // staged activation rows
-  constexpr int DEPTH = C::DEPTH;
+  constexpr int DEPTH = depth<R, GROUPED, KSL, KH>();
+  constexpr int ROWS_WG = S::ROWS_WG, GPS = S::GPS;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, slot = lane >> 4;
+  const int wrow = wave % S::WPK, kh = wave / S::WPK;  // row group and part of K of this wave
   const int M = a.M, N = a.N, K = a.K, G = a.G;
-  const int k0 = (int)blockIdx.y * kKSlice;
-  const int klen = min(kKSlice, K - k0);
+  const int k0 = (int)blockIdx.y * KSL;
+  const int klen = min(KSL, K - k0);
   const int ngl = (klen + 127) >> 7;              // groups of 128 in the slice
   const int steps = (klen + C::STEP - 1) / C::STEP;
-  constexpr int xstride = kKSlice + kXPadE;       // elements
+  // this wave's steps: all of the slice, or one of KH parts in whole groups
+  int s0 = 0, s1 = steps;
+  if (KH > 1) {
+    const int units = steps / C::SPG;
+    s0 = (units * kh / KH) * C::SPG;
+    s1 = (units * (kh + 1) / KH) * C::SPG;
+  }
+  constexpr int xstride = KSL + kXPadE;           // elements
 
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [ROWS][xstride]
   float* sxs = reinterpret_cast<float*>(smem + (size_t)ROWS * xstride * 2);      // [ngl][ROWS]
-  float* azs = sxs + (kKSlice / 128) * ROWS;                                     // [2][kRows][8]
+  float* azs = sxs + GPS * ROWS;                                     // [2][ROWS_WG][GPS]
+  float* red = azs + 2 * ROWS_WG * GPS;  // KH = 2: [WPK][64][RBW][MB][4] second half's sums
 
-  const int n0 = (int)blockIdx.x * kRows;
+  const int n0 = (int)blockIdx.x * ROWS_WG;
   const int rowbytes = K * R / 8;
   const uint32_t plane = (uint32_t)((int64_t)N * rowbytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.packed, plane);
@@ -120,12 +145,13 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   // activations and group scales (which the first barrier waits for), then
   // the weights (which it does not).  Every loop here is unrolled, so no
   // wait is placed before a load is issued.
-  // ---- activations of the slice: two 1 KiB pieces (512 codes) per row,
+  // ---- activations of the slice: 1 KiB pieces (512 codes) of each row,
   //      one per wave instruction; rows past M and columns past K read zeros
+  constexpr int PPR = KSL / 512;  // pieces per row
 #pragma unroll
-  for (int q = 0; q < ROWS * 2 / kNW; ++q) {
+  for (int q = 0; q < ROWS * PPR / kNW; ++q) {
     const int pc = wave + q * kNW;
-    const int m = pc >> 1, j = pc & 1;
+    const int m = pc / PPR, j = pc % PPR;
     const int k = k0 + j * 512 + lane * 8;
     const uint32_t off = (m < M && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
     lds_dma16(xr, xs + (size_t)m * xstride + j * 512, off);
@@ -138,15 +164,15 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.zero, (uint32_t)((int64_t)N * G * 4));
     const int g0 = k0 >> 7;
 #pragma unroll
-    for (int e = 0; e < kRows * 8 / (64 * kNW); ++e) {
-      const int base = (wave + e * kNW) * 64;  // kRows rows x 8 groups, one entry per lane
+    for (int e = 0; e < ROWS_WG * GPS / (64 * kNW); ++e) {
+      const int base = (wave + e * kNW) * 64;  // ROWS_WG rows x GPS groups, one entry per lane
       const int idx = base + lane;
-      const int rr = idx >> 3, gg = idx & 7;
+      const int rr = idx / GPS, gg = idx % GPS;
       const int nn = n0 + rr;
       const uint32_t off =
           (nn < N && gg < ngl) ? (uint32_t)(((int64_t)nn * G + g0 + gg) * 4) : 0x80000000u;
       lds_dma4(ar, azs + base, off);
-      lds_dma4(zr, azs + kRows * 8 + base, off);
+      lds_dma4(zr, azs + ROWS_WG * GPS + base, off);
     }
   }
 
@@ -155,10 +181,10 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   // all N rows of the high plane
   constexpr int WH = C::SPLIT ? C::RH : R;  // bits per code in the (high) plane
   const uint32_t hrow = (uint32_t)(K * WH / 8), lrow = (uint32_t)(K * C::RL / 8);
-  uint32_t base_hi[kRBW], base_lo[kRBW];
+  uint32_t base_hi[RBW], base_lo[RBW];
 #pragma unroll
-  for (int b = 0; b < kRBW; ++b) {
-    const int n = n0 + wave * 32 + b * 16 + col;  // weight row this lane loads
+  for (int b = 0; b < RBW; ++b) {
+    const int n = n0 + wrow * RBW * 16 + b * 16 + col;  // weight row this lane loads
     const uint32_t kb = (uint32_t)((k0 + slot * C::CPL) * WH / 8);
     base_hi[b] = n < N ? (uint32_t)n * hrow + kb : plane;
     base_lo[b] = n < N ? (uint32_t)N * hrow + (uint32_t)n * lrow +
@@ -166,27 +192,27 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
                        : plane;
   }
   auto loff = [&](int b, int st) -> uint32_t {
-    return st < steps ? base_hi[b] + (uint32_t)(st * (C::STEP * WH / 8)) : 0x80000000u;
+    return st < s1 ? base_hi[b] + (uint32_t)(st * (C::STEP * WH / 8)) : 0x80000000u;
   };
   auto loff_lo = [&](int b, int st) -> uint32_t {
-    return st < steps ? base_lo[b] + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
+    return st < s1 ? base_lo[b] + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
   };
   using LD = typename C::LD;
-  typename LD::T buf[kRBW][DEPTH];
+  typename LD::T buf[RBW][DEPTH];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j)
 #pragma unroll
-    for (int b = 0; b < kRBW; ++b) buf[b][j] = LD::load(wr, loff(b, j), loff_lo(b, j));
+    for (int b = 0; b < RBW; ++b) buf[b][j] = LD::load(wr, loff(b, s0 + j), loff_lo(b, s0 + j));
 
   // per-channel scales of this lane's output rows (needed at the end only;
   // issued after the weights so that no wait before the loop covers them)
-  float pa[kRBW][4], pz[kRBW][4];
+  float pa[RBW][4], pz[RBW][4];
   if (!GROUPED) {
 #pragma unroll
-    for (int b = 0; b < kRBW; ++b)
+    for (int b = 0; b < RBW; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int n = n0 + wave * 32 + b * 16 + 4 * slot + e;
+        const int n = n0 + wrow * RBW * 16 + b * 16 + 4 * slot + e;
         const int nc = n < N ? n : N - 1;
         pa[b][e] = a.alpha[nc];
         pz[b][e] = a.zero[nc];
@@ -196,10 +222,10 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
 
   // ---- group factors in place: alpha 2^(8-r) and -alpha (z + shift)
   if (GROUPED) {
-    for (int t = tid; t < kRows * 8; t += 64 * kNW) {
-      const float al = azs[t], ze = azs[kRows * 8 + t];
+    for (int t = tid; t < ROWS_WG * GPS; t += 64 * kNW) {
+      const float al = azs[t], ze = azs[ROWS_WG * GPS + t];
       azs[t] = al * Enc<R>::kStep;
-      azs[kRows * 8 + t] = -al * (ze + Enc<R>::kOffsetShift);
+      azs[ROWS_WG * GPS + t] = -al * (ze + Enc<R>::kOffsetShift);
     }
   }
 
@@ -232,9 +258,9 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   // accumulators: lane holds rows 4 * slot + e of each 16-row block, for
   // activation row mb * 16 + col; per-channel: acc only; group-128: part
   // collects one group (two at r = 2: part and part2), acc the scaled sum
-  f32x4 acc[kRBW][MB], part[kRBW][MB], part2[kRBW][MB];
+  f32x4 acc[RBW][MB], part[RBW][MB], part2[RBW][MB];
 #pragma unroll
-  for (int b = 0; b < kRBW; ++b)
+  for (int b = 0; b < RBW; ++b)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -253,16 +279,16 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   // group end: acc += alpha 2^(8-r) * P - alpha (z + shift) * sum_g x for
   // the lane's four rows of each block (both factors formed once above),
   // then the group's products restart
-  auto group_end = [&](int gl, f32x4 (&p)[kRBW][MB]) {
+  auto group_end = [&](int gl, f32x4 (&p)[RBW][MB]) {
     if (gl < ngl) {
 #pragma unroll
-      for (int b = 0; b < kRBW; ++b) {
-        const float* azr = azs + (wave * 32 + b * 16 + 4 * slot) * 8 + gl;
+      for (int b = 0; b < RBW; ++b) {
+        const float* azr = azs + (wrow * RBW * 16 + b * 16 + 4 * slot) * GPS + gl;
         float av[4], nb[4];  // alpha 2^(8-r), -alpha (z + shift)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          av[e] = azr[e * 8];
-          nb[e] = azr[kRows * 8 + e * 8];
+          av[e] = azr[e * GPS];
+          nb[e] = azr[ROWS_WG * GPS + e * GPS];
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -274,7 +300,7 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
       }
     }
 #pragma unroll
-    for (int b = 0; b < kRBW; ++b)
+    for (int b = 0; b < RBW; ++b)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -282,14 +308,14 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   };
 
 #pragma unroll 1
-  for (int base = 0; base < steps; base += DEPTH) {
+  for (int base = s0; base < s1; base += DEPTH) {
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
       const int st = base + j;
-      if (st < steps) {
-        uint32_t d[kRBW][LD::NW];
+      if (st < s1) {
+        uint32_t d[RBW][LD::NW];
 #pragma unroll
-        for (int b = 0; b < kRBW; ++b) {
+        for (int b = 0; b < RBW; ++b) {
           LD::words(buf[b][j], d[b]);
           if constexpr (C::SWAP) {
             // after the exchange words 0-1 hold first-group codes and words
@@ -313,7 +339,7 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
                 bf16x8, *reinterpret_cast<const u32x4*>(xp + (size_t)mb * 16 * xstride + xo));
           }
 #pragma unroll
-          for (int b = 0; b < kRBW; ++b) {
+          for (int b = 0; b < RBW; ++b) {
             const bf16x8 w = unpack_b<R>(d[b], i, uk, uk36);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
@@ -336,12 +362,32 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
         }
       }
       // refill this slot after its last use (while steps remain)
-      if (st + DEPTH < steps) {
+      if (st + DEPTH < s1) {
 #pragma unroll
-        for (int b = 0; b < kRBW; ++b)
+        for (int b = 0; b < RBW; ++b)
           buf[b][j] = LD::load(wr, loff(b, st + DEPTH), loff_lo(b, st + DEPTH));
       }
     }
+  }
+
+  // ---- two parts of K: the second half's sums go through LDS and are
+  //      added to the first's (fixed order); the first half's waves store
+  if constexpr (KH == 2) {
+    float* rw = red + (size_t)(wrow * 64 + lane) * RBW * MB * 4;
+    if (kh == 1) {
+#pragma unroll
+      for (int b = 0; b < RBW; ++b)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          *reinterpret_cast<f32x4*>(rw + (b * MB + mb) * 4) = acc[b][mb];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int b = 0; b < RBW; ++b)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[b][mb] += *reinterpret_cast<const f32x4*>(rw + (b * MB + mb) * 4);
   }
 
   // ---- epilogue: lane holds rows n = row block + 4 * slot + e (e = 0..3)
@@ -357,8 +403,8 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
       for (int gl = 0; gl < ngl; ++gl) tot += sxs[gl * ROWS + m];
     }
 #pragma unroll
-    for (int b = 0; b < kRBW; ++b) {
-      const int nb0 = n0 + wave * 32 + b * 16 + 4 * slot;
+    for (int b = 0; b < RBW; ++b) {
+      const int nb0 = n0 + wrow * RBW * 16 + b * 16 + 4 * slot;
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -405,16 +451,27 @@ __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ p
 
 struct PanelPlan {
   int slices, panels;
+  bool whole;  // one workgroup per 64-row panel over all of K (no partial slices)
 };
 
+// Whole K per workgroup needs the activations of all of K in LDS (M <= 16,
+// K <= kKFull, in whole 512-code pieces) and enough 64-row panels to fill
+// the chip (N >= 12288: 192 or more); otherwise K is split over workgroups.
 static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
-  (void)M;
   PanelPlan p;
-  p.panels = (int)((N + panel::kRows - 1) / panel::kRows);
-  // K slice: the largest the activations allow in LDS (1024 codes): longer
-  // workgroups and fewer partial slices measured faster than more, shorter
-  // ones at the Mistral shapes (M = 16 and 64)
-  p.slices = (int)((K + panel::kKSlice - 1) / panel::kKSlice);
+  p.whole = M <= 16 && K <= panel::kKFull && K % 512 == 0 && N >= 12288;
+  if (p.whole) {
+    using S = panel::Shape<panel::kKFull, 1, 2>;
+    p.panels = (int)((N + S::ROWS_WG - 1) / S::ROWS_WG);
+    p.slices = 1;
+  } else {
+    using S = panel::Shape<panel::kKSlice, 2, 1>;
+    p.panels = (int)((N + S::ROWS_WG - 1) / S::ROWS_WG);
+    // K slice: the largest the activations allow in LDS at M = 64 (1024
+    // codes): longer workgroups and fewer partial slices measured faster
+    // than more, shorter ones at the Mistral shapes (M = 16 and 64)
+    p.slices = (int)((K + panel::kKSlice - 1) / panel::kKSlice);
+  }
   return p;
 }
 
@@ -423,19 +480,21 @@ size_t panel_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return p.slices > 1 ? (size_t)p.slices * M * N * 4 : 0;
 }
 
-template <int R, int MB, bool GROUPED>
+template <int R, int MB, bool GROUPED, int KSL, int RBW, int KH>
 static hipError_t launch_panel_t(const panel::Args& a, const PanelPlan& p, hipStream_t s) {
   using namespace panel;
-  const size_t lds = (size_t)16 * MB * (kKSlice + kXPadE) * 2 + (size_t)(kKSlice / 128) * 16 * MB * 4 +
-                     (size_t)2 * kRows * 8 * 4;
+  using S = Shape<KSL, RBW, KH>;
+  const size_t lds = (size_t)16 * MB * (KSL + kXPadE) * 2 + (size_t)S::GPS * 16 * MB * 4 +
+                     (size_t)2 * S::ROWS_WG * S::GPS * 4 +
+                     (KH == 2 ? (size_t)S::WPK * 64 * RBW * MB * 4 * 4 : 0);
   // the LDS limit is raised once per process (a function-local static is
   // initialized exactly once, also when several host threads launch)
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)panel_kernel<R, MB, GROUPED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
+      (const void*)panel_kernel<R, MB, GROUPED, KSL, RBW, KH>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((panel_kernel<R, MB, GROUPED>), dim3(p.panels, p.slices), dim3(64 * kNW), lds,
-                     s, a);
+  hipLaunchKernelGGL((panel_kernel<R, MB, GROUPED, KSL, RBW, KH>), dim3(p.panels, p.slices),
+                     dim3(64 * kNW), lds, s, a);
   return hipGetLastError();
 }
 
@@ -443,11 +502,18 @@ static hipError_t launch_panel_t(const panel::Args& a, const PanelPlan& p, hipSt
 template <int R>
 static hipError_t launch_panel_r(const panel::Args& a, const PanelPlan& p, bool grouped,
                                  hipStream_t s) {
+  using namespace panel;
+  if (p.whole)
+    return grouped ? launch_panel_t<R, 1, true, kKFull, 1, 2>(a, p, s)
+                   : launch_panel_t<R, 1, false, kKFull, 1, 2>(a, p, s);
   if (a.M <= 16)
-    return grouped ? launch_panel_t<R, 1, true>(a, p, s) : launch_panel_t<R, 1, false>(a, p, s);
+    return grouped ? launch_panel_t<R, 1, true, kKSlice, 2, 1>(a, p, s)
+                   : launch_panel_t<R, 1, false, kKSlice, 2, 1>(a, p, s);
   if (a.M <= 32)
-    return grouped ? launch_panel_t<R, 2, true>(a, p, s) : launch_panel_t<R, 2, false>(a, p, s);
-  return grouped ? launch_panel_t<R, 4, true>(a, p, s) : launch_panel_t<R, 4, false>(a, p, s);
+    return grouped ? launch_panel_t<R, 2, true, kKSlice, 2, 1>(a, p, s)
+                   : launch_panel_t<R, 2, false, kKSlice, 2, 1>(a, p, s);
+  return grouped ? launch_panel_t<R, 4, true, kKSlice, 2, 1>(a, p, s)
+                 : launch_panel_t<R, 4, false, kKSlice, 2, 1>(a, p, s);
 }
 
 hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, const float* zero,

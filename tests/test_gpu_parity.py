@@ -412,6 +412,55 @@ def test_gemm_small(r, group, M):
     compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm r{r} g{g} M{M}")
 
 
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [12, 24, 40])
+def test_gemm_small_batch_every_instance(r, group, M):
+    """The small-batch kernel at every precision, both scale granularities
+    and each number of 16-row activation blocks (1, 2, 4), with a ragged
+    last panel and three K slices whose last is short: 128 codes at group
+    128 (at r = 2 a step spans two groups, the second past the slice) and 64
+    codes per-channel (a partial step at r = 2, 3, 4 and 6).  N = 300 takes
+    the 16-byte output stores, N = 302 the element stores."""
+    n = 300 if group == 128 else 302
+    k = 2176 if group == 128 else 2112
+    g = k if group == "K" else 128
+    note(f"gemm small-batch every instance r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=7)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=7, heavy_channels=8)
+    plane = mq.pack(m["q_d"], r)
+    y, check = guarded_f32(M, n)
+    mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
+    torch.cuda.synchronize()
+    check(f"gemm small-batch r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm every instance r{r} g{g} M{M}")
+
+
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [9, 16])
+@pytest.mark.parametrize("k", [2048, 4096])
+def test_gemm_small_batch_whole_k(r, group, M, k):
+    """M <= 16 with many output rows (N >= 12288) and K <= 4096: one
+    workgroup takes a 64-row panel over all of K, its two halves of K summed
+    in LDS (no partial slices, no second launch).  N = 12300 leaves a ragged
+    last panel; K = 4096 fills the staged activations' LDS."""
+    if k == 4096 and not (r in (4, 2) and M == 16):
+        pytest.skip("K = 4096 at r = 4 and 2, M = 16 only (the oracle's cost)")
+    n = 12300
+    g = k if group == "K" else 128
+    note(f"gemm small-batch whole K r={r} g={g} M={M} K={k}")
+    m = quantized("mistral_small", n, k, g, matrix=8)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=8, heavy_channels=8)
+    plane = mq.pack(m["q_d"], r)
+    assert mq.gemm_workspace_bytes(M, n, k, g) == 0  # no partial slices on this path
+    y, check = guarded_f32(M, n)
+    mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
+    torch.cuda.synchronize()
+    check(f"gemm whole K r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm whole K r{r} g{g} M{M} K{k}")
+
+
 @pytest.mark.parametrize("r", [8, 4, 2])
 @pytest.mark.parametrize("group", ["K", 128])
 @pytest.mark.parametrize("M", [65, 100, 127, 128, 255])
