@@ -39,14 +39,16 @@ namespace mq {
 namespace panel {
 
 constexpr int kKSlice = 1024;          // codes of K per workgroup when K is split over workgroups
-constexpr int kKFull = 4096;           // longest K one workgroup takes whole (M <= 16)
+constexpr int kKFull = 4096;           // codes of K per workgroup of the 64-row panels (M <= 16)
 constexpr int kXPadE = 8;              // bf16 padding per staged activation row
 constexpr int kNW = 8;                 // waves per workgroup
 
-// Workgroup shapes.  Split: 8 waves x two 16-row blocks = 256 weight rows,
-// K in slices of kKSlice over blockIdx.y (partials summed by reduce_slices).
-// Whole K (M <= 16, K <= kKFull): 4 row blocks x 2 halves of K = 64 weight
-// rows; the two halves are summed in LDS (fixed order), no second launch.
+// Workgroup shapes (K in slices over blockIdx.y; when there are several,
+// reduce_slices sums the partials in slice order):
+//  - 8 waves x two 16-row blocks = 256 weight rows, slices of kKSlice codes;
+//  - M <= 16: 4 row blocks x 2 halves of the slice = 64 weight rows, slices
+//    of kKFull codes (one slice up to K = 4096); the two halves are summed
+//    in LDS (fixed order).
 template <int KSL, int RBW, int KH>
 struct Shape {
   static constexpr int WPK = kNW / KH;         // waves per part of K
@@ -451,19 +453,24 @@ __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ p
 
 struct PanelPlan {
   int slices, panels;
-  bool whole;  // one workgroup per 64-row panel over all of K (no partial slices)
+  bool wide;  // 64-row panels over slices of kKFull codes (halves of a slice summed in LDS)
 };
 
-// Whole K per workgroup needs the activations of all of K in LDS (M <= 16,
-// K <= kKFull, in whole 512-code pieces) and enough 64-row panels to fill
-// the chip (N >= 12288: 192 or more); otherwise K is split over workgroups.
+// At M <= 16 the activations of kKFull codes fit in LDS, so a workgroup can
+// take a 64-row panel over a slice of up to 4096 codes, in whole 512-code
+// pieces: at N >= 12288 and K <= 4096 that is all of K (no partial slices,
+// no second launch), at the 4096-wide down projection (K = 14336) four
+// slices instead of fourteen.  It is used when its workgroups fill the chip
+// (192 or more); otherwise 256-row panels over slices of kKSlice codes.
 static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
   PanelPlan p;
-  p.whole = M <= 16 && K <= panel::kKFull && K % 512 == 0 && N >= 12288;
-  if (p.whole) {
-    using S = panel::Shape<panel::kKFull, 1, 2>;
-    p.panels = (int)((N + S::ROWS_WG - 1) / S::ROWS_WG);
-    p.slices = 1;
+  using W = panel::Shape<panel::kKFull, 1, 2>;
+  const int64_t wpanels = (N + W::ROWS_WG - 1) / W::ROWS_WG;
+  const int64_t wslices = (K + panel::kKFull - 1) / panel::kKFull;
+  p.wide = M <= 16 && K % 512 == 0 && wpanels * wslices >= 192;
+  if (p.wide) {
+    p.panels = (int)wpanels;
+    p.slices = (int)wslices;
   } else {
     using S = panel::Shape<panel::kKSlice, 2, 1>;
     p.panels = (int)((N + S::ROWS_WG - 1) / S::ROWS_WG);
@@ -503,7 +510,7 @@ template <int R>
 static hipError_t launch_panel_r(const panel::Args& a, const PanelPlan& p, bool grouped,
                                  hipStream_t s) {
   using namespace panel;
-  if (p.whole)
+  if (p.wide)
     return grouped ? launch_panel_t<R, 1, true, kKFull, 1, 2>(a, p, s)
                    : launch_panel_t<R, 1, false, kKFull, 1, 2>(a, p, s);
   if (a.M <= 16)

@@ -461,6 +461,27 @@ def test_gemm_small_batch_whole_k(r, group, M, k):
     compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm whole K r{r} g{g} M{M} K{k}")
 
 
+@pytest.mark.parametrize("r", [8, 6, 4, 3, 2])
+@pytest.mark.parametrize("group", ["K", 128])
+@pytest.mark.parametrize("M", [9, 16])
+def test_gemm_small_batch_wide_panels_split_k(r, group, M):
+    """M <= 16, K longer than one 4096-code slice: 64-row panels over three
+    slices (4096, 4096, 512 codes), each slice's halves summed in LDS, the
+    slices by reduce_slices; 65 panels (N = 4100, ragged) x 3 slices."""
+    n, k = 4100, 8704
+    g = k if group == "K" else 128
+    note(f"gemm small-batch wide panels split K r={r} g={g} M={M}")
+    m = quantized("mistral_small", n, k, g, matrix=9)
+    xb = inputs.activations_bf16("mistral_small", M, k, matrix=9, heavy_channels=8)
+    plane = mq.pack(m["q_d"], r)
+    assert mq.gemm_workspace_bytes(M, n, k, g) == 3 * M * n * 4  # three partial slices
+    y, check = guarded_f32(M, n)
+    mq.gemm(plane, r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
+    torch.cuda.synchronize()
+    check(f"gemm wide split r{r} g{g} M{M}")
+    compare_linear(y, xb, m["q"], m["alpha"], m["zero"], g, r, f"gemm wide split r{r} g{g} M{M}")
+
+
 @pytest.mark.parametrize("r", [8, 4, 2])
 @pytest.mark.parametrize("group", ["K", 128])
 @pytest.mark.parametrize("M", [65, 100, 127, 128, 255])
