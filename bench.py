@@ -128,6 +128,17 @@ def run_main(torch, mq, inputs, dev, steps, warmup):
     t1 = T.event()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    # spread of single steps: 50 more steps, each between its own two events
+    # (the events add their own cost to each reading)
+    pairs = []
+    for j in range(50):
+        a = T.event()
+        step(warmup + steps + j)
+        pairs.append((a, T.event()))
+    torch.cuda.synchronize()
+    one = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    spread = {"p10": round(one[4], 2), "median": round(one[25], 2), "p90": round(one[44], 2),
+              "n": 50, "how": "each step between its own two HIP events"}
     # for reference: each r alone (three products per launch), back to back
     # (replayed from a graph: see time_loop)
     per_r_us = {}
@@ -137,7 +148,17 @@ def run_main(torch, mq, inputs, dev, steps, warmup):
                   for ps in planes[r]]
         per_r_us[r] = time_loop(torch, lambda i: single[i % len(single)](), max(steps, 50),
                                 stream=side)
-    return dict(total_ms=total_ms, step_bytes=step_bytes, per_r_us=per_r_us, mats=mats)
+    # and each matrix alone at each r (one product per launch)
+    per_matrix_us = {}
+    for r in RS:
+        per_matrix_us[f"r{r}"] = {}
+        for j, m in enumerate(mats):
+            alone = [mq.GemvGroupedPlan(gemma_problems(mq, [m], [ps[j]]), r, 1, side)
+                     for ps in planes[r]]
+            per_matrix_us[f"r{r}"][m["name"]] = round(
+                time_loop(torch, lambda i: alone[i % len(alone)](), 50, stream=side), 2)
+    return dict(total_ms=total_ms, step_bytes=step_bytes, per_r_us=per_r_us, mats=mats,
+                spread=spread, per_matrix_us=per_matrix_us)
 
 
 # --------------------------------------------------------------------------- roofline
@@ -287,8 +308,26 @@ def row_prefill_down(torch, mq, inputs, dev):
     return down
 
 
+def row_tiny(torch, mq, inputs, dev):
+    """The tiny linear (K = 512 -> N = 256, per-channel) at M = 1 and 4: the
+    parity configuration, launch-bound; microseconds per call."""
+    n, k = 256, 512
+    w = torch.from_numpy(inputs.gaussian_weights("tiny_linear", n, k)).to(dev)
+    codes, alpha, zero = mq.quantize(w, k)
+    out = {}
+    for r in RS:
+        pl = mq.pack(codes, r)
+        for m in (1, 4):
+            x = torch.from_numpy(inputs.activations_bf16("tiny_linear", m, k).view("int16")).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            us = time_loop(torch, lambda i: mq.gemv(pl, r, alpha, zero, k, n, k, x, out=y), 50)
+            out[f"r{r}_M{m}"] = round(us, 2)
+    return out
+
+
 # name -> (function, what it measures); run in this order
 ROWS = {
+    "gemv_tiny_linear": (row_tiny, "parity configuration: 512 -> 256, M = 1, 4"),
     "pack_gemma_down": (row_pack, "a1 slice-and-pack"),
     "gemm_mistral_small": (row_small, "a3 small-batch GEMM"),
     "gemm_prefill_M2048": (row_prefill, "a4 prefill GEMM"),
@@ -573,10 +612,37 @@ def cpu_baseline(inputs):
                 nbytes += linear_bytes(n, k, r, k, 1)
         reps += 1
     dt = time.perf_counter() - t0
+    # the same oracle on one thread: the tiny linear (K = 512 -> N = 256) at
+    # every r and M = 1, 4, and the Gemma down matrix at r = 4 once
+    one_thread = None
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            tq, ta, tz = oracle.quantize_minmax(inputs.gaussian_weights("tiny_linear", 256, 512), 512)
+            tiny = {}
+            for r in RS:
+                for m in (1, 4):
+                    tx = inputs.activations_bf16("tiny_linear", m, 512)
+                    n_calls, t1 = 0, time.perf_counter()
+                    while n_calls == 0 or time.perf_counter() - t1 < 0.3:
+                        oracle.linear(tx, tq, ta, tz, 512, r)
+                        n_calls += 1
+                    tiny[f"r{r}_M{m}"] = round((time.perf_counter() - t1) / n_calls * 1e6, 1)
+            q, a, z, k, xb, n = data[2]
+            t1 = time.perf_counter()
+            oracle.linear(xb, q, a, z, k, 4)
+            dd = time.perf_counter() - t1
+            one_thread = {"cores": 1, "tiny_linear_us_per_call": tiny,
+                          "gemma_down_r4_s": round(dd, 3),
+                          "gemma_down_r4_GBs": round(linear_bytes(n, k, 4, k, 1) / dd / 1e9, 4)}
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"{reps} full steps: the 3 Gemma-2-9B MLP matrices at r=8,4,2, batch 1, "
-                       f"float64 numpy oracle, {dt:.1f} s")}
+                       f"float64 numpy oracle, {dt:.1f} s"),
+            "one_thread": one_thread}
 
 
 # --------------------------------------------------------------------------- entry
@@ -644,6 +710,8 @@ def main():
                 "measured_read_peak": read_step,
                 "frac_of_measured_read": round(achieved / read_step, 4),
                 "per_r_single_mlp_launch": per_r,
+                "per_matrix_launch_us": res["per_matrix_us"],
+                "step_spread_us": res["spread"],
                 "measured_peaks": peaks}
     del res
 

@@ -58,6 +58,7 @@ struct Sk {
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
 constexpr int kSkinnyWaves = 4;   // waves per workgroup
+constexpr int kSkinnyFillTiles = 256;  // workgroups a launch should have (one per CU)
 
 template <int R>
 __device__ __forceinline__ bf16x8 unpack_op(const uint32_t* d, int i, const UnpackK& k,
@@ -519,6 +520,31 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
       p.tiles = (rblocks + p.rbpw - 1) / p.rbpw;
       steps_per_wave[i] = steps / p.ks;
     }
+  }
+  // fill: a launch with fewer workgroups than CUs (a lone 14336-long down
+  // projection at r = 2 gets 112) splits the K of its longest problem further
+  // while every wave keeps at least 8 load steps (r = 2 down alone: 13.4 ->
+  // about 9 us)
+  for (;;) {
+    int tiles = 0, best = -1;
+    for (int i = 0; i < args.count; ++i) tiles += args.p[i].tiles;
+    if (tiles >= kSkinnyFillTiles) break;
+    for (int i = 0; i < args.count; ++i) {
+      const SkinnyProblem& p = args.p[i];
+      const int steps = ((p.K + 511) / 512) * 512 / step_codes(p.r, grouped);
+      const int spg = grouped ? 128 / step_codes(p.r, grouped) : 1;
+      const int ks_max = p.y2 ? waves / 2 : waves;
+      if (p.ks < ks_max && ((steps / spg) / (p.ks * 2)) * spg >= 8 &&
+          (best < 0 || steps_per_wave[i] > steps_per_wave[best]))
+        best = i;
+    }
+    if (best < 0) break;
+    SkinnyProblem& p = args.p[best];
+    p.ks *= 2;
+    p.rbpw = waves / p.ks;
+    const int rblocks = (p.N + 15) / 16 * (p.y2 ? 2 : 1);
+    p.tiles = (rblocks + p.rbpw - 1) / p.rbpw;
+    steps_per_wave[best] = ((p.K + 511) / 512) * 512 / step_codes(p.r, grouped) / p.ks;
   }
   // longest workgroups first: they start early and the short ones fill in
   for (int i = 1; i < args.count; ++i)
