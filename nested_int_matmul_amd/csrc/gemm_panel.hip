@@ -6,8 +6,10 @@
 //
 // Design (gfx950, v_mfma_f32_16x16x32_bf16, A = weights, B = activations):
 //  - A workgroup owns a panel of 256 weight rows (8 waves x two 16-row
-//    blocks) and a slice of K of at most 1024 codes.  The activations of that
-//    slice (all M rows, padded to 16 * MB) are brought into LDS once with
+//    blocks) and a slice of K of at most 1024 codes; or, at M <= 16, a panel
+//    of 64 rows (four 16-row blocks x two halves of the slice) and a slice of
+//    up to 4096 codes, which at K <= 4096 is all of K.  The activations of
+//    the slice (all M rows, padded to 16 * MB) are brought into LDS once with
 //    buffer-to-LDS loads; the per-128 sums of x are formed from LDS.
 //  - Four lanes share a weight row and load 16 contiguous packed bytes each
 //    per step, so one load instruction reads 64 contiguous bytes of each of
@@ -26,9 +28,10 @@
 //    activations; group-128 scales are applied at each group end in fp32
 //    (y += alpha 2^(8-r) P_g - alpha (z + shift) sum_g x), per-channel scales
 //    once at the end.
-//  - When K is split over several workgroups, each writes its fp32 partial
-//    tile to the workspace and a second kernel sums the slices in a fixed
-//    order (deterministic).
+//  - The two halves of a 64-row panel's slice are summed in LDS, the first
+//    half's sums then the second's.  When K is split over several
+//    workgroups, each writes its fp32 partial tile to the workspace and a
+//    second kernel sums the slices in a fixed order (deterministic).
 #include <algorithm>
 
 #include "mq_device.h"
