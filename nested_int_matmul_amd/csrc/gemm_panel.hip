@@ -118,7 +118,10 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   constexpr int ROWS_WG = S::ROWS_WG, GPS = S::GPS;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: in a scalar register, the loop bounds below
+  // and every branch on them are scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, slot = lane >> 4;
   const int wrow = wave % S::WPK, kh = wave / S::WPK;  // row group and part of K of this wave
   const int M = a.M, N = a.N, K = a.K, G = a.G;
@@ -135,10 +138,13 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   }
   constexpr int xstride = KSL + kXPadE;           // elements
 
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [ROWS][xstride]
-  float* sxs = reinterpret_cast<float*>(smem + (size_t)ROWS * xstride * 2);      // [ngl][ROWS]
-  float* azs = sxs + GPS * ROWS;                                     // [2][ROWS_WG][GPS]
-  float* red = azs + 2 * ROWS_WG * GPS;  // KH = 2: [WPK][64][RBW][MB][4] second half's sums
+  // the small arrays first, so that their reads take immediate offsets (under
+  // 64 KiB), the staged activations after them
+  float* azs = reinterpret_cast<float*>(smem);  // [2][GPS][ROWS_WG] (staged as [2][ROWS_WG][GPS])
+  float* sxs = azs + 2 * ROWS_WG * GPS;         // [ngl][ROWS]
+  float* red = sxs + GPS * ROWS;  // KH = 2: [WPK][64][RBW][MB][4] second half's sums
+  uint16_t* xs = reinterpret_cast<uint16_t*>(red + (KH == 2 ? S::WPK * 64 * RBW * MB * 4 : 0));
+  // [ROWS][xstride]
 
   const int n0 = (int)blockIdx.x * ROWS_WG;
   const int rowbytes = K * R / 8;
@@ -225,12 +231,28 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   }
   __syncthreads();
 
-  // ---- group factors in place: alpha 2^(8-r) and -alpha (z + shift)
+  // ---- group factors: alpha 2^(8-r) and -alpha (z + shift), transposed to
+  //      [group][row] so that a lane's four consecutive output rows are one
+  //      16-byte read.  Each wave instruction takes 64 rows on a diagonal of
+  //      the groups (row rbase + lane, group (lane / Q + c) mod GPS): its reads
+  //      of the [row][group] layout fall on 64 distinct banks, its writes on
+  //      64 consecutive words.  All reads are done before a barrier, the
+  //      writes after it (the transpose is in place).
+  constexpr int kTr = ROWS_WG * GPS / (64 * kNW);  // entries per thread
+  static_assert(ROWS_WG * GPS == kTr * 64 * kNW && 64 % GPS == 0 && ROWS_WG % 64 == 0,
+                "the diagonal transpose covers the panel's scales exactly");
+  float tav[kTr], tnb[kTr];
+  int tdst[kTr];
   if (GROUPED) {
-    for (int t = tid; t < ROWS_WG * GPS; t += 64 * kNW) {
-      const float al = azs[t], ze = azs[ROWS_WG * GPS + t];
-      azs[t] = al * Enc<R>::kStep;
-      azs[ROWS_WG * GPS + t] = -al * (ze + Enc<R>::kOffsetShift);
+    constexpr int Q = 64 / GPS;
+#pragma unroll
+    for (int k = 0; k < kTr; ++k) {
+      const int q = wave + k * kNW;
+      const int r = (q / GPS) * 64 + lane, g = (lane / Q + q % GPS) % GPS;
+      const float al = azs[r * GPS + g], ze = azs[ROWS_WG * GPS + r * GPS + g];
+      tav[k] = al * Enc<R>::kStep;
+      tnb[k] = -al * (ze + Enc<R>::kOffsetShift);
+      tdst[k] = g * ROWS_WG + r;
     }
   }
 
@@ -252,6 +274,14 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) sp = dot2_bf16(w[c][q], ones, sp);
       sxs[gl * ROWS + m] = sp;
+    }
+  }
+  if (GROUPED) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTr; ++k) {
+      azs[tdst[k]] = tav[k];
+      azs[ROWS_WG * GPS + tdst[k]] = tnb[k];
     }
   }
   __syncthreads();
@@ -288,13 +318,10 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
     if (gl < ngl) {
 #pragma unroll
       for (int b = 0; b < RBW; ++b) {
-        const float* azr = azs + (wrow * RBW * 16 + b * 16 + 4 * slot) * GPS + gl;
-        float av[4], nb[4];  // alpha 2^(8-r), -alpha (z + shift)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          av[e] = azr[e * GPS];
-          nb[e] = azr[ROWS_WG * GPS + e * GPS];
-        }
+        const float* azr = azs + gl * ROWS_WG + wrow * RBW * 16 + b * 16 + 4 * slot;
+        // alpha 2^(8-r) and -alpha (z + shift) of the lane's four rows
+        const f32x4 av = *reinterpret_cast<const f32x4*>(azr);
+        const f32x4 nb = *reinterpret_cast<const f32x4*>(azr + ROWS_WG * GPS);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const float sx = sxs[gl * ROWS + mb * 16 + col];
