@@ -187,6 +187,12 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
     }
   }
 
+  // every wave has issued its activation and scale loads before any wave
+  // issues weight loads, so that the staged data (cache hits) is not queued
+  // behind weight requests to HBM (no wait here: the loads stay in flight);
+  // measured at M = 16: 12.7 -> 12.0 us (14336 x 4096, r = 4)
+  __builtin_amdgcn_s_barrier();
+
   // ---- the first DEPTH weight loads of both row blocks
   // split planes: the lane's high-plane bytes, and its low-plane bytes after
   // all N rows of the high plane
