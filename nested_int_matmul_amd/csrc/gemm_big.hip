@@ -98,7 +98,10 @@ __global__ void __launch_bounds__(THREADS)
   unsigned char* ws0 = smem + 2 * XT_BYTES;                   // [2][BN][WROW]
   float* sxg = reinterpret_cast<float*>(smem + 2 * XT_BYTES + 2 * C::WT_BYTES);  // [BM]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: in a scalar register, the staging addresses
+  // derived from it (and the LDS bases of buffer-to-LDS loads) stay scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
   // ---- tile of this workgroup: the workgroups of one XCD (id % 8) walk
