@@ -462,21 +462,43 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
 }
 
 // y = sum over S slices of the partial tiles, in slice order.  16-byte
-// vectors only when every slice starts 16-byte aligned (count % 4 == 0).
+// vectors only when every slice starts 16-byte aligned (count % 4 == 0).  The
+// slices of an element are loaded kReduceBatch at a time, all issued before
+// the first is added (a slice per memory latency otherwise), and added in
+// slice order.
+constexpr int kReduceBatch = 8;
+
 __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ part,
                                                      float* __restrict__ y, int64_t count,
                                                      int S) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t n4 = (count & 3) ? 0 : count >> 2;
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(part);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    f32x4 v = reinterpret_cast<const f32x4*>(part)[i];
-    for (int sl = 1; sl < S; ++sl) v += reinterpret_cast<const f32x4*>(part + sl * count)[i];
+    f32x4 v = p4[i];
+    for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
+      f32x4 t[kReduceBatch];
+#pragma unroll
+      for (int b = 0; b < kReduceBatch; ++b)
+        if (s0 + b < S) t[b] = p4[(int64_t)(s0 + b) * n4 + i];
+#pragma unroll
+      for (int b = 0; b < kReduceBatch; ++b)
+        if (s0 + b < S) v += t[b];
+    }
     reinterpret_cast<f32x4*>(y)[i] = v;
   }
   for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
        i += stride) {
     float v = part[i];
-    for (int sl = 1; sl < S; ++sl) v += part[sl * count + i];
+    for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
+      float t[kReduceBatch];
+#pragma unroll
+      for (int b = 0; b < kReduceBatch; ++b)
+        if (s0 + b < S) t[b] = part[(int64_t)(s0 + b) * count + i];
+#pragma unroll
+      for (int b = 0; b < kReduceBatch; ++b)
+        if (s0 + b < S) v += t[b];
+    }
     y[i] = v;
   }
 }
