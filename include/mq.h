@@ -312,8 +312,9 @@ MQ_API mq_status mq_gemv_bitplanes(const uint8_t* planes, int r, int extra, cons
  *   h = h + o + d                             (fp32 residual stream)
  * k and v are computed and written to the workspace but not consumed.
  * Shapes: q, o: [H, H]; k, v: [Hkv, H]; up, gate: [F, H]; down: [H, F];
- * the same H, Hkv, F in every layer.  Each mq_linear holds the plane packed
- * at its layer's r.
+ * the same H, Hkv, F in every layer, H <= 16384 (the norm holds a row in
+ * registers; larger H returns MQ_ERR_SHAPE).  Each mq_linear holds the plane
+ * packed at its layer's r.
  */
 typedef struct mq_linear {
   const uint8_t* packed; /* uint8 [N, K*r/8] at the layer's r */

@@ -379,6 +379,7 @@ mq_status check_stack(const mq_layer* layers, int n_layers, int64_t M, StackDims
   if (!layers) return MQ_ERR_NULL;
   if (n_layers < 1 || M < 1 || M > mq::kSkinnyMaxM) return MQ_ERR_SHAPE;
   const int64_t H = layers[0].q.N, Hkv = layers[0].k.N, F = layers[0].up.N;
+  if (H > mq::kStackMaxH) return MQ_ERR_SHAPE;  // the norm holds a row in registers
   for (int i = 0; i < n_layers; ++i) {
     const mq_layer& L = layers[i];
     const mq_linear* all[7] = {&L.q, &L.k, &L.v, &L.o, &L.up, &L.gate, &L.down};

@@ -14,7 +14,8 @@ namespace mq {
 constexpr int kNormThreads = 1024;
 
 // One workgroup per activation row.  Thread t owns the 4-float vectors
-// t, t + 1024, ... (at most VPT of them: H <= 4096 VPT): they stay in
+// t, t + 1024, ... (at most VPT of them: H <= 4096 VPT, VPT = 1 or 4 for
+// H <= kStackMaxH): they stay in
 // registers between the two passes, and all their loads are issued before
 // the first is used, so a row costs a few memory latencies rather than one
 // per vector.  Fixed-order reduction (deterministic).  LOAD: h = x first
@@ -90,14 +91,11 @@ static hipError_t launch_norm(float* h, const float* o, const float* d, uint16_t
   if (per <= 1)
     hipLaunchKernelGGL((norm_kernel<RESIDUAL, NORM, LOAD, 1>), grid, block, 0, stream, h, o, d,
                        a, (int)H, x0);
-  else if (per <= 4)
+  else if (per <= 4 && H <= kStackMaxH)
     hipLaunchKernelGGL((norm_kernel<RESIDUAL, NORM, LOAD, 4>), grid, block, 0, stream, h, o, d,
                        a, (int)H, x0);
-  else if (per <= 16)
-    hipLaunchKernelGGL((norm_kernel<RESIDUAL, NORM, LOAD, 16>), grid, block, 0, stream, h, o, d,
-                       a, (int)H, x0);
   else
-    return hipErrorInvalidValue;  // H > 65536 is rejected before any launch
+    return hipErrorInvalidValue;  // H > kStackMaxH is rejected before any launch
   return hipGetLastError();
 }
 

@@ -107,7 +107,8 @@ struct OverflowProblem {
 hipError_t launch_overflow_apply(OverflowProblem* probs, int count, int r, int64_t M,
                                  hipStream_t s);
 
-// Mix'n'Match helpers.
+// Mix'n'Match helpers.  The norm keeps a row in registers: H <= kStackMaxH.
+constexpr int64_t kStackMaxH = 16384;
 hipError_t launch_rmsnorm_bf16(const float* h, uint16_t* a, int64_t M, int64_t H,
                                hipStream_t stream);
 // h = x (bf16, exact in fp32), then a = bf16(h / rms(h))

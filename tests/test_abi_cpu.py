@@ -198,6 +198,10 @@ def test_mixnmatch_validation(L):
     assert L.mq_mixnmatch_forward(_layer(o=bad), 1, P16, 1, P16, P16, ws, NULL) == 5
     bad = mq.Linear(0x10000, 0x10000, 0x10000, 64, 128, 128)                   # down-shaped o
     assert L.mq_mixnmatch_forward(_layer(o=bad), 1, P16, 1, P16, P16, ws, NULL) == 2
+    # the norm holds a row in registers: H up to 16384
+    assert L.mq_mixnmatch_workspace_bytes(_layer(H=16384), 1, 1) > 0
+    assert L.mq_mixnmatch_workspace_bytes(_layer(H=16448), 1, 1) == 0
+    assert L.mq_mixnmatch_forward(_layer(H=16448), 1, P16, 1, P16, P16, ws, NULL) == 2
 
 
 def test_gemm_noalloc_validation(L):

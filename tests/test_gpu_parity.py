@@ -699,6 +699,35 @@ def test_mixnmatch_small_stack(group_kind, M, rs):
     assert torch.equal(h, h_out)
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_mixnmatch_wide_rows(M):
+    """H = 4160 (1040 four-float vectors per row): the norm's first 16
+    threads hold two vectors and the rest one, its four-vector path partly
+    filled.  The plain, the loading and the residual norm are each checked:
+    a of a one-layer in-place call against the definition, then two layers
+    end to end from the bf16 input against the float64 stack."""
+    H, rs = 4160, [8, 2]
+    note(f"mixnmatch wide rows H={H} M={M}")
+    host, devl = _small_stack(rs, H=H, Hkv=64, F=128)
+    arr = mq.make_layers(devl)
+    xb = inputs.activations_bf16("mistral_stack", M, H)
+    h0 = oracle.float_from_bf16_bits(xb)
+    ws = torch.empty(mq.mixnmatch_workspace_bytes(arr, M), dtype=torch.uint8, device=dev())
+    off = mq.mixnmatch_workspace_offsets(mq.make_layers(devl[0:1]), M)
+    h = torch.from_numpy(h0.astype(np.float32)).to(dev())
+    mq.mixnmatch_forward_inplace(mq.make_layers(devl[0:1]), h, ws)
+    torch.cuda.synchronize()
+    a_bits = ws[off[0]:off[0] + M * H * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    want_a = oracle.bf16_bits_from_float(oracle.rms_normalize(h0))
+    mism = np.count_nonzero(a_bits.reshape(M, H) != want_a)
+    assert mism <= max(2, M * H // 200), f"{mism} bf16 rounding differences in a"
+    h_out, check = guarded_f32(M, H)
+    mq.mixnmatch_forward(arr, x_device(xb), ws, out=h_out)
+    torch.cuda.synchronize()
+    check("wide stack h_out")
+    compare(h_out, oracle.mixnmatch_forward(host, xb), "wide stack end-to-end", reg=1e-3)
+
+
 # ---------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("r", [8, 4, 2])
