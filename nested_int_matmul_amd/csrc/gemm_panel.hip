@@ -88,6 +88,7 @@ struct Args {
   const uint16_t* x;
   float* y;     // output [M, N] (one K slice) or the partial slices [S][M][N]
   int M, N, K, G;
+  int ksl;      // codes per K slice: <= the shape's KSL, a multiple of 512 when K is split
 };
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
@@ -125,8 +126,10 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   const int col = lane & 15, slot = lane >> 4;
   const int wrow = wave % S::WPK, kh = wave / S::WPK;  // row group and part of K of this wave
   const int M = a.M, N = a.N, K = a.K, G = a.G;
-  const int k0 = (int)blockIdx.y * KSL;
-  const int klen = min(KSL, K - k0);
+  const int ksl = min(a.ksl, KSL);  // (bounded by KSL in the code, so that loops over the
+                                    //  slice's groups keep a known trip count)
+  const int k0 = (int)blockIdx.y * ksl;
+  const int klen = min(ksl, K - k0);
   const int ngl = (klen + 127) >> 7;              // groups of 128 in the slice
   const int steps = (klen + C::STEP - 1) / C::STEP;
   // this wave's steps: all of the slice, or one of KH parts in whole groups
@@ -164,7 +167,8 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
     const int pc = wave + q * kNW;
     const int m = pc / PPR, j = pc % PPR;
     const int k = k0 + j * 512 + lane * 8;
-    const uint32_t off = (m < M && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
+    const uint32_t off =
+        (m < M && k < k0 + klen) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
     lds_dma16(xr, xs + (size_t)m * xstride + j * 512, off);
   }
   // ---- group-128 scales of the panel staged in LDS as
@@ -511,6 +515,7 @@ __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ p
 
 struct PanelPlan {
   int slices, panels;
+  int ksl;    // codes per slice: the slices of a split are equal (multiples of 512)
   bool wide;  // 64-row panels over slices of kKFull codes (halves of a slice summed in LDS)
 };
 
@@ -529,6 +534,7 @@ static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
   if (p.wide) {
     p.panels = (int)wpanels;
     p.slices = (int)wslices;
+    p.ksl = panel::kKFull;
   } else {
     using S = panel::Shape<panel::kKSlice, 2, 1>;
     p.panels = (int)((N + S::ROWS_WG - 1) / S::ROWS_WG);
@@ -536,6 +542,14 @@ static PanelPlan plan_panel(int64_t M, int64_t N, int64_t K) {
     // codes): longer workgroups and fewer partial slices measured faster
     // than more, shorter ones at the Mistral shapes (M = 16 and 64)
     p.slices = (int)((K + panel::kKSlice - 1) / panel::kKSlice);
+    p.ksl = panel::kKSlice;
+  }
+  // equal slices, so that no workgroup streams a longer K than the others
+  // (14336 in four slices of 3584, not 3 x 4096 + 2048); each a multiple of
+  // 512 codes (whole activation pieces and groups), at most the shape's
+  if (p.slices > 1) {
+    const int64_t per = (K + p.slices - 1) / p.slices;
+    p.ksl = (int)std::min<int64_t>((per + 511) / 512 * 512, p.ksl);
   }
   return p;
 }
@@ -595,6 +609,7 @@ hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, c
   a.N = (int)N;
   a.K = (int)K;
   a.G = (int)(K / group);
+  a.ksl = p.ksl;
   const bool grouped = group != K;
   hipError_t e;
   switch (r) {
