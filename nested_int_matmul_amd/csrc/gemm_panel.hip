@@ -403,12 +403,12 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
           }
         }
       }
-      // refill this slot after its last use (while steps remain)
-      if (st + DEPTH < s1) {
+      // refill this slot after its last use; past the wave's steps the
+      // offset points past the plane (zeros, no memory traffic), so every
+      // trip issues the same loads and the waits stay exact across trips
 #pragma unroll
-        for (int b = 0; b < RBW; ++b)
-          buf[b][j] = LD::load(wr, loff(b, st + DEPTH), loff_lo(b, st + DEPTH));
-      }
+      for (int b = 0; b < RBW; ++b)
+        buf[b][j] = LD::load(wr, loff(b, st + DEPTH), loff_lo(b, st + DEPTH));
     }
   }
 
