@@ -300,9 +300,8 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       const int bpr = clen / PB;
       const uint32_t ones = 0x3F803F80u;
       float* part_s = sxs;   // [waves] partial sums (sxs is free per-channel)
-      float* part_so = sxos;
       for (int m = 0; m < M; ++m) {
-        float s = 0.f, so = 0.f;
+        float s = 0.f;
         for (int bi = threadIdx.x; bi < bpr; bi += blockDim.x) {
           const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + bi * PB);
 #pragma unroll
@@ -310,17 +309,11 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (lane == 0) {
-          part_s[wave] = s;
-          part_so[wave] = so;
-        }
+        if (lane == 0) part_s[wave] = s;
         __syncthreads();
         if (threadIdx.x == 0) {
-          float ts = 0.f, tso = 0.f;
-          for (int w = 0; w < kSkinnyWaves; ++w) {
-            ts += part_s[w];
-            tso += part_so[w];
-          }
+          float ts = 0.f;
+          for (int w = 0; w < kSkinnyWaves; ++w) ts += part_s[w];
           sxt[m] += ts;
           sxot[m] += (float)Enc<R>::kOffset * ts;
         }
