@@ -72,13 +72,16 @@ struct Pc {
   static constexpr int SPG = STEP >= 128 ? 1 : 128 / STEP;  // steps per group (r = 8: 2)
   using LD = LoadT<R, SPLIT ? 0 : 16>;      // one lane's loads of a step
 };
-// weight loads in flight per lane and row block: a wave's whole share at
-// r = 2 and 4 of a 1024-code slice, else 8; 4 steps of the split planes
-// (two loads each)
+// weight loads in flight per lane and row block: 4 steps (or the wave's
+// whole share when shorter).  With the refills issued on every trip the wait
+// at the loop head is exact, and 4 measured best: at M = 16 against 8,
+// 14336 x 4096 r = 2 10.3 -> 9.4 us and 4096 x 14336 r = 4 / 2 13.1 -> 12.4 /
+// 12.2 -> 11.2 us; at M = 64, r = 4, 24.4 -> 23.2 us (2, 3, 6 and 12 no
+// better)
 template <int R, bool GROUPED, int KSL, int KH>
 constexpr int depth() {
   using C = Pc<R, GROUPED>;
-  return C::SPLIT ? 4 : (KSL / (C::STEP * KH) < 8 ? KSL / (C::STEP * KH) : 8);
+  return KSL / (C::STEP * KH) < 4 ? KSL / (C::STEP * KH) : 4;
 }
 
 struct Args {
