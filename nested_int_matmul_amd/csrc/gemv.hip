@@ -221,6 +221,13 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       return st < hi ? cbase_lo + (uint32_t)(st * (C::STEP * C::RL / 8)) : 0x80000000u;
     };
     typename LD::T buf[C::DEPTH];
+    // nothing in flight when the chunk starts: the previous chunk's last
+    // refills (past its steps) must land before their registers are reused.
+    // Said explicitly here, the compiler's own wait for them (which, placed
+    // after the staging loads, also waited for the activations before the
+    // first weight load) goes away, and the weights are issued behind the
+    // staging as intended.  vmcnt(0); expcnt and lgkmcnt at their maximum.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     // ---- stage x[:, ck0 : ck0 + clen) as stored, then form the per-128 sums
     //      of x and of offset * x (v_dot2 against constant bf16 pairs).
