@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
       const int bpr = clen / 8;
       const int total = M * bpr;
       const uint32_t ones = 0x3F803F80u;
-      for (int b0 = 0; b0 < total; b0 += blockDim.x) {
+      for (int b0 = 0; b0 < total; b0 += (64 * kWaves)) {
         const int b = b0 + threadIdx.x;
         float s = 0.f;
         int m = 0, kb = 0;
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(64 * kWaves) bp_gemv_kernel(const Args P) {
     const int rr = ep_rr;
     const int rbl2 = rr >> 4, row = rr & 15;
     const int n = rb0 * 16 + rr;
-    const int mstep = (int)blockDim.x / rows_wg;
+    const int mstep = (64 * kWaves) / rows_wg;
     if (n < N) {
       for (int m = threadIdx.x / rows_wg; m < M; m += mstep) {
         float s = 0.f;
@@ -362,15 +362,16 @@ __device__ __forceinline__ void transpose8x8(uint32_t& lo, uint32_t& hi) {
 // of each group of 8 gives one byte per plane, and a 4 x 4 byte transpose
 // places the four bytes of each plane (even codes 0-14, 16-30, odd codes
 // 1-15, 17-31).
-__global__ void __launch_bounds__(256) pack_bitplanes_kernel(const uint8_t* __restrict__ codes,
+constexpr int kPackThreads = 256;  // (a constant: blockDim.x is a vector load from the dispatch packet)
+__global__ void __launch_bounds__(kPackThreads) pack_bitplanes_kernel(const uint8_t* __restrict__ codes,
                                                              int N, int K,
                                                              uint8_t* __restrict__ planes) {
   const int64_t wpr = K / 32;
   const int64_t total = (int64_t)N * wpr;
   const int64_t plane_words = total;
   uint32_t* out = reinterpret_cast<uint32_t*>(planes);
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t t = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * kPackThreads) {
     const int64_t n = t / wpr;
     const int wi = (int)(t - n * wpr);
     const int sb = wi >> 4, s = (wi >> 2) & 3, g = wi & 3;
@@ -440,7 +441,7 @@ hipError_t launch_pack_bitplanes(const uint8_t* codes, int64_t N, int64_t K, uin
   const int64_t total = N * (K / 32);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(bp::pack_bitplanes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes,
+  hipLaunchKernelGGL(bp::pack_bitplanes_kernel, dim3((unsigned)blocks), dim3(bp::kPackThreads), 0, s, codes,
                      (int)N, (int)K, planes);
   return hipGetLastError();
 }

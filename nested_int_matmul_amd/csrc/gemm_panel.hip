@@ -475,13 +475,14 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
 // slice order.
 constexpr int kReduceBatch = 8;
 
-__global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ part,
+constexpr int kReduceThreads = 256;  // (a constant: blockDim.x is a vector load)
+__global__ void __launch_bounds__(kReduceThreads) reduce_slices(const float* __restrict__ part,
                                                      float* __restrict__ y, int64_t count,
                                                      int S) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t stride = (int64_t)gridDim.x * kReduceThreads;
   const int64_t n4 = (count & 3) ? 0 : count >> 2;
   const f32x4* p4 = reinterpret_cast<const f32x4*>(part);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+  for (int64_t i = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x; i < n4; i += stride) {
     f32x4 v = p4[i];
     for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
       f32x4 t[kReduceBatch];
@@ -494,7 +495,7 @@ __global__ void __launch_bounds__(256) reduce_slices(const float* __restrict__ p
     }
     reinterpret_cast<f32x4*>(y)[i] = v;
   }
-  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * kReduceThreads + threadIdx.x; i < count;
        i += stride) {
     float v = part[i];
     for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
@@ -628,7 +629,7 @@ hipError_t launch_gemm_panel(const uint8_t* packed, int r, const float* alpha, c
 
 hipError_t launch_reduce_slices(const float* part, float* y, int64_t count, int S, hipStream_t s) {
   const int blocks = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 2048);
-  hipLaunchKernelGGL(panel::reduce_slices, dim3(blocks), dim3(256), 0, s, part, y, count, S);
+  hipLaunchKernelGGL(panel::reduce_slices, dim3(blocks), dim3(panel::kReduceThreads), 0, s, part, y, count, S);
   return hipGetLastError();
 }
 

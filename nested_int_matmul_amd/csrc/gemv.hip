@@ -58,6 +58,10 @@ struct Sk {
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
 constexpr int kSkinnyWaves = 4;   // waves per workgroup
+// threads per workgroup, as a constant: blockDim.x is read from the dispatch
+// packet with a vector load, and waiting for that load would also wait for
+// every weight load issued before it
+constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 constexpr int kSkinnyFillTiles = 256;  // workgroups a launch should have (one per CU)
 
 template <int R>
@@ -157,7 +161,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       (n_ld < N) ? (uint32_t)N * hrow + (uint32_t)n_ld * lrow : plane_bytes;
 
   // per-channel epilogue operands, fetched now: thread t writes row
-  // rr = t % rows_wg of the tile, for m = t / rows_wg, + blockDim / rows_wg, ...
+  // rr = t % rows_wg of the tile, for m = t / rows_wg, + kSkinnyThreads / rows_wg, ...
   const int rows_wg = P.rbpw * 16;
   const int ep_rr = threadIdx.x % rows_wg;
   float ep_a = 0.f, ep_b = 0.f;
@@ -249,7 +253,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       // kStageBatch loads in flight per thread
       const int bpr = clen / PB;
       const int total = M * bpr;
-      const int nthr = blockDim.x;
+      const int nthr = kSkinnyThreads;
       for (int b0 = 0; b0 < total; b0 += kStageBatch * nthr) {
         u32x4 w4[kStageBatch];
 #pragma unroll
@@ -285,7 +289,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       // reduction)
       const int gl_n = clen / 128;
       const uint32_t ones = 0x3F803F80u;
-      for (int t = threadIdx.x; t < M * gl_n; t += blockDim.x) {
+      for (int t = threadIdx.x; t < M * gl_n; t += kSkinnyThreads) {
         const int m = t / gl_n, gl = t - m * gl_n;
         const uint16_t* p = xs + (size_t)m * xstride + gl * 128;
         u32x4 w4[16];
@@ -309,7 +313,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
       float* part_s = sxs;   // [waves] partial sums (sxs is free per-channel)
       for (int m = 0; m < M; ++m) {
         float s = 0.f;
-        for (int bi = threadIdx.x; bi < bpr; bi += blockDim.x) {
+        for (int bi = threadIdx.x; bi < bpr; bi += kSkinnyThreads) {
           const u32x4 w4 = *reinterpret_cast<const u32x4*>(xs + (size_t)m * xstride + bi * PB);
 #pragma unroll
           for (int q = 0; q < 4; ++q) s = dot2_bf16(w4[q], ones, s);
@@ -389,7 +393,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * slot + i) * M + col] = acc[i];
   }
   __syncthreads();
-  const int mstep = (int)blockDim.x / rows_wg;
+  const int mstep = kSkinnyThreads / rows_wg;
   {
     const int rr = ep_rr;
     const int rbl2 = rr >> 4, row = rr & 15;
@@ -410,7 +414,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
     // bf16(first * act(second)) for the rows of this workgroup
     __syncthreads();
     const int half = rows_wg / 2;  // distinct rows
-    for (int t = threadIdx.x; t < half * M; t += blockDim.x) {
+    for (int t = threadIdx.x; t < half * M; t += kSkinnyThreads) {
       const int j = t % half, m = t / half;
       const int rr1 = ((j >> 4) * 2) * 16 + (j & 15), rr2 = rr1 + 16;
       const int n = (rb0 + (j >> 4)) * 16 + (j & 15);
@@ -427,7 +431,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 // The byte-aligned precisions (2, 4, 8) and the split ones (3, 6) are two
 // kernels, so that the registers of one set do not limit the other's occupancy.
 template <bool GROUPED, bool SPLIT>
-__global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const SkinnyArgs args) {
+__global__ void __launch_bounds__(kSkinnyThreads) skinny_kernel(const SkinnyArgs args) {
   int pi = 0;
 #pragma unroll 1
   for (int i = 1; i < args.count; ++i)
@@ -461,7 +465,7 @@ static hipError_t launch_t(const SkinnyArgs& a, size_t lds, hipStream_t s) {
       160 * 1024);
   if (attr != hipSuccess) return attr;
   int tiles = a.p[a.count - 1].tile0 + a.p[a.count - 1].tiles;
-  hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(tiles), dim3(64 * kSkinnyWaves), lds, s,
+  hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(tiles), dim3(kSkinnyThreads), lds, s,
                      a);
   return hipGetLastError();
 }

@@ -17,6 +17,10 @@ namespace mq {
 // fp32 alpha would be zero or subnormal (no usable scale).
 // ---------------------------------------------------------------------------
 #pragma clang fp contract(off)
+// threads per workgroup of these kernels, as a constant (blockDim.x is a
+// vector load from the dispatch packet)
+constexpr int kPackThreads = 256;
+
 __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ w, int64_t n_vec,
                                                        int group, uint8_t* __restrict__ codes,
                                                        float* __restrict__ alpha,
@@ -105,11 +109,11 @@ __device__ __forceinline__ uint32_t slice4(uint32_t w) {
 // bytes of the second source, 4-7 bytes of the first).  At r = 8 the same
 // layout swaps bytes 1 and 2 of every dword (codes 0, 2 low; 1, 3 high).
 template <int R>
-__global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ codes,
+__global__ void __launch_bounds__(kPackThreads) pack_kernel(const u32x4* __restrict__ codes,
                                                    uint8_t* __restrict__ out, int64_t n_in16) {
   if constexpr (R == 4) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_in16 / 2;
-         i += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t i = blockIdx.x * (int64_t)kPackThreads + threadIdx.x; i < n_in16 / 2;
+         i += (int64_t)gridDim.x * kPackThreads) {
       const u32x4 in0 = __builtin_nontemporal_load(codes + 2 * i);
       const u32x4 in1 = __builtin_nontemporal_load(codes + 2 * i + 1);
       u32x4 o;
@@ -122,8 +126,8 @@ __global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ cod
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + i);
     }
   } else {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_in16;
-         i += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t i = blockIdx.x * (int64_t)kPackThreads + threadIdx.x; i < n_in16;
+         i += (int64_t)gridDim.x * kPackThreads) {
       const u32x4 in = __builtin_nontemporal_load(codes + i);
       if constexpr (R == 8) {
         u32x4 o;
@@ -183,15 +187,15 @@ __device__ __forceinline__ uint32_t word_of1(const uint32_t* t) {
 // plane.  Each thread takes 32 consecutive codes (two 16-byte loads): 4 r_hi
 // bytes of the high plane and 4 r_lo bytes of the low plane.
 template <int R>
-__global__ void __launch_bounds__(256) pack_split_kernel(const u32x4* __restrict__ codes,
+__global__ void __launch_bounds__(kPackThreads) pack_split_kernel(const u32x4* __restrict__ codes,
                                                          uint8_t* __restrict__ out,
                                                          int64_t n_thr, int64_t lo_base) {
   constexpr int RL = R == 6 ? 2 : 1, RH = R - RL;
   constexpr int CODES = 32;  // codes per thread
   constexpr int IN16 = CODES / 16;
   constexpr int HW = RH, LW = RL;  // high- and low-plane words per thread
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_thr;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = blockIdx.x * (int64_t)kPackThreads + threadIdx.x; i < n_thr;
+       i += (int64_t)gridDim.x * kPackThreads) {
     u32x4 in[IN16];
 #pragma unroll
     for (int j = 0; j < IN16; ++j) in[j] = __builtin_nontemporal_load(codes + i * IN16 + j);
@@ -233,10 +237,10 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_
     const int64_t lo_base = N * K * rh / 8;
     const u32x4* in = reinterpret_cast<const u32x4*>(codes);
     if (r == 6)
-      hipLaunchKernelGGL(pack_split_kernel<6>, dim3((unsigned)blocks), dim3(256), 0, stream, in,
+      hipLaunchKernelGGL(pack_split_kernel<6>, dim3((unsigned)blocks), dim3(kPackThreads), 0, stream, in,
                          packed, n_thr, lo_base);
     else
-      hipLaunchKernelGGL(pack_split_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, in,
+      hipLaunchKernelGGL(pack_split_kernel<3>, dim3((unsigned)blocks), dim3(kPackThreads), 0, stream, in,
                          packed, n_thr, lo_base);
     return hipGetLastError();
   }
@@ -248,13 +252,13 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int r, uint8_
   uint8_t* out = packed;
   switch (r) {
     case 2:
-      hipLaunchKernelGGL(pack_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
+      hipLaunchKernelGGL(pack_kernel<2>, dim3((unsigned)blocks), dim3(kPackThreads), 0, stream, in, out, n16);
       break;
     case 4:
-      hipLaunchKernelGGL(pack_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
+      hipLaunchKernelGGL(pack_kernel<4>, dim3((unsigned)blocks), dim3(kPackThreads), 0, stream, in, out, n16);
       break;
     default:
-      hipLaunchKernelGGL(pack_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n16);
+      hipLaunchKernelGGL(pack_kernel<8>, dim3((unsigned)blocks), dim3(kPackThreads), 0, stream, in, out, n16);
       break;
   }
   return hipGetLastError();
