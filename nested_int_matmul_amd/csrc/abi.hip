@@ -40,6 +40,12 @@ bool valid_r(int r) { return r == 2 || r == 3 || r == 4 || r == 6 || r == 8; }
 
 constexpr int64_t kMaxK = 65536;
 constexpr int64_t kMaxPlaneBytes = (int64_t)1 << 31;
+// Mix'n'Match stack: bytes at the head of the next layer's q plane that a
+// layer's second launch warms into the last-level cache, and the workgroups
+// that read them, 64 KiB each (on the 32-layer Mistral-7B stack: 1321 to
+// 1307 us per token; 4 and 8 MiB gained less, 10 MiB and more cost time)
+constexpr uint64_t kStackWarmBytes = (uint64_t)6 << 20;
+constexpr int kWarmWorkgroups = 96;
 
 // a * b > lim for a, b >= 1, without forming the product (sizes come from
 // the caller unchecked and may be anywhere in int64)
@@ -71,18 +77,24 @@ mq_status skinny_run(mq::SkinnyArgs& a, bool grouped, hipStream_t stream) {
 }
 
 // One launch per (scale granularity, precision set) present among the problems.
-mq_status run_mixed(mq::SkinnyProblem* probs, int count, int64_t M, hipStream_t s) {
+// warm, warm_bytes: optional cache warm-up carried by the first of these launches.
+mq_status run_mixed(mq::SkinnyProblem* probs, int count, int64_t M, hipStream_t s,
+                    const uint8_t* warm = nullptr, uint32_t warm_bytes = 0) {
   for (int pass = 0; pass < 4; ++pass) {
     const bool grouped = (pass & 1) != 0, split = (pass & 2) != 0;
     mq::SkinnyArgs a;
     std::memset(&a, 0, sizeof a);
     a.M = (int)M;
+    a.warm = warm;
+    a.warm_bytes = warm_bytes;
+    a.warm_wgs = kWarmWorkgroups;
     for (int i = 0; i < count; ++i)
       if ((probs[i].group != probs[i].K) == grouped && mq::split_precision(probs[i].r) == split)
         a.p[a.count++] = probs[i];
     if (a.count == 0) continue;
     mq_status st = skinny_run(a, grouped, s);
     if (st != MQ_OK) return st;
+    warm = nullptr;
   }
   return MQ_OK;
 }
@@ -501,7 +513,17 @@ mq_status run_stack(const mq_layer* layers, int n_layers, const uint16_t* x, flo
     mq::SkinnyProblem p2[2] = {prob(L.o, L.r, qb, nullptr, mq::kXBf16, o),
                                pair ? prob(L.down, L.r, ugb, nullptr, mq::kXBf16, dd)
                                     : prob(L.down, L.r, u, g, mq::kXF32Prod, dd)};
-    s = run_mixed(p2, 2, M, st);
+    // this launch (about a third of the layer's bytes, on fewer workgroups
+    // than the CUs hold) also warms the head of the next layer's q plane
+    const uint8_t* warm = nullptr;
+    uint32_t warm_bytes = 0;
+    if (i + 1 < n_layers) {
+      const mq_linear& nq = layers[i + 1].q;
+      const uint64_t qb = (uint64_t)nq.N * (uint64_t)nq.K * (uint64_t)layers[i + 1].r / 8;
+      warm = nq.packed;
+      warm_bytes = (uint32_t)(qb < kStackWarmBytes ? qb : kStackWarmBytes);
+    }
+    s = run_mixed(p2, 2, M, st, warm, warm_bytes);
     if (s != MQ_OK) return s;
     // the last layer leaves its own input a in the workspace
     e = mq::launch_residual_rmsnorm(h, o, dd, i + 1 < n_layers ? a : nullptr, M, d.H, st);

@@ -430,8 +430,30 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi
 // precisions of one stored model); each workgroup runs its problem's body.
 // The byte-aligned precisions (2, 4, 8) and the split ones (3, 6) are two
 // kernels, so that the registers of one set do not limit the other's occupancy.
+// Cache warm-up workgroup w of n: reads its own contiguous share of
+// warm[0, bytes) (a multiple of 64 KiB; the shares past the end are empty)
+// with buffer-to-LDS loads into one KiB of LDS that nothing reads (no
+// registers held, and the loads cannot be dropped), all in flight at once,
+// then waits for them before the workgroup's LDS is released.  Contiguous
+// shares measured 1% faster on the Mistral-7B stack than 4 KiB pieces
+// interleaved over the workgroups, which gained nothing.
+__device__ __forceinline__ void warm_body(const uint8_t* warm, uint32_t bytes, int w, int n) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(warm, bytes);
+  const uint32_t share = ((bytes + (uint32_t)n - 1) / (uint32_t)n + 65535u) & ~65535u;
+  const uint32_t beg = (uint32_t)w * share;
+  for (uint32_t off = beg + threadIdx.x * 16; off < beg + share; off += kSkinnyThreads * 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)smem, 16,
+                                             off, 0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+}
+
 template <bool GROUPED, bool SPLIT>
 __global__ void __launch_bounds__(kSkinnyThreads) skinny_kernel(const SkinnyArgs args) {
+  if ((int)blockIdx.x >= args.tiles) {
+    warm_body(args.warm, args.warm_bytes, (int)blockIdx.x - args.tiles, args.warm_wgs);
+    return;
+  }
   int pi = 0;
 #pragma unroll 1
   for (int i = 1; i < args.count; ++i)
@@ -464,9 +486,8 @@ static hipError_t launch_t(const SkinnyArgs& a, size_t lds, hipStream_t s) {
       (const void*)skinny_kernel<GROUPED, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
       160 * 1024);
   if (attr != hipSuccess) return attr;
-  int tiles = a.p[a.count - 1].tile0 + a.p[a.count - 1].tiles;
-  hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(tiles), dim3(kSkinnyThreads), lds, s,
-                     a);
+  const int wgs = a.tiles + (a.warm && a.warm_bytes ? a.warm_wgs : 0);
+  hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(wgs), dim3(kSkinnyThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -565,6 +586,8 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
     args.p[i].tile0 = tile0;
     tile0 += args.p[i].tiles;
   }
+  args.tiles = tile0;
+  if (args.warm_wgs < 0) args.warm_wgs = 0;
   const int gpc = kc / 128;
   const size_t lds = (size_t)M * (kc + kXPad) * 2 +
                      (size_t)(2 * M * gpc + 2 * kSkinnyMaxM) * 4 + (size_t)2 * waves * 16 * M * 4;

@@ -51,6 +51,14 @@ struct SkinnyArgs {
   int count;
   int M;
   int kc;        // activation codes staged per chunk (multiple of every step size)
+  int tiles;     // workgroups of the products (set by launch_skinny)
+  // optional cache warm-up: warm_wgs further workgroups read warm[0, warm_bytes)
+  // (weights a later launch streams first) and discard it, so that the later
+  // launch finds those bytes in the last-level cache; they run in this
+  // launch's ramp and tail, when its own loads leave HBM idle
+  const uint8_t* warm;
+  uint32_t warm_bytes;
+  int warm_wgs;
 };
 
 // Host-side planning + launch of the skinny (M <= 8) kernel.  `probs` hold the
