@@ -548,8 +548,9 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
   }
   // fill: a launch with fewer workgroups than CUs (a lone 14336-long down
   // projection at r = 2 gets 112) splits the K of its longest problem further
-  // while every wave keeps at least 8 load steps (r = 2 down alone: 13.4 ->
-  // about 9 us)
+  // while every wave keeps at least 4 load steps (r = 2 down alone: 13.4 ->
+  // about 9 us; a lone 14336 x 3584 matrix at r = 2, 224 -> 448 workgroups of
+  // 7 steps per wave: 9.0 -> 8.2 us)
   for (;;) {
     int tiles = 0, best = -1;
     for (int i = 0; i < args.count; ++i) tiles += args.p[i].tiles;
@@ -559,7 +560,7 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
       const int steps = ((p.K + 511) / 512) * 512 / step_codes(p.r, grouped);
       const int spg = grouped ? 128 / step_codes(p.r, grouped) : 1;
       const int ks_max = p.y2 ? waves / 2 : waves;
-      if (p.ks < ks_max && ((steps / spg) / (p.ks * 2)) * spg >= 8 &&
+      if (p.ks < ks_max && ((steps / spg) / (p.ks * 2)) * spg >= 4 &&
           (best < 0 || steps_per_wave[i] > steps_per_wave[best]))
         best = i;
     }
