@@ -37,7 +37,7 @@
 
 namespace mq {
 
-template <int R, bool GROUPED>
+template <int R, bool GROUPED, bool LEAN = false>
 struct Sk {
   // r = 3 and r = 6 planes are split in a high-bit and a low-bit plane
   static constexpr bool SPLIT = (R == 3 || R == 6);
@@ -52,8 +52,13 @@ struct Sk {
   static constexpr int PB = 8;                            // staging block (values)
   // loads in flight per lane: 8, and 4 at r = 2 (measured on the Gemma MLP
   // launch at r = 2: 15.0 against 16.6 us with 8; r = 4 and 8 unchanged or
-  // slower with 4)
-  static constexpr int DEPTH = R == 2 ? 4 : 8;
+  // slower with 4).  LEAN (per-channel launches whose LDS leaves room for six
+  // workgroups per CU): 6 at r = 4, which brings the kernel from 88 to 76
+  // VGPRs, so six waves fit per SIMD instead of five (a lone 14336 x 3584
+  // matrix at r = 4: 9.4 -> 8.6 us).  Where the staged activations allow only
+  // five workgroups per CU anyway, 8 keeps more bytes in flight (the Gemma
+  // nine-product launch was 0.4 us slower with 6).
+  static constexpr int DEPTH = R == 2 ? 4 : (R == 4 && LEAN) ? 6 : 8;
 };
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
@@ -114,9 +119,9 @@ __device__ __forceinline__ float gate_act(float g, int act) {
 }
 
 // One workgroup's share of problem pi, at slice precision R.
-template <int R, bool GROUPED>
+template <int R, bool GROUPED, bool LEAN = false>
 __device__ __forceinline__ void skinny_body(const SkinnyArgs& args, const int pi) {
-  using C = Sk<R, GROUPED>;
+  using C = Sk<R, GROUPED, LEAN>;
   using LD = LoadT<R, C::SPLIT ? 0 : C::V>;
   extern __shared__ __align__(16) unsigned char smem[];
   const SkinnyProblem& P = args.p[pi];
@@ -448,8 +453,8 @@ __device__ __forceinline__ void warm_body(const uint8_t* warm, uint32_t bytes, i
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
-template <bool GROUPED, bool SPLIT>
-__global__ void __launch_bounds__(kSkinnyThreads) skinny_kernel(const SkinnyArgs args) {
+template <bool GROUPED, bool SPLIT, bool LEAN>
+__device__ __forceinline__ void skinny_dispatch(const SkinnyArgs& args) {
   if ((int)blockIdx.x >= args.tiles) {
     warm_body(args.warm, args.warm_bytes, (int)blockIdx.x - args.tiles, args.warm_wgs);
     return;
@@ -463,10 +468,21 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_kernel(const SkinnyArgs
     if (r == 6) skinny_body<6, GROUPED>(args, pi);
     else skinny_body<3, GROUPED>(args, pi);
   } else {
-    if (r == 8) skinny_body<8, GROUPED>(args, pi);
-    else if (r == 4) skinny_body<4, GROUPED>(args, pi);
-    else skinny_body<2, GROUPED>(args, pi);
+    if (r == 8) skinny_body<8, GROUPED, LEAN>(args, pi);
+    else if (r == 4) skinny_body<4, GROUPED, LEAN>(args, pi);
+    else skinny_body<2, GROUPED, LEAN>(args, pi);
   }
+}
+
+template <bool GROUPED, bool SPLIT>
+__global__ void __launch_bounds__(kSkinnyThreads) skinny_kernel(const SkinnyArgs args) {
+  skinny_dispatch<GROUPED, SPLIT, false>(args);
+}
+
+// per-channel scales, r in {2, 4, 8}, short enough activation chunks for six
+// workgroups per CU: the same body with fewer registers (Sk::DEPTH)
+__global__ void __launch_bounds__(kSkinnyThreads) skinny_lean_kernel(const SkinnyArgs args) {
+  skinny_dispatch<false, false, true>(args);
 }
 
 // ---------------------------------------------------------------------------
@@ -478,16 +494,19 @@ static int step_codes(int r, bool grouped) {
   return 4 * V * 8 / r;
 }
 
-template <bool GROUPED, bool SPLIT>
+template <bool GROUPED, bool SPLIT, bool LEAN>
 static hipError_t launch_t(const SkinnyArgs& a, size_t lds, hipStream_t s) {
+  const void* fn = LEAN ? (const void*)skinny_lean_kernel : (const void*)skinny_kernel<GROUPED, SPLIT>;
   // the LDS limit is raised once per process (a function-local static is
   // initialized exactly once, also when several host threads launch)
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)skinny_kernel<GROUPED, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
   const int wgs = a.tiles + (a.warm && a.warm_bytes ? a.warm_wgs : 0);
-  hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(wgs), dim3(kSkinnyThreads), lds, s, a);
+  if constexpr (LEAN)
+    hipLaunchKernelGGL(skinny_lean_kernel, dim3(wgs), dim3(kSkinnyThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<GROUPED, SPLIT>), dim3(wgs), dim3(kSkinnyThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -594,8 +613,13 @@ hipError_t launch_skinny(SkinnyArgs& args, bool grouped, hipStream_t stream) {
                      (size_t)(2 * M * gpc + 2 * kSkinnyMaxM) * 4 + (size_t)2 * waves * 16 * M * 4;
   const bool split = args.p[0].r == 3 || args.p[0].r == 6;
   if (split)
-    return grouped ? launch_t<true, true>(args, lds, stream) : launch_t<false, true>(args, lds, stream);
-  return grouped ? launch_t<true, false>(args, lds, stream) : launch_t<false, false>(args, lds, stream);
+    return grouped ? launch_t<true, true, false>(args, lds, stream)
+                   : launch_t<false, true, false>(args, lds, stream);
+  if (grouped) return launch_t<true, false, false>(args, lds, stream);
+  // six workgroups per CU fit the 160 KiB of LDS (in 512-byte units)
+  const bool lean = 6 * ((lds + 511) / 512 * 512) <= 160 * 1024;
+  return lean ? launch_t<false, false, true>(args, lds, stream)
+              : launch_t<false, false, false>(args, lds, stream);
 }
 
 }  // namespace mq
