@@ -325,6 +325,61 @@ def row_tiny(torch, mq, inputs, dev):
     return out
 
 
+def row_decode_split(torch, mq, inputs, dev):
+    """f1: the Gemma-2-9B MLP decode at the split precisions r = 6 and 3, each
+    r alone (three products per launch), rotating over weight copies."""
+    mats = []
+    for i, name in enumerate(("up", "gate", "down")):
+        n, k = inputs.GEMMA9B_MLP[name]
+        w = inputs.device_gaussian_weights("gemma9b_mlp", n, k, dev, matrix=i, outlier_frac=1e-3)
+        codes, alpha, zero = mq.quantize(w, k)
+        del w
+        xb = inputs.activations_bf16("gemma9b_mlp", 1, k, matrix=i)
+        x = torch.from_numpy(xb.view("int16")).to(dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        mats.append(dict(name=name, N=n, K=k, codes=codes, alpha=alpha, zero=zero, x=x, y=y))
+    out = {}
+    side = torch.cuda.Stream()
+    for r in (6, 3):
+        base = [mq.pack(m["codes"], r) for m in mats]
+        b = sum(linear_bytes(m["N"], m["K"], r, m["K"], 1) for m in mats)
+        ncopy = max(2, -(-ROTATE_BYTES // b))
+        sets = [base] + [[p.clone() for p in base] for _ in range(ncopy - 1)]
+        plans = [mq.GemvGroupedPlan(gemma_problems(mq, mats, ps), r, 1, side) for ps in sets]
+        us = time_loop(torch, lambda i: plans[i % ncopy](), 50, stream=side)
+        out[f"r{r}"] = {"us": round(us, 2), "bytes": b, "GB/s": round(b / us / 1e3, 1),
+                        "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del plans, sets, base
+    del mats
+    return out
+
+
+def row_mid_m(torch, mq, inputs, dev):
+    """a4 between small batch and prefill: the 4096-wide down projection
+    (K = 14336), group 128, r = 4, at M = 128, 256, 512 and 1024 (the kernel
+    splits K over workgroups where the output tiles are few)."""
+    _, K, N = inputs.PREFILL_SHAPE
+    w = inputs.device_gaussian_weights("prefill", K, N, dev, matrix=1)
+    c, a, z = mq.quantize(w, 128)
+    del w
+    r = 4
+    pl = mq.pack(c, r)
+    out = {}
+    for M in (128, 256, 512, 1024):
+        xb = inputs.activations_bf16("prefill", M, N, matrix=1)
+        x = torch.from_numpy(xb.view("int16")).to(dev)
+        y = torch.empty((M, K), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, mq.gemm_workspace_bytes(M, K, N, 128)), dtype=torch.uint8,
+                         device=dev)
+        us = time_loop(torch, lambda i: mq.gemm(pl, r, a, z, 128, K, N, x, out=y, workspace=ws),
+                       20)
+        tf = 2 * M * N * K / us / 1e6
+        out[f"M{M}_r{r}"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+                             "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del c, a, z, pl
+    return out
+
+
 # name -> (function, what it measures); run in this order
 ROWS = {
     "gemv_tiny_linear": (row_tiny, "parity configuration: 512 -> 256, M = 1, 4"),
@@ -332,6 +387,8 @@ ROWS = {
     "gemm_mistral_small": (row_small, "a3 small-batch GEMM"),
     "gemm_prefill_M2048": (row_prefill, "a4 prefill GEMM"),
     "gemm_prefill_down_M2048": (row_prefill_down, "a4 prefill down projection"),
+    "gemm_down_mid_M": (row_mid_m, "a4 down projection at M = 128 to 1024"),
+    "gemv_gemma9b_mlp_r6_r3": (row_decode_split, "f1 decode at r = 6, 3"),
     "mixnmatch_mistral7b_32l": (lambda t, m, i, d: run_stack(t, m, i, d), "a5 Mix'n'Match stack"),
     "extra_precision_gemma_r2": (lambda t, m, i, d: run_extra(t, m, i, d), "f2 Extra-Precision"),
     "bitplanes_gemma9b_mlp": (lambda t, m, i, d: run_bitplanes(t, m, i, d), "f3 bit-planes"),
