@@ -57,8 +57,12 @@ struct Sk {
   // VGPRs, so six waves fit per SIMD instead of five (a lone 14336 x 3584
   // matrix at r = 4: 9.4 -> 8.6 us).  Where the staged activations allow only
   // five workgroups per CU anyway, 8 keeps more bytes in flight (the Gemma
-  // nine-product launch was 0.4 us slower with 6).
-  static constexpr int DEPTH = R == 2 ? 4 : (R == 4 && LEAN) ? 6 : 8;
+  // nine-product launch was 0.4 us slower with 6).  The split precisions
+  // (two planes per step) take 4: 88 instead of 120 VGPRs per-channel (five
+  // waves per SIMD instead of four), 124 instead of 160 with groups; the
+  // Gemma MLP at r = 6 / 3 went from 34.6-36.5 / 30.7-31.2 to 33.4-33.8 /
+  // 29.1 us (6 measured in between).
+  static constexpr int DEPTH = R == 2 ? 4 : (R == 4 && LEAN) ? 6 : SPLIT ? 4 : 8;
 };
 
 constexpr int kXPad = 8;          // bf16 elements of padding per staged activation row
