@@ -392,7 +392,7 @@ __global__ void __launch_bounds__(THREADS)
         for (int j = 0; j < NB; ++j) {
           if (ncol[j] >= N) continue;
           const float v = av[j] * (acc[i][j][eq * 4 + e3] - cz[j] * sv[e3]);
-          y[(int64_t)m * N + ncol[j]] = v;
+          store_out(y + (int64_t)m * N + ncol[j], v);
         }
       }
     }

@@ -439,8 +439,18 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
   //      of activation row m = mb * 16 + col
   float* out = a.y + (size_t)blockIdx.y * M * N;
   const bool vec = (N & 3) == 0;
+  // device-scope (write-through) stores of the tile: measured faster at
+  // M = 64 for r <= 6 (14336 x 4096 r = 4 / 2 / 3: 23.1-23.5 / 24.9 / 28.2 ->
+  // 22.0-22.4 / 22.5 / 26.2-26.5 us with the slice sum), slower at r = 8 and
+  // at M = 32 (27.8-28.5 -> 28.8-29.1 us; 16.0 -> 16.5 us), where plain
+  // stores are kept
+  constexpr bool kWriteThrough = R < 8 && MB == 4;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
+    // the block's 16 output rows from its first row at column n0: at most
+    // 16 N floats (N <= 2^25, so under 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t orr =
+        make_rsrc(out + (size_t)mb * 16 * N + n0, (uint32_t)(16 * (int64_t)N * 4));
     const int m = mb * 16 + col;
     if (m >= M) continue;
     float tot = 0.f;
@@ -458,7 +468,8 @@ __global__ void __launch_bounds__(64 * kNW) panel_kernel(const Args a) {
                              pa[b][e] * (pz[b][e] + Enc<R>::kOffsetShift) * tot;
       float* o = out + (size_t)m * N + nb0;
       if (vec && nb0 + 3 < N) {
-        *reinterpret_cast<f32x4*>(o) = v;
+        if (kWriteThrough) store_out16(orr, (uint32_t)((col * (int64_t)N + nb0 - n0) * 4), v);
+        else *reinterpret_cast<f32x4*>(o) = v;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -482,7 +493,11 @@ __global__ void __launch_bounds__(kReduceThreads) reduce_slices(const float* __r
   const int64_t stride = (int64_t)gridDim.x * kReduceThreads;
   const int64_t n4 = (count & 3) ? 0 : count >> 2;
   const f32x4* p4 = reinterpret_cast<const f32x4*>(part);
-  for (int64_t i = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x; i < n4; i += stride) {
+  for (int64_t i0 = (int64_t)blockIdx.x * kReduceThreads; i0 < n4; i0 += stride) {
+    // this trip's kReduceThreads vectors from a uniform base
+    const int64_t i = i0 + threadIdx.x;
+    if (i >= n4) break;
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + 4 * i0, kReduceThreads * 16);
     f32x4 v = p4[i];
     for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
       f32x4 t[kReduceBatch];
@@ -493,7 +508,7 @@ __global__ void __launch_bounds__(kReduceThreads) reduce_slices(const float* __r
       for (int b = 0; b < kReduceBatch; ++b)
         if (s0 + b < S) v += t[b];
     }
-    reinterpret_cast<f32x4*>(y)[i] = v;
+    store_out16(yr, (uint32_t)threadIdx.x * 16, v);
   }
   for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * kReduceThreads + threadIdx.x; i < count;
        i += stride) {
@@ -507,7 +522,7 @@ __global__ void __launch_bounds__(kReduceThreads) reduce_slices(const float* __r
       for (int b = 0; b < kReduceBatch; ++b)
         if (s0 + b < S) v += t[b];
     }
-    y[i] = v;
+    store_out(y + i, v);
   }
 }
 

@@ -43,6 +43,23 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // num_records (out-of-range loads return 0).
 constexpr uint32_t kBufferWord3 = 0x00020000u;
 
+// Results a kernel writes once and never reads back (GEMM output tiles,
+// K-slice partials, summed slices) may be stored at device scope (the sc1
+// bit), so that the XCD's L2 writes them through instead of holding them
+// dirty until the write-back at the end of the kernel; where that pays is
+// measured per kernel.  Whole 16-byte pieces go through a buffer store (a
+// relaxed atomic store is at most 8 bytes, and two 8-byte halves written
+// through separately measured slower than plain 16-byte stores).  The bits
+// stored are the same either way.
+constexpr int kCachePolicySc1 = 16;  // the sc1 bit of a vector memory instruction
+__device__ __forceinline__ void store_out(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_out16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0,
+                                         kCachePolicySc1);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            (int)kBufferWord3);
