@@ -582,6 +582,27 @@ def test_gemm_prefill_full_size(r):
 
 
 @pytest.mark.parametrize("r", [4, 2, 8, 6, 3])
+@pytest.mark.parametrize("group", [128, "K"])
+def test_gemm_prefill_second_round_ragged(r, group):
+    """More 256 x 256 tiles than one round of CUs (2048 x 8676: 272 tiles,
+    the last column of tiles ragged).  Every column from 8128 on (the tiles
+    of the second round and the ragged end) and a sample before it, all
+    2048 rows, against the oracle; guard elements after the output."""
+    M, n, k = 2048, 8676, 256
+    g = k if group == "K" else 128
+    note(f"gemm prefill second round ragged r={r} g={g}")
+    m = quantized("prefill", n, k, g, matrix=2)
+    xb = inputs.activations_bf16("prefill", M, k, matrix=2)
+    y, check = guarded_f32(M, n)
+    mq.gemm(mq.pack(m["q_d"], r), r, m["alpha_d"], m["zero_d"], g, n, k, x_device(xb), out=y)
+    torch.cuda.synchronize()
+    check(f"second round ragged r{r} g{g}")
+    cols = np.unique(np.concatenate([_sample_rows(8128, 64, seed=r), np.arange(8128, n)]))
+    compare_linear(y[:, cols], xb, m["q"][cols], m["alpha"][cols], m["zero"][cols], g, r,
+                   f"second round ragged r{r} g{g}")
+
+
+@pytest.mark.parametrize("r", [4, 2, 8, 6, 3])
 @pytest.mark.parametrize("M,group", [(2048, 128), (512, 128), (512, "K")])
 def test_gemm_prefill_down_projection_split_k(r, M, group):
     """The 4096-wide down projection (K = 14336) has 128 (M = 2048) or 32
